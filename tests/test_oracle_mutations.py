@@ -1,0 +1,140 @@
+"""Planted mistakes in the oracle must be caught by its pins (CPU only).
+
+Each case swaps one oracle function for a plausibly wrong variant (a dropped
+term, a wrong sign, index or operand) and checks that at least one pin test
+fails on it. Nothing here touches the GPU.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.rib as orib
+import test_oracle_attention as ta
+import test_oracle_posgen as tp
+
+
+def _golden():
+    import os
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _fails(fn, *args):
+    try:
+        fn(*args)
+    except (AssertionError, ValueError, IndexError):
+        return True
+    return False
+
+
+def _scores_no_bias(qc, kc, qp, kp, scale):
+    return scale * (np.asarray(qc) @ np.asarray(kc).T)
+
+
+def _scores_transposed_bias(qc, kc, qp, kp, scale):
+    return scale * (np.asarray(qc) @ np.asarray(kc).T + np.asarray(kp) @ np.asarray(qp).T)
+
+
+def _scores_unscaled_bias(qc, kc, qp, kp, scale):
+    return scale * (np.asarray(qc) @ np.asarray(kc).T) + np.asarray(qp) @ np.asarray(kp).T
+
+
+def _fwd_wrong_axis(qc, kc, v, qp, kp, scale):
+    S = orib.concat_scores(qc, kc, qp, kp, scale)
+    E = np.exp(S - S.max(axis=0, keepdims=True))
+    P = E / E.sum(axis=0, keepdims=True)
+    return P @ np.asarray(v, np.float64), np.log(np.exp(S).sum(1)), P
+
+
+def _bwd_missing_d(qc, kc, v, qp, kp, do, scale):
+    qc, kc, v, qp, kp, do = (np.asarray(a, np.float64) for a in (qc, kc, v, qp, kp, do))
+    _, _, P = orib.attention_window_fwd(qc, kc, v, qp, kp, scale)
+    dS = P * (do @ v.T)                       # D term dropped
+    qh = np.concatenate([qc, qp], 1)
+    kh = np.concatenate([kc, kp], 1)
+    dq, dk = scale * dS @ kh, scale * dS.T @ qh
+    d = qc.shape[1]
+    return dq[:, :d], dk[:, :d], P.T @ do, dq[:, d:], dk[:, d:]
+
+
+def _bwd_unscaled(qc, kc, v, qp, kp, do, scale):
+    g = list(orib.__dict__["_orig_bwd"](qc, kc, v, qp, kp, do, scale))
+    return g[0], g[1] / scale, g[2], g[3], g[4] / scale
+
+
+def _coords_pixel_centres(w):
+    n = [2 * i + 1 - w for i in range(w)]
+    return n, np.array([v / w for v in n])
+
+
+def _fourier_linear_freqs(w, F):
+    _, c = orib.window_coords(w)
+    out = np.zeros((w * w, 4 * F))
+    for t in range(w * w):
+        iy, ix = divmod(t, w)
+        for k in range(F):
+            a, b = (k + 1) * math.pi * c[ix], (k + 1) * math.pi * c[iy]
+            out[t, [k, F + k, 2 * F + k, 3 * F + k]] = [math.sin(a), math.cos(a), math.sin(b), math.cos(b)]
+    return out
+
+
+def _fourier_interleaved(w, F):
+    f = orib.__dict__["_orig_fourier"](w, F)
+    return f.reshape(w * w, 4, F).transpose(0, 2, 1).reshape(w * w, 4 * F)
+
+
+def _posgen_swapped(w, F, w1, b1, w2, b2, r):
+    qp, kp = orib.__dict__["_orig_posgen"](w, F, w1, b1, w2, b2, r)
+    return kp, qp
+
+
+def _gelu_tanh(z):
+    z = np.asarray(z, np.float64)
+    return 0.5 * z * (1 + np.tanh(math.sqrt(2 / math.pi) * (z + 0.044715 * z ** 3)))
+
+
+def _partition_col_major(x, w):
+    B, H, W, heads, d = x.shape
+    out = orib.__dict__["_orig_partition"](x, w)
+    N = w * w
+    perm = np.array([(t % w) * w + t // w for t in range(N)])
+    return out[:, :, perm, :]
+
+
+MUTATIONS = [
+    ("concat_scores", _scores_no_bias, [(ta.test_worked_example_w2, "golden"), (ta.test_concat_identity,)]),
+    ("concat_scores", _scores_transposed_bias, [(ta.test_concat_identity,), (ta.test_matches_torch_sdpa_with_additive_bias,)]),
+    ("concat_scores", _scores_unscaled_bias, [(ta.test_worked_example_w2, "golden"), (ta.test_concat_identity,)]),
+    ("attention_window_fwd", _fwd_wrong_axis, [(ta.test_softmax_rows_sum_to_one_and_lse,), (ta.test_closed_forms,)]),
+    ("attention_window_bwd", _bwd_missing_d, [(ta.test_backward_finite_differences,), (ta.test_backward_invariants,)]),
+    ("attention_window_bwd", _bwd_unscaled, [(ta.test_backward_finite_differences,), (ta.test_worked_example_w2, "golden")]),
+    ("window_coords", _coords_pixel_centres, [(tp.test_coords_match_linspace, 16), (tp.test_fourier_hand_derived, "golden")]),
+    ("fourier_features", _fourier_linear_freqs, [(tp.test_fourier_hand_derived, "golden"), (tp.test_fourier_periodicity_power_of_two_windows, 4)]),
+    ("fourier_features", _fourier_interleaved, [(tp.test_fourier_hand_derived, "golden")]),
+    ("posgen", _posgen_swapped, [(tp.test_posgen_matches_torch_mlp, 16, 8)]),
+    ("gelu", _gelu_tanh, [(tp.test_gelu_matches_torch,), (tp.test_posgen_matches_torch_mlp, 32, 16)]),
+    ("window_partition", _partition_col_major, [(ta.test_partition_bijection_brute_force, 2, 6, 9, 2, 3, 3)]),
+]
+
+
+@pytest.mark.parametrize("name,bad,pins", MUTATIONS, ids=[f"{m[0]}:{m[1].__name__}" for m in MUTATIONS])
+def test_planted_mistake_is_caught(monkeypatch, name, bad, pins):
+    orig = getattr(orib, name)
+    for key, fn in (("_orig_bwd", orib.attention_window_bwd), ("_orig_fourier", orib.fourier_features),
+                    ("_orig_posgen", orib.posgen), ("_orig_partition", orib.window_partition)):
+        monkeypatch.setitem(orib.__dict__, key, fn)
+    monkeypatch.setattr(orib, name, bad)
+    monkeypatch.setattr(oracle, name, bad)
+    caught = []
+    for pin in pins:
+        fn, args = pin[0], [(_golden() if a == "golden" else a) for a in pin[1:]]
+        caught.append(_fails(fn, *args))
+    assert any(caught), f"no pin caught the planted mistake in {name}"
+    monkeypatch.setattr(orib, name, orig)
+    # the unmodified oracle passes the same pins
+    monkeypatch.setattr(oracle, name, orig)
+    for pin in pins:
+        fn, args = pin[0], [(_golden() if a == "golden" else a) for a in pin[1:]]
+        fn(*args)
