@@ -1,0 +1,176 @@
+/*
+ * rib.h - C ABI of the MI355X (gfx950) RIB window-attention library (librib.so).
+ *
+ * Rank-factorized Implicit Neural Bias (RIB) replaces an additive relative
+ * positional bias by low-rank positional tokens Q_p, K_p that are generated
+ * from normalized in-window coordinates (Fourier features + a small MLP) and
+ * appended channel-wise to the content tokens, so the biased score is one
+ * dot product:  S = [Q_c, Q_p][K_c, K_p]^T = Q_c K_c^T + Q_p K_p^T.
+ * Sources (web pages on the paper "Rank-Factorized Implicit Neural Bias:
+ * Scaling Super-Resolution Transformer with FlashAttention", arXiv 2603.06738):
+ *   [EN]  gist.science/paper/2603.06738, "Technical Summary"
+ *   [DE]  gist.science/de/paper/2603.06738, "Technische Zusammenfassung"
+ *   [ZH]  gist.science/zh/paper/2603.06738, technical part
+ *   [ABS] khansong-paper-with-me.hf.space, the paper's abstract
+ *
+ * Conventions shared by every entry point
+ *  - Pointers marked (device) are HIP device pointers, caller-allocated and
+ *    caller-owned; the library never allocates or frees device memory and
+ *    keeps no global mutable device state. Pointers to structs are host.
+ *  - Tensors are dense, row-major, innermost dimension last, and 16-byte
+ *    aligned. A feature map is [B, H, W, heads, d_c].
+ *  - Windows are square, non-overlapping, unshifted and unpadded: H and W
+ *    must be multiples of w. Inside a window, token t = iy*w + ix (row-major).
+ *    Units (batch, window, head) are ordered: windows row-major per image,
+ *    images in batch order, heads innermost.
+ *  - Activations are RIB_F32 or RIB_BF16 (bfloat16). MLP weights, LSE and the
+ *    positional-token gradients dQ_p, dK_p are always float32.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream): no host or device synchronisation. Outputs are overwritten,
+ *    never accumulated into. Calls on different streams are safe when they
+ *    use distinct output and workspace buffers.
+ *  - Arguments are validated before anything is launched. A failing call
+ *    launches nothing and returns a non-zero status; rib_last_error() then
+ *    holds a message (per host thread). No C++ exception crosses this ABI.
+ *  - Empty inputs (B == 0) are valid and launch nothing.
+ *  - Supported today: d_c = 32; 1 <= r <= 32; 2 <= w <= 256.
+ */
+#ifndef RIB_H
+#define RIB_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RIB_OK = 0,
+  RIB_ERR_INVALID_ARG = 1, /* bad shape, null or misaligned pointer, bad dtype */
+  RIB_ERR_UNSUPPORTED = 2, /* valid arguments this build does not implement */
+  RIB_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
+  RIB_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} rib_status_t;
+
+typedef enum { RIB_F32 = 0, RIB_BF16 = 1 } rib_dtype_t;
+
+/* A hipStream_t passed as an opaque handle. */
+typedef void* rib_stream_t;
+
+/* Shape of one attention call. */
+typedef struct {
+  int32_t B, H, W; /* batch and feature-map height / width */
+  int32_t heads;   /* attention heads */
+  int32_t d_c;     /* content channels per head (Q_c, K_c, V, O) */
+  int32_t w;       /* window side; N = w*w tokens per window */
+  int32_t r;       /* rank of the positional tokens Q_p, K_p */
+} rib_shape_t;
+
+/* Position MLP, nn.Linear layout (out x in), float32 (device). */
+typedef struct {
+  int32_t n_freq;   /* F: frequencies 2^k * pi, k = 0..F-1, per axis; 4F features */
+  int32_t hidden;   /* hidden width */
+  int32_t rank;     /* r: the MLP emits 2r values, Q_p first, then K_p */
+  const float* w1;  /* [hidden, 4F] */
+  const float* b1;  /* [hidden], or NULL for zeros */
+  const float* w2;  /* [2r, hidden] */
+  const float* b2;  /* [2r], or NULL for zeros */
+} rib_mlp_t;
+
+/*
+ * rib_posgen - positional tokens of one window size [DE §2.A.1-2], [EN §2.A.1-2].
+ *
+ * Token t = iy*w + ix gets (x, y) = (c_ix, c_iy) with c_i = (2i - (w-1))/(w-1),
+ * i.e. linspace(-1, 1, w) [DE §2.A.1]; features
+ * phi = [sin(2^k pi x)]_k ++ [cos(2^k pi x)]_k ++ [sin(2^k pi y)]_k ++ [cos(2^k pi y)]_k;
+ * out = W2 GELU(W1 phi + b1) + b2 with the exact (erf) GELU; Q_p[t] = out[0:r],
+ * K_p[t] = out[r:2r]. The phase 2^k n/(w-1) is reduced exactly in integers
+ * before sin/cos are evaluated. One (Q_p, K_p) serves every window, batch and
+ * head of this window size, so it can be computed once and cached [DE §2.A.4].
+ *
+ *   w          window side, 2..256
+ *   mlp        host pointer; 1 <= n_freq <= 16, 1 <= hidden <= 128, 1 <= rank <= 32
+ *   out_dtype  element type of q_p and k_p
+ *   q_p, k_p   (device) outputs, [w*w, rank] each
+ */
+rib_status_t rib_posgen(int32_t w, const rib_mlp_t* mlp, rib_dtype_t out_dtype,
+                        void* q_p, void* k_p, rib_stream_t stream);
+
+/*
+ * rib_window_partition / rib_window_unpartition - the window gather and its inverse.
+ *
+ * partition:   x [B, H, W, heads, d_c]  ->  x_win [B*(H/w)*(W/w), heads, w*w, d_c]
+ * unpartition: x_win -> x (the exact inverse). A pure copy: bit-exact.
+ * Only shape->B, H, W, heads, d_c and w are used (any d_c with d_c*esize a
+ * multiple of 16 bytes).
+ */
+rib_status_t rib_window_partition(const rib_shape_t* shape, rib_dtype_t dtype,
+                                  const void* x, void* x_win, rib_stream_t stream);
+rib_status_t rib_window_unpartition(const rib_shape_t* shape, rib_dtype_t dtype,
+                                    const void* x_win, void* x, rib_stream_t stream);
+
+/* Bytes of device workspace rib_window_attn_fwd needs for this shape (0 when
+ * the shape is invalid). Linear in the feature-map size: no N x N buffer. */
+size_t rib_fwd_workspace_size(const rib_shape_t* shape, rib_dtype_t dtype);
+
+/*
+ * rib_window_attn_fwd - RIB window attention, forward [EN §2.A.3-4], [ABS].
+ *
+ * For every unit (batch, window, head):
+ *   O = softmax(scale * [Q_c | Q_p][K_c | K_p]^T) V
+ * over the N = w*w tokens of the window, with the same (Q_p, K_p) for every
+ * unit. The N x N score matrix is never written to memory.
+ *
+ *   scale          softmax scale; <= 0 selects 1/sqrt(d_c + r)
+ *   q_c, k_c, v    (device) [B, H, W, heads, d_c], dtype
+ *   q_p, k_p       (device) [w*w, r], dtype (as produced by rib_posgen)
+ *   o              (device) output [B, H, W, heads, d_c], dtype
+ *   lse            (device) output [B, H, W, heads] float32 natural-log
+ *                  log-sum-exp of each score row, or NULL
+ *   workspace      (device) at least rib_fwd_workspace_size() bytes, 256-byte aligned
+ */
+rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, float scale,
+                                 const void* q_c, const void* k_c, const void* v,
+                                 const void* q_p, const void* k_p,
+                                 void* o, float* lse,
+                                 void* workspace, size_t workspace_bytes,
+                                 rib_stream_t stream);
+
+/* Bytes of device workspace rib_window_attn_bwd needs (0 when invalid). */
+size_t rib_bwd_workspace_size(const rib_shape_t* shape, rib_dtype_t dtype);
+
+/*
+ * rib_window_attn_bwd - gradients of the forward above given dO.
+ *
+ * Recomputes P from LSE (no N x N buffer) and returns the content-token
+ * gradients dQ_c, dK_c, dV and the positional-token gradients dQ_p, dK_p,
+ * which sum the contributions of every unit that shares them. Deterministic:
+ * the same inputs give the same bits on every call.
+ *
+ *   o, lse         (device) the forward's output and log-sum-exp (required)
+ *   d_o            (device) upstream gradient [B, H, W, heads, d_c], dtype
+ *   dq_c, dk_c, dv (device) outputs [B, H, W, heads, d_c], dtype
+ *   dq_p, dk_p     (device) outputs [w*w, r] float32
+ *   workspace      (device) at least rib_bwd_workspace_size() bytes, 256-byte aligned
+ */
+rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, float scale,
+                                 const void* q_c, const void* k_c, const void* v,
+                                 const void* q_p, const void* k_p,
+                                 const void* o, const float* lse, const void* d_o,
+                                 void* dq_c, void* dk_c, void* dv,
+                                 float* dq_p, float* dk_p,
+                                 void* workspace, size_t workspace_bytes,
+                                 rib_stream_t stream);
+
+/* Static text naming a status code. */
+const char* rib_status_string(rib_status_t status);
+
+/* Detail of the last failing call on this host thread ("" if none). */
+const char* rib_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RIB_H */

@@ -1,0 +1,139 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+include/rib.h declares, and rejects bad arguments before launching anything.
+
+None of these calls reaches a kernel launch: each returns from validation.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import windowed_attention_implicit_amd as rib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x7F0000001000)       # aligned, never dereferenced (validation fails first)
+MISALIGNED = ctypes.c_void_p(0x7F0000001008)
+
+
+def _header_functions():
+    txt = open(os.path.join(ROOT, "include", "rib.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(rib_[a-z_0-9]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(rib.lib_path):
+        pytest.fail("librib.so is not built (run __graft_entry__.build())")
+    return rib.lib()
+
+
+def test_exports_every_declared_symbol(L):
+    declared = _header_functions()
+    assert len(declared) >= 9
+    for name in declared:
+        assert hasattr(L, name), f"{name} declared in rib.h but not exported"
+    assert set(declared) == set(rib.exported_symbols)
+
+
+def test_header_compiles_as_c():
+    import shutil
+    import subprocess
+    import tempfile
+    cc = shutil.which("gcc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    with tempfile.TemporaryDirectory() as d:
+        src = os.path.join(d, "t.c")
+        with open(src, "w") as f:
+            f.write('#include "rib.h"\nint main(void){ rib_shape_t s = {0}; (void)s; return 0; }\n')
+        r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), src,
+                            "-o", os.path.join(d, "t")], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
+
+
+def test_status_strings(L):
+    names = [L.rib_status_string(i).decode() for i in range(5)]
+    assert names == ["RIB_OK", "RIB_ERR_INVALID_ARG", "RIB_ERR_UNSUPPORTED", "RIB_ERR_WORKSPACE", "RIB_ERR_HIP"]
+
+
+def _fwd(L, shape, ws_bytes=1 << 40, ptrs=None, dtype=rib.RIB_BF16, scale=0.0, ws=FAKE):
+    p = ptrs or [FAKE] * 6
+    return L.rib_window_attn_fwd(ctypes.byref(shape), dtype, scale, p[0], p[1], p[2], p[3], p[4], p[5], None,
+                                 ws, ws_bytes, None)
+
+
+def test_fwd_validation(L):
+    good = rib.Shape(2, 192, 192, 6, 32, 96, 16)
+    assert _fwd(L, rib.Shape(2, 190, 192, 6, 32, 96, 16)) == rib.RIB_ERR_INVALID_ARG    # H % w
+    assert b"multiple" in L.rib_last_error()
+    assert _fwd(L, rib.Shape(2, 192, 192, 6, 32, 1, 16)) == rib.RIB_ERR_INVALID_ARG     # w < 2
+    assert _fwd(L, rib.Shape(2, 192, 192, 6, 32, 96, 0)) == rib.RIB_ERR_INVALID_ARG     # r < 1
+    assert _fwd(L, rib.Shape(-1, 192, 192, 6, 32, 96, 16)) == rib.RIB_ERR_INVALID_ARG   # B < 0
+    assert _fwd(L, rib.Shape(2, 192, 192, 6, 64, 96, 16)) == rib.RIB_ERR_UNSUPPORTED    # d_c
+    assert _fwd(L, rib.Shape(2, 192, 192, 6, 32, 96, 33)) == rib.RIB_ERR_UNSUPPORTED    # r > 32
+    assert _fwd(L, rib.Shape(1, 512, 512, 1, 32, 512, 16)) == rib.RIB_ERR_UNSUPPORTED   # w > 256
+    assert _fwd(L, good, dtype=7) == rib.RIB_ERR_INVALID_ARG
+    assert _fwd(L, good, scale=float("nan")) == rib.RIB_ERR_INVALID_ARG
+    assert _fwd(L, good, ptrs=[FAKE, None, FAKE, FAKE, FAKE, FAKE]) == rib.RIB_ERR_INVALID_ARG
+    assert b"k_c" in L.rib_last_error()
+    assert _fwd(L, good, ptrs=[FAKE, FAKE, MISALIGNED, FAKE, FAKE, FAKE]) == rib.RIB_ERR_INVALID_ARG
+    assert b"aligned" in L.rib_last_error()
+    need = L.rib_fwd_workspace_size(ctypes.byref(good), rib.RIB_BF16)
+    assert need > 0
+    assert _fwd(L, good, ws_bytes=need - 1) == rib.RIB_ERR_WORKSPACE
+    assert _fwd(L, good, ws=None) == rib.RIB_ERR_WORKSPACE
+    assert _fwd(L, good, ws=MISALIGNED) == rib.RIB_ERR_INVALID_ARG
+    # an empty batch is a valid no-op
+    assert _fwd(L, rib.Shape(0, 192, 192, 6, 32, 96, 16), ptrs=[None] * 6, ws=None, ws_bytes=0) == rib.RIB_OK
+
+
+def test_bwd_validation(L):
+    good = rib.Shape(2, 192, 192, 6, 32, 64, 16)
+    need = L.rib_bwd_workspace_size(ctypes.byref(good), rib.RIB_BF16)
+    assert need > 0
+
+    def call(shape, ws_bytes, nulls=()):
+        p = [None if i in nulls else FAKE for i in range(13)]
+        return L.rib_window_attn_bwd(ctypes.byref(shape), rib.RIB_BF16, 0.0, *p, FAKE, ws_bytes, None)
+
+    assert call(rib.Shape(2, 192, 100, 6, 32, 64, 16), need) == rib.RIB_ERR_INVALID_ARG
+    assert call(good, need, nulls=(6,)) == rib.RIB_ERR_INVALID_ARG        # lse is required
+    assert b"lse" in L.rib_last_error()
+    assert call(good, need, nulls=(12,)) == rib.RIB_ERR_INVALID_ARG       # dk_p
+    assert call(good, need - 256) == rib.RIB_ERR_WORKSPACE
+
+
+def test_posgen_validation(L):
+    mlp = rib._Mlp(16, 64, 16, FAKE.value, None, FAKE.value, None)
+    assert L.rib_posgen(1, ctypes.byref(mlp), rib.RIB_BF16, FAKE, FAKE, None) == rib.RIB_ERR_INVALID_ARG
+    assert L.rib_posgen(96, None, rib.RIB_BF16, FAKE, FAKE, None) == rib.RIB_ERR_INVALID_ARG
+    bad = rib._Mlp(16, 64, 33, FAKE.value, None, FAKE.value, None)
+    assert L.rib_posgen(96, ctypes.byref(bad), rib.RIB_BF16, FAKE, FAKE, None) == rib.RIB_ERR_UNSUPPORTED
+    bad = rib._Mlp(17, 64, 16, FAKE.value, None, FAKE.value, None)
+    assert L.rib_posgen(96, ctypes.byref(bad), rib.RIB_BF16, FAKE, FAKE, None) == rib.RIB_ERR_UNSUPPORTED
+    assert L.rib_posgen(96, ctypes.byref(mlp), rib.RIB_BF16, None, FAKE, None) == rib.RIB_ERR_INVALID_ARG
+
+
+def test_partition_validation(L):
+    s = rib.Shape(1, 96, 96, 6, 32, 96, 1)
+    assert L.rib_window_partition(ctypes.byref(s), rib.RIB_BF16, None, FAKE, None) == rib.RIB_ERR_INVALID_ARG
+    s2 = rib.Shape(1, 96, 90, 6, 32, 96, 1)
+    assert L.rib_window_unpartition(ctypes.byref(s2), rib.RIB_BF16, FAKE, FAKE, None) == rib.RIB_ERR_INVALID_ARG
+    s3 = rib.Shape(1, 96, 96, 6, 4, 96, 1)   # 4 bf16 channels = 8 bytes per row
+    assert L.rib_window_partition(ctypes.byref(s3), rib.RIB_BF16, FAKE, FAKE, None) == rib.RIB_ERR_UNSUPPORTED
+
+
+def test_workspace_is_linear_not_quadratic(L):
+    """No N x N buffer: the workspace grows with the map, not with the window area squared."""
+    def ws(B, H, w, fn=L.rib_fwd_workspace_size):
+        return fn(ctypes.byref(rib.Shape(B, H, H, 6, 32, w, 16)), rib.RIB_BF16)
+    for fn in (L.rib_fwd_workspace_size, L.rib_bwd_workspace_size):
+        small, big = ws(2, 192, 16, fn), ws(2, 192, 96, fn)
+        assert abs(big - small) <= 0.01 * small            # same map, 36x larger windows
+        assert ws(4, 192, 96, fn) <= 2 * ws(2, 192, 96, fn) + 4096
+        N = 96 * 96
+        assert big < 2 * 6 * N * N                          # far below one N x N matrix per unit
+    assert L.rib_fwd_workspace_size(ctypes.byref(rib.Shape(1, 10, 10, 1, 32, 3, 16)), rib.RIB_BF16) == 0

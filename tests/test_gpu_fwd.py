@@ -1,0 +1,147 @@
+"""GPU parity of the RIB window-attention forward against the float64 oracle.
+
+Small and ragged shapes are compared on every output; the method's full-size
+workloads are compared on sampled (batch, window, head) units, which the
+oracle computes one at a time, plus size-independent closed forms.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import rib_synth
+import windowed_attention_implicit_amd as rib
+from gpu_util import check, device, sample_units, to_f64, to_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(wl, x, dev, use_posgen=True, qpkp=None):
+    dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+    q, k, v = (to_gpu(x[n], dev) for n in ("q_c", "k_c", "v"))
+    if use_posgen:
+        W = {n: torch.from_numpy(x[n]).to(dev) for n in ("w1", "w2")}
+        qp, kp = rib.posgen(wl.w, W["w1"], None, W["w2"], None, wl.r, n_freq=wl.n_freq, out_dtype=dt)
+        rqp, rkp = oracle.posgen(wl.w, wl.n_freq, x["w1"], None, x["w2"], None, wl.r)
+    else:
+        qp, kp = (to_gpu(t, dev) for t in qpkp)
+        rqp, rkp = qpkp[0].f64(), qpkp[1].f64()
+    o, lse = rib.window_attn_fwd(q, k, v, qp, kp, wl.w)
+    torch.cuda.synchronize()
+    return o, lse, rqp, rkp
+
+
+def _compare(wl, x, o, lse, rqp, rkp, units=None, tag=""):
+    ro, rl = oracle.rib_window_attn_fwd(x["q_c"].f64(), x["k_c"].f64(), x["v"].f64(), rqp, rkp, wl.w, units=units)
+    check(f"{tag} O", to_f64(o), ro, wl.dtype)
+    lerr = np.nanmax(np.abs(to_f64(lse) - rl))
+    print(f"{tag} LSE max-abs {lerr:.3e}", flush=True)
+    assert lerr <= (1e-5 if wl.dtype == "f32" else 2e-2)
+
+
+def test_fwd_w16_single_fp32():
+    dev = device()
+    wl = rib_synth.WORKLOADS["w16_single_fp32"]
+    x = rib_synth.make_inputs(wl)
+    o, lse, rqp, rkp = _run(wl, x, dev)
+    _compare(wl, x, o, lse, rqp, rkp, tag=wl.name)
+
+
+def test_fwd_w32_map256_full():
+    dev = device()
+    wl = rib_synth.WORKLOADS["w32_map256_bf16"]
+    x = rib_synth.make_inputs(wl)
+    o, lse, rqp, rkp = _run(wl, x, dev)
+    _compare(wl, x, o, lse, rqp, rkp, tag=wl.name)
+
+
+@pytest.mark.parametrize("name,k", [("w64_map128x8_bf16", 6), ("w96_map192x4_bf16", 3)])
+def test_fwd_large_workloads_sampled(name, k):
+    dev = device()
+    wl = rib_synth.WORKLOADS[name]
+    x = rib_synth.make_inputs(wl)
+    o, lse, rqp, rkp = _run(wl, x, dev)
+    units = sample_units(wl, k, seed=1)
+    print(f"{name}: units {units}", flush=True)
+    _compare(wl, x, o, lse, rqp, rkp, units=units, tag=name)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("shape", [
+    # B, H, W, heads, d_c, w, r, dtype
+    (1, 10, 15, 2, 32, 5, 3, "bf16"),
+    (2, 14, 14, 1, 32, 7, 1, "bf16"),
+    (1, 20, 20, 3, 32, 10, 16, "bf16"),
+    (1, 24, 48, 2, 32, 24, 17, "bf16"),
+    (1, 40, 40, 1, 32, 40, 32, "bf16"),
+    (1, 2, 2, 1, 32, 2, 4, "bf16"),
+    (1, 10, 15, 2, 32, 5, 3, "f32"),
+    (2, 24, 24, 2, 32, 12, 20, "f32"),
+    (1, 32, 32, 1, 32, 32, 8, "f32"),
+], ids=lambda s: "B{}_H{}_W{}_h{}_d{}_w{}_r{}_{}".format(*s))
+def test_fwd_ragged_and_edge_shapes(shape):
+    dev = device()
+    B, H, W, heads, d, w, r, dt = shape
+    print(f"fwd edge {shape}", flush=True)
+    wl = rib_synth.custom_workload(B, H, W, heads, d, w, r, dt, seed=sum(shape[:7]))
+    x = rib_synth.make_inputs(wl)
+    qpkp = rib_synth.make_positional(w * w, r, dt, seed=w + r)
+    o, lse, rqp, rkp = _run(wl, x, dev, use_posgen=False, qpkp=qpkp)
+    _compare(wl, x, o, lse, rqp, rkp, tag=str(shape))
+
+
+def test_fwd_closed_forms_at_full_size():
+    """At the 96x96 shape: constant V gives constant O; zero scores give O = window mean of V."""
+    dev = device()
+    wl = rib_synth.custom_workload(1, 192, 192, 2, 32, 96, 16, "bf16", seed=5)
+    x = rib_synth.make_inputs(wl)
+    q, k = to_gpu(x["q_c"], dev), to_gpu(x["k_c"], dev)
+    qp, kp = (to_gpu(t, dev) for t in rib_synth.make_positional(96 * 96, 16, "bf16", seed=3))
+    vc = torch.linspace(-2, 2, 32, device=dev).to(torch.bfloat16).expand(1, 192, 192, 2, 32).contiguous()
+    o, _ = rib.window_attn_fwd(q, k, vc, qp, kp, 96)
+    err = (o.float() - vc.float()).abs().max().item()
+    print(f"constant V: max-abs {err:.3e}", flush=True)
+    assert err <= 2e-2
+    z = torch.zeros_like(q)
+    zp = torch.zeros_like(qp)
+    v = to_gpu(x["v"], dev)
+    o, lse = rib.window_attn_fwd(z, z, v, zp, zp, 96)
+    vw = v.float().reshape(1, 2, 96, 2, 96, 2, 32)
+    mean = vw.mean(dim=(2, 4), keepdim=True).expand_as(vw).reshape(1, 192, 192, 2, 32)
+    err = (o.float() - mean).abs().max().item()
+    print(f"zero scores: max-abs {err:.3e}", flush=True)
+    assert err <= 2e-3
+    assert torch.allclose(lse, torch.full_like(lse, float(np.log(96 * 96))), atol=1e-4)
+
+
+def test_fwd_deterministic_and_empty():
+    dev = device()
+    wl = rib_synth.custom_workload(2, 64, 64, 3, 32, 32, 16, "bf16", seed=9)
+    x = rib_synth.make_inputs(wl)
+    qpkp = rib_synth.make_positional(32 * 32, 16, "bf16", seed=4)
+    o1, l1, _, _ = _run(wl, x, dev, use_posgen=False, qpkp=qpkp)
+    o2, l2, _, _ = _run(wl, x, dev, use_posgen=False, qpkp=qpkp)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(l1, l2)
+    e = torch.empty((0, 64, 64, 3, 32), dtype=torch.bfloat16, device=dev)
+    qp, kp = (to_gpu(t, dev) for t in qpkp)
+    o, lse = rib.window_attn_fwd(e, e, e, qp, kp, 32)
+    assert o.shape == e.shape and lse.shape == (0, 64, 64, 3)
+
+
+def test_fwd_bias_cancels_content():
+    """Q_p K_p^T = -Q_c K_c^T makes every score zero: O is the window mean of V (the
+    content and bias terms enter one dot product)."""
+    dev = device()
+    w, r = 8, 32
+    wl = rib_synth.custom_workload(1, 8, 8, 1, 32, w, r, "f32", seed=2)
+    x = rib_synth.make_inputs(wl)
+    qc = x["q_c"].data.reshape(64, 32)
+    kc = x["k_c"].data.reshape(64, 32)
+    qp = torch.from_numpy(np.ascontiguousarray(qc)).to(dev)
+    kp = torch.from_numpy(np.ascontiguousarray(-kc)).to(dev)
+    q, k, v = (to_gpu(x[n], dev) for n in ("q_c", "k_c", "v"))
+    o, _ = rib.window_attn_fwd(q, k, v, qp, kp, w)
+    mean = v.reshape(64, 32).mean(0)
+    err = (o.reshape(64, 32) - mean).abs().max().item()
+    assert err <= 1e-5, err

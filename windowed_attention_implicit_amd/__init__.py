@@ -1,0 +1,248 @@
+"""Python binding of librib.so: RIB window attention on MI355X (gfx950).
+
+Thin ctypes marshalling over the C ABI in include/rib.h. torch supplies device
+memory and the current stream; every step of the computation runs in the HIP
+kernels of librib.so. There is no fallback: if the library is missing or no
+GPU is present, the compute entry points raise.
+
+Entry points (same names as the C ABI, without the ``rib_`` prefix):
+  posgen, window_partition, window_unpartition, window_attn_fwd,
+  window_attn_bwd, fwd_workspace_size, bwd_workspace_size
+plus ``FwdPlan`` / ``BwdPlan``, which preallocate workspace and outputs so a
+call can be repeated without allocating.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import torch
+
+__all__ = [
+    "RIB_OK", "RIB_ERR_INVALID_ARG", "RIB_ERR_UNSUPPORTED", "RIB_ERR_WORKSPACE", "RIB_ERR_HIP",
+    "RIB_F32", "RIB_BF16", "RibError", "lib", "lib_path", "exported_symbols",
+    "posgen", "window_partition", "window_unpartition", "window_attn_fwd", "window_attn_bwd",
+    "fwd_workspace_size", "bwd_workspace_size", "FwdPlan", "BwdPlan", "Shape",
+]
+
+RIB_OK, RIB_ERR_INVALID_ARG, RIB_ERR_UNSUPPORTED, RIB_ERR_WORKSPACE, RIB_ERR_HIP = range(5)
+RIB_F32, RIB_BF16 = 0, 1
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG_DIR, "librib.so")
+
+
+class RibError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("W", ctypes.c_int32),
+                ("heads", ctypes.c_int32), ("d_c", ctypes.c_int32), ("w", ctypes.c_int32),
+                ("r", ctypes.c_int32)]
+
+
+class _Mlp(ctypes.Structure):
+    _fields_ = [("n_freq", ctypes.c_int32), ("hidden", ctypes.c_int32), ("rank", ctypes.c_int32),
+                ("w1", ctypes.c_void_p), ("b1", ctypes.c_void_p), ("w2", ctypes.c_void_p),
+                ("b2", ctypes.c_void_p)]
+
+
+_LIB = None
+_vp, _sz, _i32, _f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
+_SIGS = {
+    "rib_posgen": (_i32, [_i32, ctypes.POINTER(_Mlp), _i32, _vp, _vp, _vp]),
+    "rib_window_partition": (_i32, [ctypes.POINTER(Shape), _i32, _vp, _vp, _vp]),
+    "rib_window_unpartition": (_i32, [ctypes.POINTER(Shape), _i32, _vp, _vp, _vp]),
+    "rib_fwd_workspace_size": (_sz, [ctypes.POINTER(Shape), _i32]),
+    "rib_bwd_workspace_size": (_sz, [ctypes.POINTER(Shape), _i32]),
+    "rib_window_attn_fwd": (_i32, [ctypes.POINTER(Shape), _i32, _f32] + [_vp] * 7 + [_vp, _sz, _vp]),
+    "rib_window_attn_bwd": (_i32, [ctypes.POINTER(Shape), _i32, _f32] + [_vp] * 13 + [_vp, _sz, _vp]),
+    "rib_status_string": (ctypes.c_char_p, [_i32]),
+    "rib_last_error": (ctypes.c_char_p, []),
+}
+exported_symbols = tuple(_SIGS)
+
+
+def lib():
+    """Loads librib.so once (raises if it has not been built)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(lib_path):
+            raise RuntimeError(f"{lib_path} is missing: build it with "
+                               "`python -m windowed_attention_implicit_amd.build`")
+        L = ctypes.CDLL(lib_path)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _LIB = L
+    return _LIB
+
+
+def _status_name(status: int) -> str:
+    try:
+        return lib().rib_status_string(status).decode()
+    except Exception:  # noqa: BLE001 - naming an error must never raise
+        return f"status {status}"
+
+
+def _check(status: int):
+    if status != RIB_OK:
+        raise RibError(status, lib().rib_last_error().decode())
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.bfloat16:
+        return RIB_BF16
+    if t == torch.float32:
+        return RIB_F32
+    raise TypeError(f"unsupported dtype {t}: use torch.bfloat16 or torch.float32")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _require_gpu(*ts):
+    for t in ts:
+        if t is not None and (not t.is_cuda or not t.is_contiguous()):
+            raise ValueError("tensors must be contiguous GPU tensors")
+
+
+def _shape_of(x: torch.Tensor, w: int, r: int) -> Shape:
+    if x.dim() != 5:
+        raise ValueError("feature maps are [B, H, W, heads, d_c]")
+    B, H, W, heads, d_c = x.shape
+    return Shape(B, H, W, heads, d_c, w, r)
+
+
+def fwd_workspace_size(shape: Shape, dtype: torch.dtype) -> int:
+    return int(lib().rib_fwd_workspace_size(ctypes.byref(shape), _dtype_code(dtype)))
+
+
+def bwd_workspace_size(shape: Shape, dtype: torch.dtype) -> int:
+    return int(lib().rib_bwd_workspace_size(ctypes.byref(shape), _dtype_code(dtype)))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns 256-byte (or better) aligned blocks
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+# ---------------------------------------------------------------- posgen
+
+def posgen(w: int, w1: torch.Tensor, b1, w2: torch.Tensor, b2, rank: int, n_freq: int = 16,
+           out_dtype: torch.dtype = torch.bfloat16):
+    """Positional tokens (Q_p, K_p) of window size w, each [w*w, rank] in out_dtype."""
+    _require_gpu(w1, b1, w2, b2)
+    for t in (w1, b1, w2, b2):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("MLP weights are float32")
+    hidden = w1.shape[0]
+    mlp = _Mlp(n_freq, hidden, rank, w1.data_ptr(), b1.data_ptr() if b1 is not None else None,
+               w2.data_ptr(), b2.data_ptr() if b2 is not None else None)
+    qp = torch.empty((w * w, rank), dtype=out_dtype, device=w1.device)
+    kp = torch.empty_like(qp)
+    _check(lib().rib_posgen(w, ctypes.byref(mlp), _dtype_code(out_dtype), _ptr(qp), _ptr(kp), _stream(w1.device)))
+    return qp, kp
+
+
+# ---------------------------------------------------------------- partition
+
+def window_partition(x: torch.Tensor, w: int) -> torch.Tensor:
+    """[B, H, W, heads, d] -> [B*(H/w)*(W/w), heads, w*w, d]."""
+    _require_gpu(x)
+    s = _shape_of(x, w, 1)
+    out = torch.empty((s.B * (s.H // w) * (s.W // w), s.heads, w * w, s.d_c), dtype=x.dtype, device=x.device)
+    _check(lib().rib_window_partition(ctypes.byref(s), _dtype_code(x.dtype), _ptr(x), _ptr(out), _stream(x.device)))
+    return out
+
+
+def window_unpartition(xw: torch.Tensor, B: int, H: int, W: int, w: int) -> torch.Tensor:
+    """Inverse of ``window_partition``."""
+    _require_gpu(xw)
+    heads, d = xw.shape[1], xw.shape[3]
+    s = Shape(B, H, W, heads, d, w, 1)
+    out = torch.empty((B, H, W, heads, d), dtype=xw.dtype, device=xw.device)
+    _check(lib().rib_window_unpartition(ctypes.byref(s), _dtype_code(xw.dtype), _ptr(xw), _ptr(out),
+                                        _stream(xw.device)))
+    return out
+
+
+# ---------------------------------------------------------------- attention
+
+class FwdPlan:
+    """Preallocated forward call: workspace, O and LSE for one shape."""
+
+    def __init__(self, q_c, k_c, v, q_p, k_p, w: int, scale: float | None = None, want_lse: bool = True):
+        _require_gpu(q_c, k_c, v, q_p, k_p)
+        self.shape = _shape_of(q_c, w, q_p.shape[1])
+        self.dtype = _dtype_code(q_c.dtype)
+        for t in (k_c, v, q_p, k_p):
+            if t.dtype != q_c.dtype:
+                raise TypeError("all activations and Q_p, K_p must share one dtype")
+        self.inputs = (q_c, k_c, v, q_p, k_p)
+        self.scale = 0.0 if scale is None else float(scale)
+        self.o = torch.empty_like(q_c)
+        s = self.shape
+        self.lse = torch.empty((s.B, s.H, s.W, s.heads), dtype=torch.float32, device=q_c.device) if want_lse else None
+        self.ws_bytes = fwd_workspace_size(self.shape, q_c.dtype)
+        self.ws = _workspace(self.ws_bytes, q_c.device)
+
+    def run(self, stream=None):
+        q_c, k_c, v, q_p, k_p = self.inputs
+        st = _stream(q_c.device) if stream is None else ctypes.c_void_p(stream)
+        _check(lib().rib_window_attn_fwd(ctypes.byref(self.shape), self.dtype, self.scale, _ptr(q_c), _ptr(k_c),
+                                         _ptr(v), _ptr(q_p), _ptr(k_p), _ptr(self.o), _ptr(self.lse),
+                                         _ptr(self.ws), self.ws_bytes, st))
+        return self.o, self.lse
+
+
+def window_attn_fwd(q_c, k_c, v, q_p, k_p, w: int, scale: float | None = None, want_lse: bool = True):
+    """O = softmax(scale [Q_c|Q_p][K_c|K_p]^T) V per window and head; returns (O, LSE or None)."""
+    return FwdPlan(q_c, k_c, v, q_p, k_p, w, scale, want_lse).run()
+
+
+class BwdPlan:
+    """Preallocated backward call: workspace and the five gradients for one shape."""
+
+    def __init__(self, q_c, k_c, v, q_p, k_p, o, lse, d_o, w: int, scale: float | None = None):
+        _require_gpu(q_c, k_c, v, q_p, k_p, o, lse, d_o)
+        self.shape = _shape_of(q_c, w, q_p.shape[1])
+        self.dtype = _dtype_code(q_c.dtype)
+        self.inputs = (q_c, k_c, v, q_p, k_p, o, lse, d_o)
+        self.scale = 0.0 if scale is None else float(scale)
+        self.dq = torch.empty_like(q_c)
+        self.dk = torch.empty_like(q_c)
+        self.dv = torch.empty_like(q_c)
+        self.dqp = torch.empty(q_p.shape, dtype=torch.float32, device=q_c.device)
+        self.dkp = torch.empty(q_p.shape, dtype=torch.float32, device=q_c.device)
+        self.ws_bytes = bwd_workspace_size(self.shape, q_c.dtype)
+        self.ws = _workspace(self.ws_bytes, q_c.device)
+
+    def run(self, stream=None):
+        q_c, k_c, v, q_p, k_p, o, lse, d_o = self.inputs
+        st = _stream(q_c.device) if stream is None else ctypes.c_void_p(stream)
+        _check(lib().rib_window_attn_bwd(ctypes.byref(self.shape), self.dtype, self.scale, _ptr(q_c), _ptr(k_c),
+                                         _ptr(v), _ptr(q_p), _ptr(k_p), _ptr(o), _ptr(lse), _ptr(d_o),
+                                         _ptr(self.dq), _ptr(self.dk), _ptr(self.dv), _ptr(self.dqp),
+                                         _ptr(self.dkp), _ptr(self.ws), self.ws_bytes, st))
+        return self.dq, self.dk, self.dv, self.dqp, self.dkp
+
+
+def window_attn_bwd(q_c, k_c, v, q_p, k_p, o, lse, d_o, w: int, scale: float | None = None):
+    """Returns (dQ_c, dK_c, dV, dQ_p, dK_p); dQ_p and dK_p are float32 [w*w, r]."""
+    return BwdPlan(q_c, k_c, v, q_p, k_p, o, lse, d_o, w, scale).run()
+
+
+def default_scale(d_c: int, r: int) -> float:
+    return 1.0 / math.sqrt(d_c + r)

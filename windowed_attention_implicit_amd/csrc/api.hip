@@ -1,0 +1,378 @@
+// C ABI of the RIB window-attention library: argument validation, workspace
+// layout and the launch sequence of each entry point. Every argument is
+// checked before the first launch; nothing here allocates device memory.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "internal.hpp"
+
+namespace rib {
+namespace {
+
+thread_local std::string g_last_error;
+
+rib_status_t fail(rib_status_t st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+rib_status_t fail(rib_status_t st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+rib_status_t ok() {
+  g_last_error.clear();
+  return RIB_OK;
+}
+
+rib_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(RIB_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int esize_of(rib_dtype_t dt) { return dt == RIB_F32 ? 4 : 2; }
+
+bool dtype_ok(rib_dtype_t dt) { return dt == RIB_F32 || dt == RIB_BF16; }
+
+int padded_rank(int r) { return r <= 16 ? 16 : 32; }
+
+constexpr int kMaxW = 256;
+
+// Shape checks shared by every attention entry point.
+rib_status_t check_shape(const rib_shape_t* s, rib_dtype_t dt, bool need_rank) {
+  if (!s) return fail(RIB_ERR_INVALID_ARG, "shape is NULL");
+  if (!dtype_ok(dt)) return fail(RIB_ERR_INVALID_ARG, "dtype %d is not RIB_F32 or RIB_BF16", (int)dt);
+  if (s->B < 0 || s->H <= 0 || s->W <= 0 || s->heads <= 0 || s->d_c <= 0)
+    return fail(RIB_ERR_INVALID_ARG, "B must be >= 0 and H, W, heads, d_c > 0 (got B=%d H=%d W=%d heads=%d d_c=%d)",
+                s->B, s->H, s->W, s->heads, s->d_c);
+  if (s->w < 2) return fail(RIB_ERR_INVALID_ARG, "window size w=%d must be >= 2", s->w);
+  if (s->H % s->w || s->W % s->w)
+    return fail(RIB_ERR_INVALID_ARG, "H=%d and W=%d must be multiples of the window size w=%d", s->H, s->W, s->w);
+  if (s->w > kMaxW) return fail(RIB_ERR_UNSUPPORTED, "window size w=%d exceeds %d", s->w, kMaxW);
+  if (need_rank) {
+    if (s->r < 1) return fail(RIB_ERR_INVALID_ARG, "rank r=%d must be >= 1", s->r);
+    if (s->r > 32) return fail(RIB_ERR_UNSUPPORTED, "rank r=%d exceeds 32", s->r);
+    if (s->d_c != 32) return fail(RIB_ERR_UNSUPPORTED, "d_c=%d: only d_c = 32 is implemented", s->d_c);
+  }
+  int64_t elems = (int64_t)s->B * s->H * s->W * s->heads * s->d_c;
+  if (elems > ((int64_t)1 << 40)) return fail(RIB_ERR_UNSUPPORTED, "feature map too large");
+  return RIB_OK;
+}
+
+rib_status_t check_ptr(const void* p, const char* name) {
+  if (!p) return fail(RIB_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(RIB_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return RIB_OK;
+}
+
+#define RIB_TRY(expr)                 \
+  do {                                \
+    rib_status_t _st = (expr);        \
+    if (_st != RIB_OK) return _st;    \
+  } while (0)
+
+// Sequential carve-out of a workspace in 256-byte aligned pieces.
+struct Carve {
+  uintptr_t base;
+  size_t off = 0;
+  explicit Carve(void* p) : base((uintptr_t)p) {}
+  void* take(size_t bytes) {
+    void* p = (void*)(base + off);
+    off += (size_t)round_up((int64_t)bytes, 256);
+    return p;
+  }
+};
+
+struct FwdLayout {
+  void *qw, *kw, *vw, *ow, *qp, *kp;
+  size_t bytes;
+};
+
+FwdLayout fwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
+  const int es = esize_of(dt);
+  const size_t t = (size_t)g.units * g.n_rows * g.d_c * es;
+  const size_t pos = (size_t)g.n_rows * padded_rank(g.r) * es;
+  Carve c(ws);
+  FwdLayout L;
+  L.qw = c.take(t);
+  L.kw = c.take(t);
+  L.vw = c.take(t);
+  L.ow = c.take(t);
+  L.qp = c.take(pos);
+  L.kp = c.take(pos);
+  L.bytes = c.off;
+  return L;
+}
+
+struct BwdLayout {
+  void *qw, *kw, *vw, *dow, *qt, *kt, *dot, *qp, *kp, *qpt, *kpt, *dqw, *dkw, *dvw;
+  float *lse2, *dd, *dqp_part, *dkp_part;
+  size_t bytes;
+};
+
+BwdLayout bwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
+  const int es = esize_of(dt);
+  const int rp = padded_rank(g.r);
+  const size_t t = (size_t)g.units * g.n_rows * g.d_c * es;
+  const size_t pos = (size_t)g.n_rows * rp * es;
+  const size_t rowf = (size_t)g.units * g.n_rows * sizeof(float);
+  const size_t part = (size_t)g.units * g.n_rows * rp * sizeof(float);
+  const bool bf = dt == RIB_BF16;
+  Carve c(ws);
+  BwdLayout L;
+  L.qw = c.take(t);
+  L.kw = c.take(t);
+  L.vw = c.take(t);
+  L.dow = c.take(t);
+  L.qt = bf ? c.take(t) : nullptr;
+  L.kt = bf ? c.take(t) : nullptr;
+  L.dot = bf ? c.take(t) : nullptr;
+  L.qp = c.take(pos);
+  L.kp = c.take(pos);
+  L.qpt = bf ? c.take(pos) : nullptr;
+  L.kpt = bf ? c.take(pos) : nullptr;
+  L.dqw = c.take(t);
+  L.dkw = c.take(t);
+  L.dvw = c.take(t);
+  L.lse2 = (float*)c.take(rowf);
+  L.dd = (float*)c.take(rowf);
+  L.dqp_part = (float*)c.take(part);
+  L.dkp_part = (float*)c.take(part);
+  L.bytes = c.off;
+  return L;
+}
+
+float resolve_scale(float scale, const rib_shape_t* s) {
+  return scale > 0.f ? scale : 1.0f / sqrtf((float)(s->d_c + s->r));
+}
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+}  // namespace
+}  // namespace rib
+
+using namespace rib;
+
+extern "C" {
+
+const char* rib_status_string(rib_status_t status) {
+  switch (status) {
+    case RIB_OK: return "RIB_OK";
+    case RIB_ERR_INVALID_ARG: return "RIB_ERR_INVALID_ARG";
+    case RIB_ERR_UNSUPPORTED: return "RIB_ERR_UNSUPPORTED";
+    case RIB_ERR_WORKSPACE: return "RIB_ERR_WORKSPACE";
+    case RIB_ERR_HIP: return "RIB_ERR_HIP";
+  }
+  return "RIB_ERR_UNKNOWN";
+}
+
+const char* rib_last_error(void) { return g_last_error.c_str(); }
+
+rib_status_t rib_posgen(int32_t w, const rib_mlp_t* mlp, rib_dtype_t out_dtype, void* q_p, void* k_p,
+                        rib_stream_t stream) {
+  try {
+    if (w < 2) return fail(RIB_ERR_INVALID_ARG, "window size w=%d must be >= 2", w);
+    if (w > kMaxW) return fail(RIB_ERR_UNSUPPORTED, "window size w=%d exceeds %d", w, kMaxW);
+    if (!mlp) return fail(RIB_ERR_INVALID_ARG, "mlp is NULL");
+    if (!dtype_ok(out_dtype)) return fail(RIB_ERR_INVALID_ARG, "out_dtype %d invalid", (int)out_dtype);
+    if (mlp->n_freq < 1 || mlp->n_freq > 16)
+      return fail(RIB_ERR_UNSUPPORTED, "n_freq=%d must be in 1..16", mlp->n_freq);
+    if (mlp->hidden < 1 || mlp->hidden > 128)
+      return fail(RIB_ERR_UNSUPPORTED, "hidden=%d must be in 1..128", mlp->hidden);
+    if (mlp->rank < 1 || mlp->rank > 32) return fail(RIB_ERR_UNSUPPORTED, "rank=%d must be in 1..32", mlp->rank);
+    const size_t lds = sizeof(float) * ((size_t)mlp->hidden * 4 * mlp->n_freq + mlp->hidden +
+                                        (size_t)2 * mlp->rank * mlp->hidden + 2 * mlp->rank);
+    if (lds > 65536) return fail(RIB_ERR_UNSUPPORTED, "MLP too large for one LDS stage (%zu bytes)", lds);
+    if (!mlp->w1 || !mlp->w2) return fail(RIB_ERR_INVALID_ARG, "mlp weights are NULL");
+    if (!q_p || !k_p) return fail(RIB_ERR_INVALID_ARG, "q_p / k_p is NULL");
+    if (((uintptr_t)mlp->w1 | (uintptr_t)mlp->w2 | (uintptr_t)mlp->b1 | (uintptr_t)mlp->b2) & 3u)
+      return fail(RIB_ERR_INVALID_ARG, "mlp weights must be 4-byte aligned");
+    if (((uintptr_t)q_p | (uintptr_t)k_p) & (uintptr_t)(esize_of(out_dtype) - 1))
+      return fail(RIB_ERR_INVALID_ARG, "q_p / k_p misaligned for their element type");
+    hipError_t e = launch_posgen(w, *mlp, out_dtype, q_p, k_p, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "posgen launch");
+    return ok();
+  } catch (...) {
+    return fail(RIB_ERR_HIP, "unexpected C++ exception in rib_posgen");
+  }
+}
+
+static rib_status_t partition_common(const rib_shape_t* shape, rib_dtype_t dtype, const void* a, void* b,
+                                     bool forward, rib_stream_t stream) {
+  try {
+    RIB_TRY(check_shape(shape, dtype, false));
+    if ((shape->d_c * esize_of(dtype)) % 16)
+      return fail(RIB_ERR_UNSUPPORTED, "d_c * element size must be a multiple of 16 bytes");
+    if (shape->B == 0) return ok();
+    RIB_TRY(check_ptr(a, forward ? "x" : "x_win"));
+    RIB_TRY(check_ptr(b, forward ? "x_win" : "x"));
+    Geom g = make_geom(*shape);
+    hipError_t e = forward ? launch_partition_plain(g, esize_of(dtype), a, b, (hipStream_t)stream)
+                           : launch_unpartition_plain(g, esize_of(dtype), a, b, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "partition launch");
+    return ok();
+  } catch (...) {
+    return fail(RIB_ERR_HIP, "unexpected C++ exception in window partition");
+  }
+}
+
+rib_status_t rib_window_partition(const rib_shape_t* shape, rib_dtype_t dtype, const void* x, void* x_win,
+                                  rib_stream_t stream) {
+  return partition_common(shape, dtype, x, x_win, true, stream);
+}
+
+rib_status_t rib_window_unpartition(const rib_shape_t* shape, rib_dtype_t dtype, const void* x_win, void* x,
+                                    rib_stream_t stream) {
+  return partition_common(shape, dtype, x_win, x, false, stream);
+}
+
+size_t rib_fwd_workspace_size(const rib_shape_t* shape, rib_dtype_t dtype) {
+  if (check_shape(shape, dtype, true) != RIB_OK) return 0;
+  Geom g = make_geom(*shape);
+  return fwd_layout(g, dtype, nullptr).bytes;
+}
+
+size_t rib_bwd_workspace_size(const rib_shape_t* shape, rib_dtype_t dtype) {
+  if (check_shape(shape, dtype, true) != RIB_OK) return 0;
+  Geom g = make_geom(*shape);
+  return bwd_layout(g, dtype, nullptr).bytes;
+}
+
+rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, float scale, const void* q_c,
+                                 const void* k_c, const void* v, const void* q_p, const void* k_p, void* o,
+                                 float* lse, void* workspace, size_t workspace_bytes, rib_stream_t stream) {
+  try {
+    RIB_TRY(check_shape(shape, dtype, true));
+    if (!(scale == scale) || isinf(scale)) return fail(RIB_ERR_INVALID_ARG, "scale is not finite");
+    if (shape->B == 0) return ok();
+    RIB_TRY(check_ptr(q_c, "q_c"));
+    RIB_TRY(check_ptr(k_c, "k_c"));
+    RIB_TRY(check_ptr(v, "v"));
+    RIB_TRY(check_ptr(q_p, "q_p"));
+    RIB_TRY(check_ptr(k_p, "k_p"));
+    RIB_TRY(check_ptr(o, "o"));
+    if (lse && ((uintptr_t)lse & 3u)) return fail(RIB_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+    Geom g = make_geom(*shape);
+    const size_t need = fwd_layout(g, dtype, nullptr).bytes;
+    if (!workspace || workspace_bytes < need)
+      return fail(RIB_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
+    if ((uintptr_t)workspace & 255u) return fail(RIB_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    FwdLayout L = fwd_layout(g, dtype, workspace);
+    hipStream_t st = (hipStream_t)stream;
+    const int es = esize_of(dtype);
+    const int rp = padded_rank(g.r);
+    hipError_t e;
+    if ((e = launch_partition(g, es, WinLayout::kRows, q_c, L.qw, st)) != hipSuccess) return hip_fail(e, "partition q");
+    if ((e = launch_partition(g, es, WinLayout::kRows, k_c, L.kw, st)) != hipSuccess) return hip_fail(e, "partition k");
+    if ((e = launch_partition(g, es, dtype == RIB_BF16 ? WinLayout::kTransKappa : WinLayout::kRows, v, L.vw, st)) !=
+        hipSuccess)
+      return hip_fail(e, "partition v");
+    if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, q_p, es, L.qp, st)) != hipSuccess) return hip_fail(e, "pack q_p");
+    if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, k_p, es, L.kp, st)) != hipSuccess) return hip_fail(e, "pack k_p");
+    FwdArgs a;
+    a.g = g;
+    a.c = resolve_scale(scale, shape) * kLog2e;
+    a.qw = L.qw; a.kw = L.kw; a.vw = L.vw; a.qp = L.qp; a.kp = L.kp; a.ow = L.ow;
+    a.lse = lse;
+    a.rp = rp;
+    e = dtype == RIB_BF16 ? launch_attn_fwd_bf16(a, st) : launch_attn_fwd_f32(a, st);
+    if (e != hipSuccess) return hip_fail(e, "attention forward");
+    if ((e = launch_unpartition(g, es, L.ow, o, st)) != hipSuccess) return hip_fail(e, "unpartition o");
+    return ok();
+  } catch (...) {
+    return fail(RIB_ERR_HIP, "unexpected C++ exception in rib_window_attn_fwd");
+  }
+}
+
+rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, float scale, const void* q_c,
+                                 const void* k_c, const void* v, const void* q_p, const void* k_p, const void* o,
+                                 const float* lse, const void* d_o, void* dq_c, void* dk_c, void* dv, float* dq_p,
+                                 float* dk_p, void* workspace, size_t workspace_bytes, rib_stream_t stream) {
+  try {
+    RIB_TRY(check_shape(shape, dtype, true));
+    if (!(scale == scale) || isinf(scale)) return fail(RIB_ERR_INVALID_ARG, "scale is not finite");
+    RIB_TRY(check_ptr(dq_p, "dq_p"));
+    RIB_TRY(check_ptr(dk_p, "dk_p"));
+    if (shape->B == 0) {
+      // no unit contributes: the positional gradients are an empty sum (zeros)
+      Geom g0 = make_geom(*shape);
+      const int rp0 = padded_rank(g0.r);
+      hipError_t e = launch_reduce_pos_grads(0, g0.N, g0.n_rows, g0.r, rp0, nullptr, dq_p, (hipStream_t)stream);
+      if (e == hipSuccess) e = launch_reduce_pos_grads(0, g0.N, g0.n_rows, g0.r, rp0, nullptr, dk_p, (hipStream_t)stream);
+      if (e != hipSuccess) return hip_fail(e, "zero dq_p / dk_p");
+      return ok();
+    }
+    RIB_TRY(check_ptr(q_c, "q_c"));
+    RIB_TRY(check_ptr(k_c, "k_c"));
+    RIB_TRY(check_ptr(v, "v"));
+    RIB_TRY(check_ptr(q_p, "q_p"));
+    RIB_TRY(check_ptr(k_p, "k_p"));
+    RIB_TRY(check_ptr(o, "o"));
+    RIB_TRY(check_ptr(lse, "lse"));
+    RIB_TRY(check_ptr(d_o, "d_o"));
+    RIB_TRY(check_ptr(dq_c, "dq_c"));
+    RIB_TRY(check_ptr(dk_c, "dk_c"));
+    RIB_TRY(check_ptr(dv, "dv"));
+    Geom g = make_geom(*shape);
+    const size_t need = bwd_layout(g, dtype, nullptr).bytes;
+    if (!workspace || workspace_bytes < need)
+      return fail(RIB_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
+    if ((uintptr_t)workspace & 255u) return fail(RIB_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    BwdLayout L = bwd_layout(g, dtype, workspace);
+    hipStream_t st = (hipStream_t)stream;
+    const int es = esize_of(dtype);
+    const int rp = padded_rank(g.r);
+    const bool bf = dtype == RIB_BF16;
+    hipError_t e;
+#define RIB_LAUNCH(call, what)                        \
+  do {                                                \
+    if ((e = (call)) != hipSuccess) return hip_fail(e, what); \
+  } while (0)
+    RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, q_c, L.qw, st), "partition q");
+    RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, k_c, L.kw, st), "partition k");
+    RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, v, L.vw, st), "partition v");
+    RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, d_o, L.dow, st), "partition do");
+    if (bf) {
+      RIB_LAUNCH(launch_partition(g, es, WinLayout::kTransKappa, q_c, L.qt, st), "partition q^T");
+      RIB_LAUNCH(launch_partition(g, es, WinLayout::kTransKappa, k_c, L.kt, st), "partition k^T");
+      RIB_LAUNCH(launch_partition(g, es, WinLayout::kTransKappa, d_o, L.dot, st), "partition do^T");
+    }
+    RIB_LAUNCH(launch_pack_pos(g.N, g.n_rows, g.r, rp, es, q_p, es, L.qp, st), "pack q_p");
+    RIB_LAUNCH(launch_pack_pos(g.N, g.n_rows, g.r, rp, es, k_p, es, L.kp, st), "pack k_p");
+    if (bf) {
+      RIB_LAUNCH(launch_pos_transpose(g.n_rows, rp, L.qp, L.qpt, st), "q_p^T");
+      RIB_LAUNCH(launch_pos_transpose(g.n_rows, rp, L.kp, L.kpt, st), "k_p^T");
+    }
+    RIB_LAUNCH(launch_bwd_prep(g, es, o, d_o, lse, L.dd, L.lse2, st), "bwd prep");
+    BwdArgs a;
+    a.g = g;
+    a.scale = resolve_scale(scale, shape);
+    a.c = a.scale * kLog2e;
+    a.rp = rp;
+    a.qw = L.qw; a.kw = L.kw; a.vw = L.vw; a.dow = L.dow;
+    a.qt = L.qt; a.kt = L.kt; a.dot = L.dot;
+    a.qp = L.qp; a.kp = L.kp; a.qpt = L.qpt; a.kpt = L.kpt;
+    a.lse2 = L.lse2; a.dd = L.dd;
+    a.dqw = L.dqw; a.dkw = L.dkw; a.dvw = L.dvw;
+    a.dqp_part = L.dqp_part; a.dkp_part = L.dkp_part;
+    RIB_LAUNCH(bf ? launch_attn_bwd_bf16(a, st) : launch_attn_bwd_f32(a, st), "attention backward");
+    RIB_LAUNCH(launch_reduce_pos_grads(g.units, g.N, g.n_rows, g.r, rp, L.dqp_part, dq_p, st), "reduce dq_p");
+    RIB_LAUNCH(launch_reduce_pos_grads(g.units, g.N, g.n_rows, g.r, rp, L.dkp_part, dk_p, st), "reduce dk_p");
+    RIB_LAUNCH(launch_unpartition(g, es, L.dqw, dq_c, st), "unpartition dq");
+    RIB_LAUNCH(launch_unpartition(g, es, L.dkw, dk_c, st), "unpartition dk");
+    RIB_LAUNCH(launch_unpartition(g, es, L.dvw, dv, st), "unpartition dv");
+#undef RIB_LAUNCH
+    return ok();
+  } catch (...) {
+    return fail(RIB_ERR_HIP, "unexpected C++ exception in rib_window_attn_bwd");
+  }
+}
+
+}  // extern "C"

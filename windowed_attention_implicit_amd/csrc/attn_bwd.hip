@@ -1,0 +1,614 @@
+// RIB window attention, backward, for gfx950.
+//
+// Given dO, recomputes P = exp(scale S - LSE) per tile (no N x N buffer) and
+// forms the textbook softmax gradients dV = P^T dO, dP = dO V^T,
+// dS = P * (dP - D) with D_i = sum_c dO_ic O_ic, and
+// d[Q_c|Q_p] = scale dS [K_c|K_p], d[K_c|K_p] = scale dS^T [Q_c|Q_p]. The
+// positional parts are summed over every (batch, window, head) unit because
+// one (Q_p, K_p) serves all of them (gist.science/de "Technische
+// Zusammenfassung" §2.A.4: Q_p, K_p depend only on the window geometry).
+//
+// bf16 design: two MFMA kernels, deterministic (no atomics):
+//  * dkv: a workgroup owns 256 keys (4 waves x 64); it streams 64-query tiles
+//    of Q_hat, dO (row-major) and their channel-major kappa-permuted copies
+//    through LDS. S = Q_hat K_hat^T and dP = dO V^T come out with one key per
+//    lane, so P and dS feed dV^T += dO^T P and dK_hat^T += Q_hat^T dS directly
+//    as MFMA B operands.
+//  * dq: a workgroup owns 256 queries; it streams 64-key tiles of K_hat, V and
+//    K_hat^T (kappa) and accumulates dQ_hat^T += K_hat^T dS^T with one query
+//    per lane, like the forward.
+//  * Positional-gradient partials are written per unit in float32 and summed
+//    over units in a fixed order by a separate reduction.
+#include "internal.hpp"
+
+namespace rib {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+constexpr int kTile = 64;          // streamed tile (queries in dkv, keys in dq)
+constexpr int kPerBlock = 256;     // owned keys (dkv) / queries (dq) per workgroup
+
+template <int KP>
+struct BwdCfg {
+  static constexpr int kSteps = 2 + KP;           // 16-channel steps of [content | pos]
+  static constexpr int kRowC = 2 * kSteps + 1;    // chunks per Q_hat / K_hat row (+1 pad)
+  static constexpr int kDRow = 5;                 // chunks per dO / V row (4 + 1 pad)
+  static constexpr int kTRow = kTile / 8 + 1;     // chunks per transposed row (8 + 1 pad)
+  static constexpr int kPosRows = 16 * KP;
+  static constexpr int kTRows = 32 + kPosRows;    // rows of a transposed [content | pos] tile
+};
+
+__device__ __forceinline__ bf16x8 lds_frag(const u32x4* p) { return __builtin_bit_cast(bf16x8, *p); }
+
+__device__ __forceinline__ bf16x8 zero_frag() { return __builtin_bit_cast(bf16x8, u32x4(0u)); }
+
+// Loads the lane's 8 channels (16s + 8h ..) of row `row` of a [content 32 | pos rp] token.
+template <int KP>
+__device__ __forceinline__ bf16x8 token_frag(const bf16* content, const bf16* pos, int64_t row, int s, int half) {
+  constexpr int rp = 16 * KP;
+  u32x4 v;
+  if (s < 2) v = *(const u32x4*)(content + row * 32 + s * 16 + half * 8);
+  else v = *(const u32x4*)(pos + row * rp + (s - 2) * 16 + half * 8);
+  return __builtin_bit_cast(bf16x8, v);
+}
+
+// ------------------------------------------------------------------ dK, dV
+template <int KP>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
+  typedef BwdCfg<KP> C;
+  __shared__ u32x4 sQ[2][kTile * C::kRowC];
+  __shared__ u32x4 sDo[2][kTile * C::kDRow];
+  __shared__ u32x4 sQt[2][C::kTRows * C::kTRow];
+  __shared__ u32x4 sDot[2][32 * C::kTRow];
+  __shared__ float sL[2][kTile];
+  __shared__ float sD[2][kTile];
+
+  const Geom& g = a.g;
+  const int N = g.N, n_rows = g.n_rows;
+  const int nkb = (N + kPerBlock - 1) / kPerBlock;
+  const int logical = xcd_remap(blockIdx.x, g.units * nkb);
+  const int unit = logical / nkb;
+  const int kb = logical - unit * nkb;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  constexpr int rp = 16 * KP;
+
+  const int64_t ub = (int64_t)unit * n_rows;
+  const bf16* qw = (const bf16*)a.qw + ub * 32;
+  const bf16* kw = (const bf16*)a.kw + ub * 32;
+  const bf16* vw = (const bf16*)a.vw + ub * 32;
+  const bf16* dow = (const bf16*)a.dow + ub * 32;
+  const bf16* qt = (const bf16*)a.qt + ub * 32;
+  const bf16* dot = (const bf16*)a.dot + ub * 32;
+  const bf16* qp = (const bf16*)a.qp;
+  const bf16* kp = (const bf16*)a.kp;
+  const bf16* qpt = (const bf16*)a.qpt;
+  const float* lse2 = a.lse2 + ub;
+  const float* dd = a.dd + ub;
+
+  // owned keys: B operands of S = Q_hat K_hat^T and dP = dO V^T
+  const int k0 = kb * kPerBlock + wave * 64;
+  bf16x8 kf[2][C::kSteps], vf[2][2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int key = k0 + nb * 32 + l32;
+    const bool ok = key < N;
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) kf[nb][s] = ok ? token_frag<KP>(kw, kp, key, s, half) : zero_frag();
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      vf[nb][s] = ok ? __builtin_bit_cast(bf16x8, *(const u32x4*)(vw + (int64_t)key * 32 + s * 16 + half * 8))
+                     : zero_frag();
+  }
+
+  f32x16 acc_dv[2], acc_dk[2], acc_dkp[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { acc_dv[nb][i] = 0.f; acc_dk[nb][i] = 0.f; acc_dkp[nb][i] = 0.f; }
+
+  // tile loader (per thread: one chunk of each tile part, pos parts on the first 128*KP threads)
+  const int r_tok = tid >> 2, r_ch = tid & 3;             // row tiles: 64 tokens x 4 chunks
+  const int p_tok = tid / (2 * KP), p_ch = tid % (2 * KP);// pos rows: 64 tokens x 2KP chunks
+  const bool p_on = tid < kTile * 2 * KP;
+  const int t_row = tid >> 3, t_ch = tid & 7;             // transposed tiles: 32 rows x 8 chunks
+  const int tp_row = tid >> 3;                            // pos transposed: rp rows x 8 chunks
+  u32x4 lq, lqp, ldo, lqt, lqpt, ldot;
+  float lfl = 0.f;
+  auto load_tile = [&](int t) {
+    const int q0 = t * kTile;
+    lq = *(const u32x4*)(qw + (int64_t)(q0 + r_tok) * 32 + r_ch * 8);
+    if (p_on) lqp = *(const u32x4*)(qp + (int64_t)(q0 + p_tok) * rp + p_ch * 8);
+    ldo = *(const u32x4*)(dow + (int64_t)(q0 + r_tok) * 32 + r_ch * 8);
+    lqt = *(const u32x4*)(qt + (int64_t)t_row * n_rows + q0 + t_ch * 8);
+    if (p_on) lqpt = *(const u32x4*)(qpt + (int64_t)tp_row * n_rows + q0 + t_ch * 8);
+    ldot = *(const u32x4*)(dot + (int64_t)t_row * n_rows + q0 + t_ch * 8);
+    if (tid < kTile) lfl = lse2[q0 + tid];
+    else if (tid < 2 * kTile) lfl = dd[q0 + tid - kTile];
+  };
+  auto store_tile = [&](int buf) {
+    sQ[buf][r_tok * C::kRowC + r_ch] = lq;
+    if (p_on) sQ[buf][p_tok * C::kRowC + 4 + p_ch] = lqp;
+    sDo[buf][r_tok * C::kDRow + r_ch] = ldo;
+    sQt[buf][t_row * C::kTRow + t_ch] = lqt;
+    if (p_on) sQt[buf][(32 + tp_row) * C::kTRow + t_ch] = lqpt;
+    sDot[buf][t_row * C::kTRow + t_ch] = ldot;
+    if (tid < kTile) sL[buf][tid] = lfl;
+    else if (tid < 2 * kTile) sD[buf][tid - kTile] = lfl;
+  };
+
+  const float c = a.c;
+  const int nqt = (N + kTile - 1) / kTile;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < nqt; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < nqt) load_tile(t + 1);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      bf16x8 qa[C::kSteps], da[2];
+#pragma unroll
+      for (int s = 0; s < C::kSteps; ++s) {
+        const int ch = s < 2 ? 2 * s + half : 4 + 2 * (s - 2) + half;
+        qa[s] = lds_frag(&sQ[buf][(sub * 32 + l32) * C::kRowC + ch]);
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) da[s] = lds_frag(&sDo[buf][(sub * 32 + l32) * C::kDRow + 2 * s + half]);
+      // per-query LSE and D of the lane's 16 accumulator rows
+      float lrow[16], drow[16];
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int qi = sub * 32 + 8 * gq + 4 * half;
+        const f32x4 l4 = *(const f32x4*)&sL[buf][qi];
+        const f32x4 d4 = *(const f32x4*)&sD[buf][qi];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) { lrow[4 * gq + i] = l4[i]; drow[4 * gq + i] = d4[i]; }
+      }
+      bf16x8 dta[2], qta[2], qpta[2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const int ch = 4 * sub + 2 * s + half;
+        dta[s] = lds_frag(&sDot[buf][l32 * C::kTRow + ch]);
+        qta[s] = lds_frag(&sQt[buf][l32 * C::kTRow + ch]);
+        qpta[s] = l32 < C::kPosRows ? lds_frag(&sQt[buf][(32 + l32) * C::kTRow + ch]) : zero_frag();
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        f32x16 sc, dp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { sc[i] = 0.f; dp[i] = 0.f; }
+#pragma unroll
+        for (int s = 0; s < C::kSteps; ++s) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[nb][s], sc, 0, 0, 0);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[s], vf[nb][s], dp, 0, 0, 0);
+        bf16x8 pb[2], sb[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int v = 8 * s + j;
+            const float p = exp2f(fmaf(sc[v], c, -lrow[v]));
+            pb[s][j] = f32_to_bf16(p);
+            sb[s][j] = f32_to_bf16(p * (dp[v] - drow[v]));
+          }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          acc_dv[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dta[s], pb[s], acc_dv[nb], 0, 0, 0);
+          acc_dk[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta[s], sb[s], acc_dk[nb], 0, 0, 0);
+          acc_dkp[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qpta[s], sb[s], acc_dkp[nb], 0, 0, 0);
+        }
+      }
+    }
+    if (t + 1 < nqt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // epilogue: lane = key, accumulator rows = channels 8(v/4) + 4h + v%4
+  bf16* dkw = (bf16*)a.dkw + ub * 32;
+  bf16* dvw = (bf16*)a.dvw + ub * 32;
+  float* dkp = a.dkp_part + ub * rp;
+  const float scale = a.scale;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int key = k0 + nb * 32 + l32;
+    if (key >= N) continue;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      bf16 v4[4], k4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v4[i] = f32_to_bf16(acc_dv[nb][4 * gq + i]);
+        k4[i] = f32_to_bf16(acc_dk[nb][4 * gq + i] * scale);
+      }
+      const int ch = 8 * gq + 4 * half;
+      *(uint2*)(dvw + (int64_t)key * 32 + ch) = *(const uint2*)v4;
+      *(uint2*)(dkw + (int64_t)key * 32 + ch) = *(const uint2*)k4;
+      if (ch < rp) {
+        f32x4 p4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p4[i] = acc_dkp[nb][4 * gq + i] * scale;
+        *(f32x4*)(dkp + (int64_t)key * rp + ch) = p4;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ dQ
+template <int KP>
+__global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
+  typedef BwdCfg<KP> C;
+  __shared__ u32x4 sK[2][kTile * C::kRowC];
+  __shared__ u32x4 sV[2][kTile * C::kDRow];
+  __shared__ u32x4 sKt[2][C::kTRows * C::kTRow];
+
+  const Geom& g = a.g;
+  const int N = g.N, n_rows = g.n_rows;
+  const int nqb = (N + kPerBlock - 1) / kPerBlock;
+  const int logical = xcd_remap(blockIdx.x, g.units * nqb);
+  const int unit = logical / nqb;
+  const int qb = logical - unit * nqb;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  constexpr int rp = 16 * KP;
+
+  const int64_t ub = (int64_t)unit * n_rows;
+  const bf16* qw = (const bf16*)a.qw + ub * 32;
+  const bf16* kw = (const bf16*)a.kw + ub * 32;
+  const bf16* vw = (const bf16*)a.vw + ub * 32;
+  const bf16* dow = (const bf16*)a.dow + ub * 32;
+  const bf16* kt = (const bf16*)a.kt + ub * 32;
+  const bf16* qp = (const bf16*)a.qp;
+  const bf16* kp = (const bf16*)a.kp;
+  const bf16* kpt = (const bf16*)a.kpt;
+
+  // owned queries: B operands of S^T = K_hat Q_hat^T and dP^T = V dO^T
+  const int q0 = qb * kPerBlock + wave * 64;
+  bf16x8 qf[2][C::kSteps], df[2][2];
+  float l2q[2], dq_d[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int q = q0 + nb * 32 + l32;
+    const bool ok = q < N;
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) qf[nb][s] = ok ? token_frag<KP>(qw, qp, q, s, half) : zero_frag();
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+      df[nb][s] = ok ? __builtin_bit_cast(bf16x8, *(const u32x4*)(dow + (int64_t)q * 32 + s * 16 + half * 8))
+                     : zero_frag();
+    l2q[nb] = ok ? a.lse2[ub + q] : INFINITY;
+    dq_d[nb] = ok ? a.dd[ub + q] : 0.f;
+  }
+
+  f32x16 acc_dq[2], acc_dqp[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { acc_dq[nb][i] = 0.f; acc_dqp[nb][i] = 0.f; }
+
+  const int r_tok = tid >> 2, r_ch = tid & 3;
+  const int p_tok = tid / (2 * KP), p_ch = tid % (2 * KP);
+  const bool p_on = tid < kTile * 2 * KP;
+  const int t_row = tid >> 3, t_ch = tid & 7;
+  u32x4 lk, lkp, lv, lkt, lkpt;
+  auto load_tile = [&](int t) {
+    const int k0 = t * kTile;
+    lk = *(const u32x4*)(kw + (int64_t)(k0 + r_tok) * 32 + r_ch * 8);
+    if (p_on) lkp = *(const u32x4*)(kp + (int64_t)(k0 + p_tok) * rp + p_ch * 8);
+    lv = *(const u32x4*)(vw + (int64_t)(k0 + r_tok) * 32 + r_ch * 8);
+    lkt = *(const u32x4*)(kt + (int64_t)t_row * n_rows + k0 + t_ch * 8);
+    if (p_on) lkpt = *(const u32x4*)(kpt + (int64_t)t_row * n_rows + k0 + t_ch * 8);
+  };
+  auto store_tile = [&](int buf) {
+    sK[buf][r_tok * C::kRowC + r_ch] = lk;
+    if (p_on) sK[buf][p_tok * C::kRowC + 4 + p_ch] = lkp;
+    sV[buf][r_tok * C::kDRow + r_ch] = lv;
+    sKt[buf][t_row * C::kTRow + t_ch] = lkt;
+    if (p_on) sKt[buf][(32 + t_row) * C::kTRow + t_ch] = lkpt;
+  };
+
+  const float c = a.c;
+  const int nkt = (N + kTile - 1) / kTile;
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < nkt; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < nkt) load_tile(t + 1);
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      bf16x8 ka[C::kSteps], va[2], kta[2], kpta[2];
+#pragma unroll
+      for (int s = 0; s < C::kSteps; ++s) {
+        const int ch = s < 2 ? 2 * s + half : 4 + 2 * (s - 2) + half;
+        ka[s] = lds_frag(&sK[buf][(sub * 32 + l32) * C::kRowC + ch]);
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        va[s] = lds_frag(&sV[buf][(sub * 32 + l32) * C::kDRow + 2 * s + half]);
+        const int ch = 4 * sub + 2 * s + half;
+        kta[s] = lds_frag(&sKt[buf][l32 * C::kTRow + ch]);
+        kpta[s] = l32 < C::kPosRows ? lds_frag(&sKt[buf][(32 + l32) * C::kTRow + ch]) : zero_frag();
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        f32x16 sc, dp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) { sc[i] = 0.f; dp[i] = 0.f; }
+#pragma unroll
+        for (int s = 0; s < C::kSteps; ++s) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[nb][s], sc, 0, 0, 0);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s], df[nb][s], dp, 0, 0, 0);
+        bf16x8 sb[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int v = 8 * s + j;
+            const float p = exp2f(fmaf(sc[v], c, -l2q[nb]));
+            sb[s][j] = f32_to_bf16(p * (dp[v] - dq_d[nb]));
+          }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          acc_dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta[s], sb[s], acc_dq[nb], 0, 0, 0);
+          acc_dqp[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kpta[s], sb[s], acc_dqp[nb], 0, 0, 0);
+        }
+      }
+    }
+    if (t + 1 < nkt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  bf16* dqw = (bf16*)a.dqw + ub * 32;
+  float* dqp = a.dqp_part + ub * rp;
+  const float scale = a.scale;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int q = q0 + nb * 32 + l32;
+    if (q >= N) continue;
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      bf16 q4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q4[i] = f32_to_bf16(acc_dq[nb][4 * gq + i] * scale);
+      const int ch = 8 * gq + 4 * half;
+      *(uint2*)(dqw + (int64_t)q * 32 + ch) = *(const uint2*)q4;
+      if (ch < rp) {
+        f32x4 p4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) p4[i] = acc_dqp[nb][4 * gq + i] * scale;
+        *(f32x4*)(dqp + (int64_t)q * rp + ch) = p4;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ prep
+template <typename T>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, PixelMap pm, const T* __restrict__ o,
+                                                       const T* __restrict__ d_o, const float* __restrict__ lse,
+                                                       float* __restrict__ dd, float* __restrict__ lse2) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t total = (int64_t)g.units * g.n_rows;
+  if (i >= total) return;
+  const int unit = (int)(i / g.n_rows);
+  const int t = (int)(i - (int64_t)unit * g.n_rows);
+  if (t >= g.N) {
+    dd[i] = 0.f;
+    lse2[i] = INFINITY;
+    return;
+  }
+  const int64_t ph = pm.pixel_head(unit, t);
+  const T* orow = o + ph * 32;
+  const T* grow = d_o + ph * 32;
+  float acc = 0.f;
+#pragma unroll
+  for (int ch = 0; ch < 32; ++ch) acc = fmaf((float)orow[ch], (float)grow[ch], acc);
+  dd[i] = acc;
+  lse2[i] = lse[ph] * 1.44269504088896340736f;
+}
+
+// ------------------------------------------------------------------ float32
+// dK, dV: one thread per key, query tiles of 64 in LDS.
+template <int RP>
+__global__ __launch_bounds__(256) void attn_bwd_dkv_f32_kernel(BwdArgs a) {
+  constexpr int D = 32, DH = D + RP;
+  __shared__ float sQ[kTile][DH + 1];
+  __shared__ float sDo[kTile][D + 1];
+  __shared__ float sL[kTile], sD[kTile];
+  const Geom& g = a.g;
+  const int N = g.N, n_rows = g.n_rows;
+  const int nkb = (N + 255) / 256;
+  const int unit = blockIdx.x / nkb;
+  const int key = (blockIdx.x - unit * nkb) * 256 + threadIdx.x;
+  const int64_t ub = (int64_t)unit * n_rows;
+  const float* qw = (const float*)a.qw + ub * D;
+  const float* dow = (const float*)a.dow + ub * D;
+  const float* qp = (const float*)a.qp;
+  const int kk = key < N ? key : 0;
+  float kh[DH], vv[D], gk[DH], gv[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) { kh[i] = ((const float*)a.kw)[(ub + kk) * D + i]; vv[i] = ((const float*)a.vw)[(ub + kk) * D + i]; }
+#pragma unroll
+  for (int i = 0; i < RP; ++i) kh[D + i] = ((const float*)a.kp)[(int64_t)kk * RP + i];
+#pragma unroll
+  for (int i = 0; i < DH; ++i) gk[i] = 0.f;
+#pragma unroll
+  for (int i = 0; i < D; ++i) gv[i] = 0.f;
+  const float c = a.c;
+  const int nqt = (N + kTile - 1) / kTile;
+  for (int t = 0; t < nqt; ++t) {
+    const int q0 = t * kTile;
+    for (int i = threadIdx.x; i < kTile * DH; i += 256) {
+      int r = i / DH, ch = i - r * DH;
+      sQ[r][ch] = ch < D ? qw[(int64_t)(q0 + r) * D + ch] : qp[(int64_t)(q0 + r) * RP + ch - D];
+    }
+    for (int i = threadIdx.x; i < kTile * D; i += 256) {
+      int r = i / D, ch = i - r * D;
+      sDo[r][ch] = dow[(int64_t)(q0 + r) * D + ch];
+    }
+    if (threadIdx.x < kTile) {
+      sL[threadIdx.x] = a.lse2[ub + q0 + threadIdx.x];
+      sD[threadIdx.x] = a.dd[ub + q0 + threadIdx.x];
+    }
+    __syncthreads();
+    for (int r = 0; r < kTile; ++r) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int i = 0; i < DH; ++i) s = fmaf(sQ[r][i], kh[i], s);
+#pragma unroll
+      for (int i = 0; i < D; ++i) dp = fmaf(sDo[r][i], vv[i], dp);
+      const float p = exp2f(fmaf(s, c, -sL[r]));
+      const float ds = p * (dp - sD[r]);
+#pragma unroll
+      for (int i = 0; i < D; ++i) gv[i] = fmaf(p, sDo[r][i], gv[i]);
+#pragma unroll
+      for (int i = 0; i < DH; ++i) gk[i] = fmaf(ds, sQ[r][i], gk[i]);
+    }
+    __syncthreads();
+  }
+  if (key < N) {
+    float* dkw = (float*)a.dkw + (ub + key) * D;
+    float* dvw = (float*)a.dvw + (ub + key) * D;
+#pragma unroll
+    for (int i = 0; i < D; ++i) { dkw[i] = gk[i] * a.scale; dvw[i] = gv[i]; }
+#pragma unroll
+    for (int i = 0; i < RP; ++i) a.dkp_part[(ub + key) * RP + i] = gk[D + i] * a.scale;
+  }
+}
+
+// dQ: one thread per query, key tiles of 64 in LDS.
+template <int RP>
+__global__ __launch_bounds__(256) void attn_bwd_dq_f32_kernel(BwdArgs a) {
+  constexpr int D = 32, DH = D + RP;
+  __shared__ float sK[kTile][DH + 1];
+  __shared__ float sV[kTile][D + 1];
+  const Geom& g = a.g;
+  const int N = g.N, n_rows = g.n_rows;
+  const int nqb = (N + 255) / 256;
+  const int unit = blockIdx.x / nqb;
+  const int q = (blockIdx.x - unit * nqb) * 256 + threadIdx.x;
+  const int64_t ub = (int64_t)unit * n_rows;
+  const float* kw = (const float*)a.kw + ub * D;
+  const float* vw = (const float*)a.vw + ub * D;
+  const float* kp = (const float*)a.kp;
+  const int qq = q < N ? q : 0;
+  float qh[DH], gd[D], gq[DH];
+#pragma unroll
+  for (int i = 0; i < D; ++i) { qh[i] = ((const float*)a.qw)[(ub + qq) * D + i]; gd[i] = ((const float*)a.dow)[(ub + qq) * D + i]; }
+#pragma unroll
+  for (int i = 0; i < RP; ++i) qh[D + i] = ((const float*)a.qp)[(int64_t)qq * RP + i];
+#pragma unroll
+  for (int i = 0; i < DH; ++i) gq[i] = 0.f;
+  const float l2 = a.lse2[ub + qq], dq_d = a.dd[ub + qq];
+  const float c = a.c;
+  const int nkt = (N + kTile - 1) / kTile;
+  for (int t = 0; t < nkt; ++t) {
+    const int k0 = t * kTile;
+    for (int i = threadIdx.x; i < kTile * DH; i += 256) {
+      int r = i / DH, ch = i - r * DH;
+      sK[r][ch] = ch < D ? kw[(int64_t)(k0 + r) * D + ch] : kp[(int64_t)(k0 + r) * RP + ch - D];
+    }
+    for (int i = threadIdx.x; i < kTile * D; i += 256) {
+      int r = i / D, ch = i - r * D;
+      sV[r][ch] = vw[(int64_t)(k0 + r) * D + ch];
+    }
+    __syncthreads();
+    const int nk = min(kTile, N - k0);
+    for (int r = 0; r < nk; ++r) {
+      float s = 0.f, dp = 0.f;
+#pragma unroll
+      for (int i = 0; i < DH; ++i) s = fmaf(qh[i], sK[r][i], s);
+#pragma unroll
+      for (int i = 0; i < D; ++i) dp = fmaf(gd[i], sV[r][i], dp);
+      const float p = exp2f(fmaf(s, c, -l2));
+      const float ds = p * (dp - dq_d);
+#pragma unroll
+      for (int i = 0; i < DH; ++i) gq[i] = fmaf(ds, sK[r][i], gq[i]);
+    }
+    __syncthreads();
+  }
+  if (q < N) {
+    float* dqw = (float*)a.dqw + (ub + q) * D;
+#pragma unroll
+    for (int i = 0; i < D; ++i) dqw[i] = gq[i] * a.scale;
+#pragma unroll
+    for (int i = 0; i < RP; ++i) a.dqp_part[(ub + q) * RP + i] = gq[D + i] * a.scale;
+  }
+}
+
+// ------------------------------------------------------------------ reduction
+// out[t][j] = sum over units (in unit order, per slice) of part[u][t][j]; 8 unit
+// slices per column are combined in slice order: a fixed summation order.
+__global__ __launch_bounds__(256) void reduce_pos_grads_kernel(int units, int N, int n_rows, int r, int rp,
+                                                               const float* __restrict__ part, float* __restrict__ out) {
+  __shared__ float red[8][32];
+  const int col = blockIdx.x * 32 + (threadIdx.x & 31);
+  const int slice = threadIdx.x >> 5;
+  const int ncols = N * rp;
+  float acc = 0.f;
+  if (col < ncols)
+    for (int u = slice; u < units; u += 8) acc += part[(int64_t)u * n_rows * rp + col];
+  red[slice][threadIdx.x & 31] = acc;
+  __syncthreads();
+  if (slice == 0 && col < ncols) {
+    float s = red[0][threadIdx.x];
+#pragma unroll
+    for (int k = 1; k < 8; ++k) s += red[k][threadIdx.x];
+    const int t = col / rp, j = col - t * rp;
+    if (j < r) out[(int64_t)t * r + j] = s;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_bwd_prep(const Geom& g, int esize, const void* o, const void* d_o, const float* lse, float* dd,
+                           float* lse2, hipStream_t stream) {
+  const int64_t total = (int64_t)g.units * g.n_rows;
+  if (total == 0) return hipSuccess;
+  dim3 grid((unsigned)((total + 255) / 256));
+  if (esize == 2)
+    hipLaunchKernelGGL(bwd_prep_kernel<bf16>, grid, dim3(256), 0, stream, g, make_pixel_map(g), (const bf16*)o,
+                       (const bf16*)d_o, lse, dd, lse2);
+  else
+    hipLaunchKernelGGL(bwd_prep_kernel<float>, grid, dim3(256), 0, stream, g, make_pixel_map(g), (const float*)o,
+                       (const float*)d_o, lse, dd, lse2);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
+  const int nb = (a.g.N + kPerBlock - 1) / kPerBlock;
+  const int64_t blocks = (int64_t)a.g.units * nb;
+  if (blocks == 0) return hipSuccess;
+  if (a.rp == 16) {
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(attn_bwd_dkv_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dq_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_f32(const BwdArgs& a, hipStream_t stream) {
+  const int nb = (a.g.N + 255) / 256;
+  const int64_t blocks = (int64_t)a.g.units * nb;
+  if (blocks == 0) return hipSuccess;
+  if (a.rp == 16) {
+    hipLaunchKernelGGL(attn_bwd_dkv_f32_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(attn_bwd_dkv_f32_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_reduce_pos_grads(int units, int N, int n_rows, int r, int rp, const float* part, float* out,
+                                   hipStream_t stream) {
+  const int ncols = N * rp;
+  hipLaunchKernelGGL(reduce_pos_grads_kernel, dim3((ncols + 31) / 32), dim3(256), 0, stream, units, N, n_rows, r, rp,
+                     part, out);
+  return hipGetLastError();
+}
+
+}  // namespace rib

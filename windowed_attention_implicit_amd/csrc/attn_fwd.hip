@@ -1,0 +1,328 @@
+// RIB window attention, forward, for gfx950.
+//
+// O = softmax(scale * [Q_c | Q_p][K_c | K_p]^T) V per (batch, window, head)
+// unit: the positional tokens are appended channel-wise to the content tokens
+// so the positional bias is part of one dot product and no N x N bias (or
+// score) matrix is ever stored (gist.science/paper/2603.06738, "Technical
+// Summary" §2.A.3-4, "Content + Bias" equation; khansong-paper-with-me.hf.space
+// abstract).
+//
+// bf16 kernel design (CDNA4, wave64, v_mfma_f32_32x32x16_bf16):
+//  * The score tile is computed transposed, S^T = K_hat Q_hat^T: keys are the
+//    MFMA rows, queries the columns, so every lane owns one query and holds 16
+//    of its scores. Row max and row sum are in-lane reductions plus one swap
+//    between the two 32-lane halves.
+//  * The concatenation is virtual: the contraction runs over two 16-channel
+//    content steps (d_c = 32) and one or two 16-channel positional steps
+//    (r padded to 16 / 32 with zeros), K_c and K_p staged side by side in LDS.
+//  * O^T = V^T P^T: P leaves the score accumulator directly as the B operand.
+//    The accumulator holds, for half h of the wave, keys 8(v/4) + 4h + v%4;
+//    V^T is stored with tokens permuted inside every 16-token group (bits 2
+//    and 3 of the token index swapped) so each lane's eight keys are one
+//    contiguous 16-byte LDS read.
+//  * A workgroup is 4 waves x 64 queries; K and V^T tiles of 64 keys are
+//    double-buffered in LDS and shared by the 4 waves; workgroups of one unit
+//    are kept on one XCD (its L2 holds the unit's K and V).
+//  * Online softmax in the log2 domain with a lazy rescale: the running max
+//    only moves (and O, l are only rescaled) when some query's max grows by
+//    more than 2^8, a wave-uniform branch.
+#include "internal.hpp"
+
+namespace rib {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kQPerWave = 64;             // two 32-query MFMA column blocks
+constexpr int kQPerBlock = kWaves * kQPerWave;
+constexpr int kKeyTile = 64;
+constexpr float kLazyTau = 8.0f;          // log2 units
+
+__device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+
+template <int KP>  // positional 16-channel steps: 1 (r <= 16) or 2 (r <= 32)
+struct FwdCfg {
+  static constexpr int kSteps = 2 + KP;             // MFMA K-steps of the score
+  static constexpr int kKRow = 2 * kSteps + 1;      // 16-byte chunks per K row in LDS (+1 pad)
+  static constexpr int kVRow = kKeyTile / 8 + 1;    // 16-byte chunks per V^T row in LDS (+1 pad)
+  static constexpr int kKChunks = kKeyTile * kKRow;
+  static constexpr int kVChunks = 32 * kVRow;
+};
+
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+template <int KP>
+__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
+  typedef FwdCfg<KP> C;
+  __shared__ u32x4 sK[2][C::kKChunks];
+  __shared__ u32x4 sV[2][C::kVChunks];
+
+  const Geom& g = a.g;
+  const int N = g.N, n_rows = g.n_rows;
+  const int nqb = (N + kQPerBlock - 1) / kQPerBlock;
+  const int total = g.units * nqb;
+  const int logical = xcd_remap(blockIdx.x, total);
+  const int unit = logical / nqb;
+  const int qb = logical - unit * nqb;
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, l32 = lane & 31;
+  const int rp = 16 * KP;
+
+  const bf16* qw = (const bf16*)a.qw + (int64_t)unit * n_rows * 32;
+  const bf16* kw = (const bf16*)a.kw + (int64_t)unit * n_rows * 32;
+  const bf16* vt = (const bf16*)a.vw + (int64_t)unit * 32 * n_rows;
+  const bf16* qp = (const bf16*)a.qp;
+  const bf16* kp = (const bf16*)a.kp;
+
+  // ---- query fragments (B operand): lane holds 8 channels of its query per step
+  const int q0 = qb * kQPerBlock + wave * kQPerWave;
+  bf16x8 qf[2][C::kSteps];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int q = q0 + nb * 32 + l32;
+    const bool ok = q < N;
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) {
+      u32x4 v = u32x4(0u);
+      if (ok) {
+        if (s < 2) v = *(const u32x4*)(qw + (int64_t)q * 32 + s * 16 + half * 8);
+        else v = *(const u32x4*)(qp + (int64_t)q * rp + (s - 2) * 16 + half * 8);
+      }
+      qf[nb][s] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  // ---- tile loader: each thread moves up to three 16-byte chunks per tile
+  const int nkt = (N + kKeyTile - 1) / kKeyTile;
+  u32x4 ldK, ldKp, ldV;
+  const int kc_key = tid >> 2, kc_ch = tid & 3;                // K content: 64 keys x 4 chunks
+  const int kp_key = tid / (2 * KP), kp_ch = tid % (2 * KP);    // K pos: 64 keys x 2KP chunks
+  const bool kp_active = tid < kKeyTile * 2 * KP;
+  const int v_row = tid >> 3, v_ch = tid & 7;                   // V^T: 32 rows x 8 chunks
+  auto load_tile = [&](int t) {
+    const int k0 = t * kKeyTile;
+    ldK = *(const u32x4*)(kw + (int64_t)(k0 + kc_key) * 32 + kc_ch * 8);
+    if (kp_active) ldKp = *(const u32x4*)(kp + (int64_t)(k0 + kp_key) * rp + kp_ch * 8);
+    ldV = *(const u32x4*)(vt + (int64_t)v_row * n_rows + k0 + v_ch * 8);
+  };
+  auto store_tile = [&](int buf) {
+    sK[buf][kc_key * C::kKRow + kc_ch] = ldK;
+    if (kp_active) sK[buf][kp_key * C::kKRow + 4 + kp_ch] = ldKp;
+    sV[buf][v_row * C::kVRow + v_ch] = ldV;
+  };
+
+  f32x16 acc[2];
+  float m_run[2], l_run[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[nb][i] = 0.f;
+    m_run[nb] = -INFINITY;
+    l_run[nb] = 0.f;
+  }
+  const float c = a.c;
+
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+
+  for (int t = 0; t < nkt; ++t) {
+    const int buf = t & 1;
+    if (t + 1 < nkt) load_tile(t + 1);
+    const bool tail = (t + 1) * kKeyTile > N;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+      // score fragments for 32 keys
+      bf16x8 kf[C::kSteps];
+#pragma unroll
+      for (int s = 0; s < C::kSteps; ++s) {
+        const int ch = s < 2 ? 2 * s + half : 4 + 2 * (s - 2) + half;
+        kf[s] = __builtin_bit_cast(bf16x8, sK[buf][(sub * 32 + l32) * C::kKRow + ch]);
+      }
+      f32x16 sc[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[nb][i] = 0.f;
+#pragma unroll
+        for (int s = 0; s < C::kSteps; ++s)
+          sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[nb][s], sc[nb], 0, 0, 0);
+      }
+      if (tail) {
+        const int kbase = t * kKeyTile + sub * 32 + 4 * half;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = kbase + 8 * (v >> 2) + (v & 3);
+          if (key >= N) { sc[0][v] = -INFINITY; sc[1][v] = -INFINITY; }
+        }
+      }
+      // online softmax (log2 domain), lazy rescale
+      bf16x8 pf[2][2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        float mx = sc[nb][0];
+#pragma unroll
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[nb][v]);
+        mx = fmaxf(mx, swap_halves(mx));
+        const float m_new = fmaxf(m_run[nb], mx * c);
+        if (__any(m_new > m_run[nb] + kLazyTau)) {
+          const float alpha = (m_new == m_run[nb]) ? 1.f : exp2f(m_run[nb] - m_new);
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[nb][i] *= alpha;
+          l_run[nb] *= alpha;
+          m_run[nb] = m_new;
+        }
+        const float mneg = -m_run[nb];
+        float lsum = 0.f;
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float p = exp2f(fmaf(sc[nb][8 * s + j], c, mneg));
+            lsum += p;
+            pf[nb][s][j] = f32_to_bf16(p);
+          }
+        }
+        l_run[nb] += lsum;
+      }
+      // O^T += V^T P^T
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, sV[buf][l32 * C::kVRow + 4 * sub + 2 * s + half]);
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb][s], acc[nb], 0, 0, 0);
+      }
+    }
+    if (t + 1 < nkt) store_tile(buf ^ 1);
+    __syncthreads();
+  }
+
+  // ---- epilogue: normalize, write O rows and LSE
+  bf16* ow = (bf16*)a.ow + (int64_t)unit * n_rows * 32;
+  PixelMap pm = make_pixel_map(g);
+  const float kLn2 = 0.69314718055994530942f;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int q = q0 + nb * 32 + l32;
+    const float l_tot = l_run[nb] + swap_halves(l_run[nb]);
+    const float inv = 1.f / l_tot;
+    if (q < N) {
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        bf16 o4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = f32_to_bf16(acc[nb][4 * gq + i] * inv);
+        *(uint2*)(ow + (int64_t)q * 32 + 8 * gq + 4 * half) = *(const uint2*)o4;
+      }
+      if (a.lse && half == 0) a.lse[pm.pixel_head(unit, q)] = (m_run[nb] + log2f(l_tot)) * kLn2;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// float32 kernel: one thread per query, K/V tiles of 64 keys in LDS, exact
+// online softmax per tile. Used for float32 runs (correctness-sized work).
+template <int RP>
+__global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
+  constexpr int D = 32;
+  constexpr int DH = D + RP;
+  __shared__ float sK[kKeyTile][DH + 1];
+  __shared__ float sV[kKeyTile][D + 1];
+  const Geom& g = a.g;
+  const int N = g.N, n_rows = g.n_rows;
+  const int nqb = (N + 255) / 256;
+  const int unit = blockIdx.x / nqb;
+  const int q = (blockIdx.x - unit * nqb) * 256 + threadIdx.x;
+  const float* qw = (const float*)a.qw + (int64_t)unit * n_rows * D;
+  const float* kw = (const float*)a.kw + (int64_t)unit * n_rows * D;
+  const float* vw = (const float*)a.vw + (int64_t)unit * n_rows * D;
+  const float* qp = (const float*)a.qp;
+  const float* kp = (const float*)a.kp;
+  float qh[DH];
+  const int qq = q < N ? q : 0;
+#pragma unroll
+  for (int i = 0; i < D; ++i) qh[i] = qw[(int64_t)qq * D + i];
+#pragma unroll
+  for (int i = 0; i < RP; ++i) qh[D + i] = qp[(int64_t)qq * RP + i];
+  float o[D];
+#pragma unroll
+  for (int i = 0; i < D; ++i) o[i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  const float c = a.c;
+  const int nkt = (N + kKeyTile - 1) / kKeyTile;
+  for (int t = 0; t < nkt; ++t) {
+    const int k0 = t * kKeyTile;
+    for (int i = threadIdx.x; i < kKeyTile * DH; i += 256) {
+      int kk = i / DH, ch = i - kk * DH;
+      sK[kk][ch] = ch < D ? kw[(int64_t)(k0 + kk) * D + ch] : kp[(int64_t)(k0 + kk) * RP + ch - D];
+    }
+    for (int i = threadIdx.x; i < kKeyTile * D; i += 256) {
+      int kk = i / D, ch = i - kk * D;
+      sV[kk][ch] = vw[(int64_t)(k0 + kk) * D + ch];
+    }
+    __syncthreads();
+    const int nk = min(kKeyTile, N - k0);
+    float s[kKeyTile];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kKeyTile; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < DH; ++i) acc = fmaf(qh[i], sK[j][i], acc);
+      s[j] = j < nk ? acc * c : -INFINITY;
+      mx = fmaxf(mx, s[j]);
+    }
+    const float m_new = fmaxf(m, mx);
+    const float alpha = exp2f(m - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int i = 0; i < D; ++i) o[i] *= alpha;
+    m = m_new;
+#pragma unroll
+    for (int j = 0; j < kKeyTile; ++j) {
+      const float p = exp2f(s[j] - m);
+      l += p;
+#pragma unroll
+      for (int i = 0; i < D; ++i) o[i] = fmaf(p, sV[j][i], o[i]);
+    }
+    __syncthreads();
+  }
+  if (q < N) {
+    float* ow = (float*)a.ow + (int64_t)unit * n_rows * D + (int64_t)q * D;
+    const float inv = 1.f / l;
+#pragma unroll
+    for (int i = 0; i < D; ++i) ow[i] = o[i] * inv;
+    if (a.lse) {
+      PixelMap pm = make_pixel_map(g);
+      a.lse[pm.pixel_head(unit, q)] = (m + log2f(l)) * 0.69314718055994530942f;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
+  const int nqb = (a.g.N + kQPerBlock - 1) / kQPerBlock;
+  const int64_t blocks = (int64_t)a.g.units * nqb;
+  if (blocks == 0) return hipSuccess;
+  if (a.rp == 16)
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_fwd_bf16_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream) {
+  const int nqb = (a.g.N + 255) / 256;
+  const int64_t blocks = (int64_t)a.g.units * nqb;
+  if (blocks == 0) return hipSuccess;
+  if (a.rp == 16)
+    hipLaunchKernelGGL(attn_fwd_f32_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(attn_fwd_f32_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace rib

@@ -1,0 +1,86 @@
+// Launchers shared between the kernel files and the C-ABI layer. Every
+// launcher only enqueues work on `stream` and returns hipGetLastError().
+#pragma once
+
+#include "common.hpp"
+
+namespace rib {
+
+// Window-layout codes of the gather/scatter kernels.
+enum class WinLayout {
+  kRows,       // [units][n_rows][d]     token-major rows, rows >= N zero
+  kTransKappa  // [units][d][n_rows]     channel-major; inside every group of 16
+               //                        tokens the positions are permuted by
+               //                        swapping bits 2 and 3 of the token index
+};
+
+hipError_t launch_posgen(int w, const rib_mlp_t& mlp, rib_dtype_t out_dtype, void* q_p, void* k_p,
+                         hipStream_t stream);
+
+// x [B,H,W,heads,d] -> windowed buffer in `layout` (rows >= N zero-filled).
+hipError_t launch_partition(const Geom& g, int esize, WinLayout layout, const void* x, void* xw,
+                            hipStream_t stream);
+// windowed kRows buffer -> x [B,H,W,heads,d].
+hipError_t launch_unpartition(const Geom& g, int esize, const void* xw, void* x, hipStream_t stream);
+// Public plain gather / scatter ([units][N][d], no padding).
+hipError_t launch_partition_plain(const Geom& g, int esize, const void* x, void* xw, hipStream_t stream);
+hipError_t launch_unpartition_plain(const Geom& g, int esize, const void* xw, void* x, hipStream_t stream);
+
+// [N, r] positional tokens -> [n_rows, rp] zero-padded copy in `out_esize`
+// precision (rows >= N and columns >= r zero). In and out may differ in type.
+hipError_t launch_pack_pos(int N, int n_rows, int r, int rp, int in_esize, const void* in, int out_esize,
+                           void* out, hipStream_t stream);
+// Transposed, kappa-permuted copy of a padded [n_rows, rp] bf16 buffer: [rp, n_rows].
+hipError_t launch_pos_transpose(int n_rows, int rp, const void* in, void* out, hipStream_t stream);
+
+struct FwdArgs {
+  Geom g;
+  float c;              // scale * log2(e)
+  const void* qw;       // [units][n_rows][32]
+  const void* kw;       // [units][n_rows][32]
+  const void* vw;       // bf16: [units][32][n_rows] kappa layout; f32: [units][n_rows][32]
+  const void* qp;       // [n_rows][rp]
+  const void* kp;       // [n_rows][rp]
+  void* ow;             // [units][n_rows][32]
+  float* lse;           // [B,H,W,heads] or nullptr
+  int rp;               // padded rank, 16 or 32
+};
+hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream);
+
+struct BwdArgs {
+  Geom g;
+  float c;              // scale * log2(e)
+  float scale;
+  int rp;
+  // windowed inputs
+  const void* qw;       // [units][n_rows][32] rows
+  const void* kw;       // [units][n_rows][32] rows
+  const void* vw;       // [units][n_rows][32] rows
+  const void* dow;      // [units][n_rows][32] rows
+  const void* qt;       // [units][32][n_rows] kappa (bf16 only)
+  const void* kt;       // [units][32][n_rows] kappa (bf16 only)
+  const void* dot;      // [units][32][n_rows] kappa (bf16 only)
+  const void* qp;       // [n_rows][rp]
+  const void* kp;       // [n_rows][rp]
+  const void* qpt;      // [rp][n_rows] kappa (bf16 only)
+  const void* kpt;      // [rp][n_rows] kappa (bf16 only)
+  const float* lse2;    // [units][n_rows]  log2-domain LSE
+  const float* dd;      // [units][n_rows]  D_i = sum_c dO_ic O_ic
+  // outputs (windowed)
+  void* dqw;            // [units][n_rows][32]
+  void* dkw;            // [units][n_rows][32]
+  void* dvw;            // [units][n_rows][32]
+  float* dqp_part;      // [units][n_rows][rp]
+  float* dkp_part;      // [units][n_rows][rp]
+};
+// D and log2-domain LSE in windowed order, from O, dO and LSE in map layout.
+hipError_t launch_bwd_prep(const Geom& g, int esize, const void* o, const void* d_o, const float* lse,
+                           float* dd, float* lse2, hipStream_t stream);
+hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_bwd_f32(const BwdArgs& a, hipStream_t stream);
+// Fixed-order sum over units of [units][n_rows][rp] partials -> [N][r] float32.
+hipError_t launch_reduce_pos_grads(int units, int N, int n_rows, int r, int rp, const float* part, float* out,
+                                   hipStream_t stream);
+
+}  // namespace rib

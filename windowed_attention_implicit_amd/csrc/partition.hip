@@ -1,0 +1,202 @@
+// Window partition / unpartition gathers for gfx950.
+//
+// The pages use non-overlapping square windows (gist.science/paper/2603.06738,
+// "Technical Summary" §3.2: windows up to 96 x 96) but never describe the
+// split; this library takes windows row-major per image, token t = iy*w + ix
+// inside a window, heads innermost.
+//
+// A [B, H, W, heads, d] map stores, for every pixel, heads*d contiguous
+// channels; one window row of one head is w runs of d channels. The kernels
+// walk the map in its own memory order (16-byte chunks, fully coalesced on the
+// map side) and scatter / gather whole d-channel runs (64 bytes for bf16,
+// d = 32) on the windowed side. Padded rows (t >= N) of the internal buffers
+// are written as zeros by extra threads of the same launch.
+#include "internal.hpp"
+
+namespace rib {
+namespace {
+
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+struct ChunkGeom {
+  int H, W, heads, w, nwy, nwx;
+  int cpr;          // 16-byte chunks per d-channel row
+  int n_rows;       // rows per unit on the windowed side
+  int N;
+};
+
+__device__ __forceinline__ void decode_pixel_chunk(const ChunkGeom& g, int64_t i, int64_t& u, int& t, int& c) {
+  c = (int)(i % g.cpr);
+  int64_t ph = i / g.cpr;
+  int head = (int)(ph % g.heads);
+  int64_t pix = ph / g.heads;
+  int x = (int)(pix % g.W);
+  int64_t rest = pix / g.W;
+  int y = (int)(rest % g.H);
+  int64_t b = rest / g.H;
+  int wx = x / g.w, ix = x - wx * g.w;
+  int wy = y / g.w, iy = y - wy * g.w;
+  u = ((b * g.nwy + wy) * g.nwx + wx) * g.heads + head;
+  t = iy * g.w + ix;
+}
+
+// map -> rows layout; threads past the map's chunks zero the padded rows.
+__global__ __launch_bounds__(256) void gather_rows_kernel(ChunkGeom g, int64_t map_chunks, int64_t pad_chunks,
+                                                          const u32x4* __restrict__ x, u32x4* __restrict__ xw) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < map_chunks) {
+    int64_t u; int t, c;
+    decode_pixel_chunk(g, i, u, t, c);
+    xw[(u * g.n_rows + t) * g.cpr + c] = __builtin_nontemporal_load(x + i);
+  } else if (i < map_chunks + pad_chunks) {
+    int64_t j = i - map_chunks;
+    int pad = g.n_rows - g.N;
+    int c = (int)(j % g.cpr);
+    int64_t r = j / g.cpr;
+    int64_t u = r / pad;
+    int t = g.N + (int)(r % pad);
+    xw[(u * g.n_rows + t) * g.cpr + c] = u32x4(0u);
+  }
+}
+
+// rows layout -> map.
+__global__ __launch_bounds__(256) void scatter_rows_kernel(ChunkGeom g, int64_t map_chunks,
+                                                           const u32x4* __restrict__ xw, u32x4* __restrict__ x) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= map_chunks) return;
+  int64_t u; int t, c;
+  decode_pixel_chunk(g, i, u, t, c);
+  __builtin_nontemporal_store(xw[(u * g.n_rows + t) * g.cpr + c], x + i);
+}
+
+// Position inside a 16-token group after swapping bits 2 and 3 (an involution).
+__device__ __forceinline__ int kappa16(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
+
+// map -> channel-major kappa layout [units][32][n_rows], bf16, d = 32. One block
+// per (unit, 64-token group): 64 tokens x 64 bytes are staged in LDS, then
+// every thread writes 8 consecutive kappa positions of one channel.
+__global__ __launch_bounds__(256) void gather_trans_kappa_kernel(PixelMap pm, int N, int n_rows,
+                                                                 const bf16* __restrict__ x, bf16* __restrict__ xt) {
+  __shared__ bf16 tile[64][32 + 2];
+  const int groups = n_rows / 64;
+  const int u = blockIdx.x / groups;
+  const int g0 = (blockIdx.x - u * groups) * 64;
+  const int tid = threadIdx.x;
+  {
+    const int tok = tid >> 2, c = tid & 3;
+    const int t = g0 + tok;
+    u32x4 v = u32x4(0u);
+    if (t < N) v = *(const u32x4*)(x + pm.pixel_head(u, t) * 32 + c * 8);
+    const bf16* pv = (const bf16*)&v;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[tok][c * 8 + j] = pv[j];
+  }
+  __syncthreads();
+  const int d = tid >> 3, pc = tid & 7;
+  bf16 vals[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int p = pc * 8 + j;
+    const int tok = (p & ~15) | kappa16(p & 15);
+    vals[j] = tile[tok][d];
+  }
+  *(u32x4*)(xt + ((int64_t)u * 32 + d) * n_rows + g0 + pc * 8) = *(const u32x4*)vals;
+}
+
+template <typename InT, typename OutT>
+__global__ void pack_pos_kernel(int N, int n_rows, int r, int rp, const InT* __restrict__ in, OutT* __restrict__ out) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_rows * rp) return;
+  int t = i / rp, j = i - t * rp;
+  float v = (t < N && j < r) ? (float)in[(int64_t)t * r + j] : 0.f;
+  out[i] = (OutT)v;
+}
+
+__global__ void pos_transpose_kernel(int n_rows, int rp, const bf16* __restrict__ in, bf16* __restrict__ out) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n_rows * rp) return;
+  int j = i / n_rows, p = i - j * n_rows;
+  int t = (p & ~15) | kappa16(p & 15);
+  out[i] = in[(int64_t)t * rp + j];
+}
+
+ChunkGeom chunk_geom(const Geom& g, int esize, int n_rows) {
+  ChunkGeom c;
+  c.H = g.H; c.W = g.W; c.heads = g.heads; c.w = g.w; c.nwy = g.nwy; c.nwx = g.nwx;
+  c.cpr = g.d_c * esize / 16;
+  c.n_rows = n_rows;
+  c.N = g.N;
+  return c;
+}
+
+int64_t blocks_for(int64_t n, int threads) { return (n + threads - 1) / threads; }
+
+}  // namespace
+
+hipError_t launch_partition(const Geom& g, int esize, WinLayout layout, const void* x, void* xw, hipStream_t stream) {
+  if (layout == WinLayout::kRows) {
+    ChunkGeom c = chunk_geom(g, esize, g.n_rows);
+    int64_t map_chunks = (int64_t)g.B * g.H * g.W * g.heads * c.cpr;
+    int64_t pad_chunks = (int64_t)g.units * (g.n_rows - g.N) * c.cpr;
+    int64_t n = map_chunks + pad_chunks;
+    if (n == 0) return hipSuccess;
+    hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks_for(n, 256)), dim3(256), 0, stream, c, map_chunks,
+                       pad_chunks, (const u32x4*)x, (u32x4*)xw);
+  } else {
+    if (g.units == 0) return hipSuccess;
+    hipLaunchKernelGGL(gather_trans_kappa_kernel, dim3((unsigned)((int64_t)g.units * (g.n_rows / 64))), dim3(256), 0,
+                       stream, make_pixel_map(g), g.N, g.n_rows, (const bf16*)x, (bf16*)xw);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_unpartition(const Geom& g, int esize, const void* xw, void* x, hipStream_t stream) {
+  ChunkGeom c = chunk_geom(g, esize, g.n_rows);
+  int64_t map_chunks = (int64_t)g.B * g.H * g.W * g.heads * c.cpr;
+  if (map_chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_rows_kernel, dim3((unsigned)blocks_for(map_chunks, 256)), dim3(256), 0, stream, c,
+                     map_chunks, (const u32x4*)xw, (u32x4*)x);
+  return hipGetLastError();
+}
+
+hipError_t launch_partition_plain(const Geom& g, int esize, const void* x, void* xw, hipStream_t stream) {
+  ChunkGeom c = chunk_geom(g, esize, g.N);
+  int64_t map_chunks = (int64_t)g.B * g.H * g.W * g.heads * c.cpr;
+  if (map_chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks_for(map_chunks, 256)), dim3(256), 0, stream, c,
+                     map_chunks, (int64_t)0, (const u32x4*)x, (u32x4*)xw);
+  return hipGetLastError();
+}
+
+hipError_t launch_unpartition_plain(const Geom& g, int esize, const void* xw, void* x, hipStream_t stream) {
+  ChunkGeom c = chunk_geom(g, esize, g.N);
+  int64_t map_chunks = (int64_t)g.B * g.H * g.W * g.heads * c.cpr;
+  if (map_chunks == 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_rows_kernel, dim3((unsigned)blocks_for(map_chunks, 256)), dim3(256), 0, stream, c,
+                     map_chunks, (const u32x4*)xw, (u32x4*)x);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_pos(int N, int n_rows, int r, int rp, int in_esize, const void* in, int out_esize, void* out,
+                           hipStream_t stream) {
+  const int n = n_rows * rp;
+  dim3 grid((n + 255) / 256), block(256);
+  if (in_esize == 4 && out_esize == 4)
+    hipLaunchKernelGGL((pack_pos_kernel<float, float>), grid, block, 0, stream, N, n_rows, r, rp, (const float*)in, (float*)out);
+  else if (in_esize == 2 && out_esize == 2)
+    hipLaunchKernelGGL((pack_pos_kernel<bf16, bf16>), grid, block, 0, stream, N, n_rows, r, rp, (const bf16*)in, (bf16*)out);
+  else if (in_esize == 4 && out_esize == 2)
+    hipLaunchKernelGGL((pack_pos_kernel<float, bf16>), grid, block, 0, stream, N, n_rows, r, rp, (const float*)in, (bf16*)out);
+  else
+    hipLaunchKernelGGL((pack_pos_kernel<bf16, float>), grid, block, 0, stream, N, n_rows, r, rp, (const bf16*)in, (float*)out);
+  return hipGetLastError();
+}
+
+hipError_t launch_pos_transpose(int n_rows, int rp, const void* in, void* out, hipStream_t stream) {
+  const int n = n_rows * rp;
+  hipLaunchKernelGGL(pos_transpose_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, n_rows, rp, (const bf16*)in,
+                     (bf16*)out);
+  return hipGetLastError();
+}
+
+}  // namespace rib
