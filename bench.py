@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Benchmark of the RIB window-attention hot path on one MI355X (gfx950).
+
+One step is one pass of the forward hot path over the 96x96-window workload
+(batch 4, 192x192 map, 6 heads, d_c = 32, r = 16, bf16; 16 windows, 96
+(batch, window, head) units): posgen of (Q_p, K_p), the window gather of
+Q_c, K_c, V, the fused RIB attention kernel and the scatter of O back to the
+map. Inputs are seeded synthetic tensors already resident in HBM.
+
+Reported (one JSON line): TFLOP/s of algorithmic work (2 N^2 (2 d_c + r) per
+unit, padding and softmax not counted) over the whole step, windows/s, % of
+the bf16 dense MFMA peak, a roofline entry for the attention kernel (timed
+with HIP events on its own stream), per-kernel GB/s of the gathers and
+posgen, the window-size stack (windows 16/32/64/96, forward + backward), and
+the float64 CPU oracle timed on a bounded sample of units as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+METRIC = "RIB window-attn TFLOP/s + windows/s at 96x96 bf16; % of MFMA bf16 peak"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_w96_traffic.json")
+ATTN_SRC = os.path.join(ROOT, "windowed_attention_implicit_amd", "csrc", "attn_fwd.hip")
+
+
+def fwd_flops(units: int, N: int, d_c: int, r: int) -> int:
+    return units * 2 * N * N * (2 * d_c + r)
+
+
+def bwd_flops(units: int, N: int, d_c: int, r: int) -> int:
+    return units * 2 * N * N * (5 * d_c + 3 * r)
+
+
+def to_gpu(t, dev):
+    import numpy as np
+    import torch
+    if t.dtype == "f32":
+        return torch.from_numpy(np.ascontiguousarray(t.data)).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(t.data).view(np.int16)).view(torch.bfloat16).to(dev)
+
+
+class FwdStep:
+    """posgen + forward call with every buffer preallocated; run() enqueues one step."""
+
+    def __init__(self, wl, x, dev):
+        import torch
+        import windowed_attention_implicit_amd as rib
+        self.rib, self.wl = rib, wl
+        self.q, self.k, self.v = (to_gpu(x[n], dev) for n in ("q_c", "k_c", "v"))
+        self.w1 = torch.from_numpy(x["w1"]).to(dev)
+        self.w2 = torch.from_numpy(x["w2"]).to(dev)
+        self.mlp = rib._Mlp(wl.n_freq, wl.hidden, wl.r, self.w1.data_ptr(), None, self.w2.data_ptr(), None)
+        self.qp = torch.empty((wl.N, wl.r), dtype=torch.bfloat16, device=dev)
+        self.kp = torch.empty_like(self.qp)
+        self.plan = rib.FwdPlan(self.q, self.k, self.v, self.qp, self.kp, wl.w)
+
+    def run(self):
+        L = self.rib.lib()
+        st = self.rib._stream(self.q.device)
+        self.rib._check(L.rib_posgen(self.wl.w, ctypes.byref(self.mlp), self.rib.RIB_BF16,
+                                     ctypes.c_void_p(self.qp.data_ptr()), ctypes.c_void_p(self.kp.data_ptr()), st))
+        self.plan.run()
+
+
+def time_steps(fn, steps: int, warmup: int, after_warmup=None):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    if after_warmup is not None:
+        after_warmup()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(steps):
+        fn()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return start.elapsed_time(end) / steps, wall / steps * 1e3
+
+
+def kernel_avg_ms(rib, group):
+    ms, n = rib.kernel_timing_read(group)
+    return (ms / n if n else None), n
+
+
+def traffic_entry():
+    """HBM bytes per launch of the attention kernel from the committed counter run,
+    only while the kernel source is the one the counters were taken on."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)
+        sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+        if rec.get("kernel_source_sha256") != sha:
+            return None
+        return rec["hbm_bytes_per_launch"]
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(wl, x, n_units: int):
+    """The float64 oracle, as it stands, on n_units (batch, window, head) units of the workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        blas = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        cores = max((p.get("num_threads", 1) for p in blas), default=1)
+        blas_name = ",".join(f"{p.get('internal_api')} {p.get('version')}" for p in blas)
+    except Exception:  # noqa: BLE001
+        cores, blas_name = os.cpu_count(), "unknown"
+    units = [(b, wy, wx, h) for b in range(wl.B) for wy in range(wl.H // wl.w)
+             for wx in range(wl.W // wl.w) for h in range(wl.heads)]
+    step = max(1, len(units) // n_units)
+    sample = units[::step][:n_units]
+    qc, kc, v = (x[n].f64() for n in ("q_c", "k_c", "v"))
+    qp, kp = oracle.posgen(wl.w, wl.n_freq, x["w1"], None, x["w2"], None, wl.r)
+    t0 = time.perf_counter()
+    oracle.rib_window_attn_fwd(qc, kc, v, qp, kp, wl.w, units=sample)
+    dt = time.perf_counter() - t0
+    flops = fwd_flops(len(sample), wl.N, wl.d_c, wl.r)
+    return {
+        "value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+        "sample": (f"{len(sample)} of {len(units)} (batch, window, head) units of the 96x96 workload, forward, "
+                   f"float64 numpy with the explicit N x N score matrix; {dt:.2f} s"),
+        "windows_per_s": len(sample) / wl.heads / dt, "seconds": dt, "blas": blas_name,
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def stack_measure(steps: int, warmup: int, dev):
+    """Forward + backward over the window-size stack (16, 32, 64, 96), per layer and total."""
+    import torch
+    import rib_synth
+    import windowed_attention_implicit_amd as rib
+    xs = rib_synth.make_stack_inputs()
+    layers = []
+    for wl, x in zip(rib_synth.STACK, xs):
+        q, k, v, do = (to_gpu(x[n], dev) for n in ("q_c", "k_c", "v", "d_o"))
+        w1, w2 = torch.from_numpy(x["w1"]).to(dev), torch.from_numpy(x["w2"]).to(dev)
+        qp, kp = rib.posgen(wl.w, w1, None, w2, None, wl.r, out_dtype=torch.bfloat16)
+        fp = rib.FwdPlan(q, k, v, qp, kp, wl.w)
+        o, lse = fp.run()
+        bp = rib.BwdPlan(q, k, v, qp, kp, o, lse, do, wl.w)
+        layers.append((wl, fp, bp))
+
+    def run_all():
+        for _, fp, bp in layers:
+            fp.run()
+            bp.run()
+
+    def reset():
+        for g in rib.KERNEL_GROUPS:
+            rib.kernel_timing_read(g)
+
+    rib.kernel_timing_enable(True)
+    ms, _ = time_steps(run_all, steps, warmup, reset)
+    per = []
+    for wl, fp, bp in layers:
+        t_f, _ = time_steps(fp.run, steps, 2, reset)
+        fa, _ = kernel_avg_ms(rib, "attn_fwd")
+        t_b, _ = time_steps(bp.run, steps, 2, reset)
+        dkv, _ = kernel_avg_ms(rib, "attn_bwd_dkv")
+        dq, _ = kernel_avg_ms(rib, "attn_bwd_dq")
+        ff, bf = fwd_flops(wl.units, wl.N, wl.d_c, wl.r), bwd_flops(wl.units, wl.N, wl.d_c, wl.r)
+        per.append({"w": wl.w, "fwd_ms": round(t_f, 4), "bwd_ms": round(t_b, 4),
+                    "fwd_tflops": round(ff / t_f / 1e9, 1), "bwd_tflops": round(bf / t_b / 1e9, 1),
+                    "attn_fwd_kernel_ms": fa and round(fa, 4), "bwd_dkv_kernel_ms": dkv and round(dkv, 4),
+                    "bwd_dq_kernel_ms": dq and round(dq, 4),
+                    "bwd_kernels_tflops": (dkv and dq) and round(bf / (dkv + dq) / 1e9, 1)})
+    rib.kernel_timing_enable(False)
+    total = sum(fwd_flops(wl.units, wl.N, wl.d_c, wl.r) + bwd_flops(wl.units, wl.N, wl.d_c, wl.r)
+                for wl, _, _ in layers)
+    return {"workload": "window-size stack 16/32/64/96 on a 192x192 map, batch 2, 6 heads, d_c=32, r=16, bf16, "
+                        "forward + backward", "ms_per_step": round(ms, 4),
+            "tflops": round(total / ms / 1e9, 1), "layers": per}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-units", type=int, default=4)
+    ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--calibration-copy-mib", type=int, default=0,
+                    help="also run one plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py: this library runs on one GPU; --gpus {args.gpus} (WORLD_SIZE={world}) is not "
+              "supported - no multi-GPU path is built", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rib_synth
+    import windowed_attention_implicit_amd as rib
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    wl = rib_synth.HEADLINE
+    x = rib_synth.make_inputs(wl)
+    step = FwdStep(wl, x, dev)
+    print(f"bench: {wl.name} units={wl.units} N={wl.N}", file=sys.stderr, flush=True)
+
+    for _ in range(3):
+        step.run()
+    torch.cuda.synchronize()
+    rib.kernel_timing_enable(True)
+
+    def reset():
+        for g in rib.KERNEL_GROUPS:
+            rib.kernel_timing_read(g)
+
+    ms, wall_ms = time_steps(step.run, args.steps, args.warmup, reset)
+    attn_ms, attn_n = kernel_avg_ms(rib, "attn_fwd")
+    part_ms, _ = kernel_avg_ms(rib, "partition")
+    unp_ms, _ = kernel_avg_ms(rib, "unpartition")
+    pg_ms, _ = kernel_avg_ms(rib, "posgen")
+    rib.kernel_timing_enable(False)
+    print(f"bench: step {ms:.4f} ms, attention kernel {attn_ms:.4f} ms over {attn_n} launches",
+          file=sys.stderr, flush=True)
+
+    flops = fwd_flops(wl.units, wl.N, wl.d_c, wl.r)
+    tflops = flops / ms / 1e9
+    attn_tflops = flops / attn_ms / 1e9
+    tensor_bytes = wl.B * wl.H * wl.W * wl.heads * wl.d_c * 2
+    part_bytes = 6 * tensor_bytes + 4 * wl.N * wl.r * 2          # read + write Q, K, V; pack Q_p, K_p
+    unp_bytes = 2 * tensor_bytes
+    pg_bytes = 4 * (wl.hidden * 4 * wl.n_freq + 2 * wl.r * wl.hidden) + 2 * wl.N * wl.r * 2
+    traffic = traffic_entry()
+
+    result = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "RIB window attention forward, 96x96 windows: batch 4, 192x192 map, 6 heads, "
+                               "d_c=32, r=16, bf16 (16 windows, 96 units of N=9216)",
+                   "B": wl.B, "H": wl.H, "W": wl.W, "heads": wl.heads, "d_c": wl.d_c, "w": wl.w, "r": wl.r,
+                   "windows": wl.windows, "units": wl.units, "parallelism": "single GPU"},
+        "windows_per_s": round(wl.windows / (ms / 1e3), 1),
+        "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                     "kernel": "attn_fwd_bf16_kernel", "flops_per_launch": flops,
+                     "avg_launch_ms": round(attn_ms, 5)},
+        "kernels": {
+            "posgen": {"ms": pg_ms and round(pg_ms, 5), "GB/s": pg_ms and round(pg_bytes / pg_ms / 1e6, 1)},
+            "partition": {"ms": round(part_ms, 5), "GB/s": round(part_bytes / part_ms / 1e6, 1),
+                          "frac_hbm": round(part_bytes / part_ms / 1e6 / PEAK_HBM_GBS, 3)},
+            "attn_fwd": {"ms": round(attn_ms, 5), "TFLOP/s": round(attn_tflops, 1)},
+            "unpartition": {"ms": round(unp_ms, 5), "GB/s": round(unp_bytes / unp_ms / 1e6, 1),
+                            "frac_hbm": round(unp_bytes / unp_ms / 1e6 / PEAK_HBM_GBS, 3)},
+        },
+        "host_ms_per_step": round(wall_ms, 4),
+    }
+
+    if args.calibration_copy_mib:
+        n = args.calibration_copy_mib * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        result["calibration_copy_bytes"] = 2 * n * 4
+
+    if not args.no_stack:
+        print("bench: window-size stack fwd+bwd", file=sys.stderr, flush=True)
+        result["stack_fwd_bwd"] = stack_measure(max(5, args.steps // 3), 2, dev)
+
+    if not args.no_cpu_baseline:
+        print("bench: cpu baseline (oracle)", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_units)
+    else:
+        result["cpu_baseline"] = None
+
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -163,6 +163,30 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
                                  void* workspace, size_t workspace_bytes,
                                  rib_stream_t stream);
 
+/*
+ * Kernel timing, a measurement aid: while enabled, every posgen / forward /
+ * backward call brackets each of its kernel groups with HIP events recorded
+ * on the call's stream. rib_kernel_timing_read() waits for the recorded
+ * events of one group, returns their summed duration in milliseconds and the
+ * number of timed launches, and forgets them. Disabled by default; while
+ * disabled no events are created. The recorded events are process-wide
+ * host state guarded by a mutex.
+ */
+typedef enum {
+  RIB_KERNEL_POSGEN = 0,       /* the posgen kernel */
+  RIB_KERNEL_PARTITION = 1,    /* the gathers of one call (map -> window layouts, positional packing) */
+  RIB_KERNEL_ATTN_FWD = 2,     /* the forward attention kernel alone */
+  RIB_KERNEL_UNPARTITION = 3,  /* the scatters of one call (window layout -> map) */
+  RIB_KERNEL_BWD_PREP = 4,     /* D = rowsum(dO * O) and log2-domain LSE */
+  RIB_KERNEL_ATTN_BWD_DKV = 5, /* the backward dK / dV kernel alone */
+  RIB_KERNEL_ATTN_BWD_DQ = 6,  /* the backward dQ kernel alone */
+  RIB_KERNEL_POS_REDUCE = 7,   /* the fixed-order sum of the dQ_p / dK_p partials */
+  RIB_KERNEL_COUNT = 8
+} rib_kernel_t;
+
+rib_status_t rib_kernel_timing_enable(int32_t enable);
+rib_status_t rib_kernel_timing_read(rib_kernel_t kernel, double* total_ms, int64_t* launches);
+
 /* Static text naming a status code. */
 const char* rib_status_string(rib_status_t status);
 

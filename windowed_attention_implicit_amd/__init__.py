@@ -25,6 +25,7 @@ __all__ = [
     "RIB_F32", "RIB_BF16", "RibError", "lib", "lib_path", "exported_symbols",
     "posgen", "window_partition", "window_unpartition", "window_attn_fwd", "window_attn_bwd",
     "fwd_workspace_size", "bwd_workspace_size", "FwdPlan", "BwdPlan", "Shape",
+    "KERNEL_GROUPS", "kernel_timing_enable", "kernel_timing_read",
 ]
 
 RIB_OK, RIB_ERR_INVALID_ARG, RIB_ERR_UNSUPPORTED, RIB_ERR_WORKSPACE, RIB_ERR_HIP = range(5)
@@ -62,6 +63,8 @@ _SIGS = {
     "rib_bwd_workspace_size": (_sz, [ctypes.POINTER(Shape), _i32]),
     "rib_window_attn_fwd": (_i32, [ctypes.POINTER(Shape), _i32, _f32] + [_vp] * 7 + [_vp, _sz, _vp]),
     "rib_window_attn_bwd": (_i32, [ctypes.POINTER(Shape), _i32, _f32] + [_vp] * 13 + [_vp, _sz, _vp]),
+    "rib_kernel_timing_enable": (_i32, [_i32]),
+    "rib_kernel_timing_read": (_i32, [_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     "rib_status_string": (ctypes.c_char_p, [_i32]),
     "rib_last_error": (ctypes.c_char_p, []),
 }
@@ -242,6 +245,22 @@ class BwdPlan:
 def window_attn_bwd(q_c, k_c, v, q_p, k_p, o, lse, d_o, w: int, scale: float | None = None):
     """Returns (dQ_c, dK_c, dV, dQ_p, dK_p); dQ_p and dK_p are float32 [w*w, r]."""
     return BwdPlan(q_c, k_c, v, q_p, k_p, o, lse, d_o, w, scale).run()
+
+
+KERNEL_GROUPS = {"posgen": 0, "partition": 1, "attn_fwd": 2, "unpartition": 3, "bwd_prep": 4,
+                 "attn_bwd_dkv": 5, "attn_bwd_dq": 6, "pos_reduce": 7}
+
+
+def kernel_timing_enable(enable: bool = True):
+    """Start (or stop) bracketing each kernel group of later calls with HIP events on their stream."""
+    _check(lib().rib_kernel_timing_enable(1 if enable else 0))
+
+
+def kernel_timing_read(group: str):
+    """(total milliseconds, launches) of one kernel group since the last read; waits for its events."""
+    ms, n = ctypes.c_double(0.0), ctypes.c_int64(0)
+    _check(lib().rib_kernel_timing_read(KERNEL_GROUPS[group], ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
 
 
 def default_scale(d_c: int, r: int) -> float:

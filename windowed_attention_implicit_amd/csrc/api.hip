@@ -6,7 +6,10 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
 #include <string>
+#include <utility>
+#include <vector>
 
 #include "internal.hpp"
 
@@ -149,6 +152,68 @@ BwdLayout bwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
   return L;
 }
 
+// ---- kernel timing (measurement aid, off by default)
+struct TimingState {
+  std::mutex mu;
+  bool enabled = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[RIB_KERNEL_COUNT];
+};
+
+TimingState& timing() {
+  static TimingState t;
+  return t;
+}
+
+// Brackets a group of launches with events on `stream` while timing is enabled;
+// a group abandoned by an early error return records nothing.
+class TimedGroup {
+ public:
+  TimedGroup(rib_kernel_t k, hipStream_t s) : k_(k), s_(s) {
+    TimingState& t = timing();
+    {
+      std::lock_guard<std::mutex> g(t.mu);
+      if (!t.enabled) return;
+    }
+    if (hipEventCreate(&a_) != hipSuccess) return;
+    if (hipEventCreate(&b_) != hipSuccess) {
+      (void)hipEventDestroy(a_);
+      return;
+    }
+    if (hipEventRecord(a_, s_) != hipSuccess) {
+      (void)hipEventDestroy(a_);
+      (void)hipEventDestroy(b_);
+      return;
+    }
+    on_ = true;
+  }
+  void end() {
+    if (!on_) return;
+    on_ = false;
+    if (hipEventRecord(b_, s_) != hipSuccess) {
+      (void)hipEventDestroy(a_);
+      (void)hipEventDestroy(b_);
+      return;
+    }
+    TimingState& t = timing();
+    std::lock_guard<std::mutex> g(t.mu);
+    t.ev[k_].push_back({a_, b_});
+  }
+  ~TimedGroup() {
+    if (on_) {
+      (void)hipEventDestroy(a_);
+      (void)hipEventDestroy(b_);
+    }
+  }
+  TimedGroup(const TimedGroup&) = delete;
+  TimedGroup& operator=(const TimedGroup&) = delete;
+
+ private:
+  rib_kernel_t k_;
+  hipStream_t s_;
+  hipEvent_t a_ = nullptr, b_ = nullptr;
+  bool on_ = false;
+};
+
 float resolve_scale(float scale, const rib_shape_t* s) {
   return scale > 0.f ? scale : 1.0f / sqrtf((float)(s->d_c + s->r));
 }
@@ -175,6 +240,44 @@ const char* rib_status_string(rib_status_t status) {
 
 const char* rib_last_error(void) { return g_last_error.c_str(); }
 
+rib_status_t rib_kernel_timing_enable(int32_t enable) {
+  TimingState& t = timing();
+  std::lock_guard<std::mutex> g(t.mu);
+  t.enabled = enable != 0;
+  return ok();
+}
+
+rib_status_t rib_kernel_timing_read(rib_kernel_t kernel, double* total_ms, int64_t* launches) {
+  try {
+    if ((int)kernel < 0 || (int)kernel >= RIB_KERNEL_COUNT)
+      return fail(RIB_ERR_INVALID_ARG, "kernel group %d out of range", (int)kernel);
+    if (!total_ms || !launches) return fail(RIB_ERR_INVALID_ARG, "output pointers are NULL");
+    std::vector<std::pair<hipEvent_t, hipEvent_t>> ev;
+    {
+      TimingState& t = timing();
+      std::lock_guard<std::mutex> g(t.mu);
+      ev.swap(t.ev[kernel]);
+    }
+    double sum = 0.0;
+    hipError_t first = hipSuccess;
+    for (auto& p : ev) {
+      float ms = 0.f;
+      hipError_t e = hipEventSynchronize(p.second);
+      if (e == hipSuccess) e = hipEventElapsedTime(&ms, p.first, p.second);
+      if (e != hipSuccess && first == hipSuccess) first = e;
+      sum += ms;
+      (void)hipEventDestroy(p.first);
+      (void)hipEventDestroy(p.second);
+    }
+    *total_ms = sum;
+    *launches = (int64_t)ev.size();
+    if (first != hipSuccess) return hip_fail(first, "reading kernel timing events");
+    return ok();
+  } catch (...) {
+    return fail(RIB_ERR_HIP, "unexpected C++ exception in rib_kernel_timing_read");
+  }
+}
+
 rib_status_t rib_posgen(int32_t w, const rib_mlp_t* mlp, rib_dtype_t out_dtype, void* q_p, void* k_p,
                         rib_stream_t stream) {
   try {
@@ -196,8 +299,10 @@ rib_status_t rib_posgen(int32_t w, const rib_mlp_t* mlp, rib_dtype_t out_dtype, 
       return fail(RIB_ERR_INVALID_ARG, "mlp weights must be 4-byte aligned");
     if (((uintptr_t)q_p | (uintptr_t)k_p) & (uintptr_t)(esize_of(out_dtype) - 1))
       return fail(RIB_ERR_INVALID_ARG, "q_p / k_p misaligned for their element type");
+    TimedGroup tg(RIB_KERNEL_POSGEN, (hipStream_t)stream);
     hipError_t e = launch_posgen(w, *mlp, out_dtype, q_p, k_p, (hipStream_t)stream);
     if (e != hipSuccess) return hip_fail(e, "posgen launch");
+    tg.end();
     return ok();
   } catch (...) {
     return fail(RIB_ERR_HIP, "unexpected C++ exception in rib_posgen");
@@ -269,6 +374,7 @@ rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
     const int es = esize_of(dtype);
     const int rp = padded_rank(g.r);
     hipError_t e;
+    TimedGroup t_part(RIB_KERNEL_PARTITION, st);
     if ((e = launch_partition(g, es, WinLayout::kRows, q_c, L.qw, st)) != hipSuccess) return hip_fail(e, "partition q");
     if ((e = launch_partition(g, es, WinLayout::kRows, k_c, L.kw, st)) != hipSuccess) return hip_fail(e, "partition k");
     if ((e = launch_partition(g, es, dtype == RIB_BF16 ? WinLayout::kTransKappa : WinLayout::kRows, v, L.vw, st)) !=
@@ -276,15 +382,20 @@ rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
       return hip_fail(e, "partition v");
     if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, q_p, es, L.qp, st)) != hipSuccess) return hip_fail(e, "pack q_p");
     if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, k_p, es, L.kp, st)) != hipSuccess) return hip_fail(e, "pack k_p");
+    t_part.end();
     FwdArgs a;
     a.g = g;
     a.c = resolve_scale(scale, shape) * kLog2e;
     a.qw = L.qw; a.kw = L.kw; a.vw = L.vw; a.qp = L.qp; a.kp = L.kp; a.ow = L.ow;
     a.lse = lse;
     a.rp = rp;
+    TimedGroup t_attn(RIB_KERNEL_ATTN_FWD, st);
     e = dtype == RIB_BF16 ? launch_attn_fwd_bf16(a, st) : launch_attn_fwd_f32(a, st);
     if (e != hipSuccess) return hip_fail(e, "attention forward");
+    t_attn.end();
+    TimedGroup t_unp(RIB_KERNEL_UNPARTITION, st);
     if ((e = launch_unpartition(g, es, L.ow, o, st)) != hipSuccess) return hip_fail(e, "unpartition o");
+    t_unp.end();
     return ok();
   } catch (...) {
     return fail(RIB_ERR_HIP, "unexpected C++ exception in rib_window_attn_fwd");
@@ -335,6 +446,7 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
   do {                                                \
     if ((e = (call)) != hipSuccess) return hip_fail(e, what); \
   } while (0)
+    TimedGroup t_part(RIB_KERNEL_PARTITION, st);
     RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, q_c, L.qw, st), "partition q");
     RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, k_c, L.kw, st), "partition k");
     RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, v, L.vw, st), "partition v");
@@ -350,7 +462,10 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
       RIB_LAUNCH(launch_pos_transpose(g.n_rows, rp, L.qp, L.qpt, st), "q_p^T");
       RIB_LAUNCH(launch_pos_transpose(g.n_rows, rp, L.kp, L.kpt, st), "k_p^T");
     }
+    t_part.end();
+    TimedGroup t_prep(RIB_KERNEL_BWD_PREP, st);
     RIB_LAUNCH(launch_bwd_prep(g, es, o, d_o, lse, L.dd, L.lse2, st), "bwd prep");
+    t_prep.end();
     BwdArgs a;
     a.g = g;
     a.scale = resolve_scale(scale, shape);
@@ -362,12 +477,23 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
     a.lse2 = L.lse2; a.dd = L.dd;
     a.dqw = L.dqw; a.dkw = L.dkw; a.dvw = L.dvw;
     a.dqp_part = L.dqp_part; a.dkp_part = L.dkp_part;
-    RIB_LAUNCH(bf ? launch_attn_bwd_bf16(a, st) : launch_attn_bwd_f32(a, st), "attention backward");
+    {
+      TimedGroup t_dkv(RIB_KERNEL_ATTN_BWD_DKV, st);
+      RIB_LAUNCH(bf ? launch_attn_bwd_dkv_bf16(a, st) : launch_attn_bwd_dkv_f32(a, st), "attention backward dK/dV");
+      t_dkv.end();
+      TimedGroup t_dq(RIB_KERNEL_ATTN_BWD_DQ, st);
+      RIB_LAUNCH(bf ? launch_attn_bwd_dq_bf16(a, st) : launch_attn_bwd_dq_f32(a, st), "attention backward dQ");
+      t_dq.end();
+    }
+    TimedGroup t_red(RIB_KERNEL_POS_REDUCE, st);
     RIB_LAUNCH(launch_reduce_pos_grads(g.units, g.N, g.n_rows, g.r, rp, L.dqp_part, dq_p, st), "reduce dq_p");
     RIB_LAUNCH(launch_reduce_pos_grads(g.units, g.N, g.n_rows, g.r, rp, L.dkp_part, dk_p, st), "reduce dk_p");
+    t_red.end();
+    TimedGroup t_unp(RIB_KERNEL_UNPARTITION, st);
     RIB_LAUNCH(launch_unpartition(g, es, L.dqw, dq_c, st), "unpartition dq");
     RIB_LAUNCH(launch_unpartition(g, es, L.dkw, dk_c, st), "unpartition dk");
     RIB_LAUNCH(launch_unpartition(g, es, L.dvw, dv, st), "unpartition dv");
+    t_unp.end();
 #undef RIB_LAUNCH
     return ok();
   } catch (...) {

@@ -575,31 +575,35 @@ hipError_t launch_bwd_prep(const Geom& g, int esize, const void* o, const void* 
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream) {
-  const int nb = (a.g.N + kPerBlock - 1) / kPerBlock;
-  const int64_t blocks = (int64_t)a.g.units * nb;
+hipError_t launch_attn_bwd_dkv_bf16(const BwdArgs& a, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a.g.units * ((a.g.N + kPerBlock - 1) / kPerBlock);
   if (blocks == 0) return hipSuccess;
-  if (a.rp == 16) {
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(attn_bwd_dkv_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(attn_bwd_dq_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  }
+  if (a.rp == 16) hipLaunchKernelGGL(attn_bwd_dkv_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(attn_bwd_dkv_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd_f32(const BwdArgs& a, hipStream_t stream) {
-  const int nb = (a.g.N + 255) / 256;
-  const int64_t blocks = (int64_t)a.g.units * nb;
+hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a.g.units * ((a.g.N + kPerBlock - 1) / kPerBlock);
   if (blocks == 0) return hipSuccess;
-  if (a.rp == 16) {
-    hipLaunchKernelGGL(attn_bwd_dkv_f32_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  } else {
-    hipLaunchKernelGGL(attn_bwd_dkv_f32_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-    hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  }
+  if (a.rp == 16) hipLaunchKernelGGL(attn_bwd_dq_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(attn_bwd_dq_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dkv_f32(const BwdArgs& a, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a.g.units * ((a.g.N + 255) / 256);
+  if (blocks == 0) return hipSuccess;
+  if (a.rp == 16) hipLaunchKernelGGL(attn_bwd_dkv_f32_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(attn_bwd_dkv_f32_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_bwd_dq_f32(const BwdArgs& a, hipStream_t stream) {
+  const int64_t blocks = (int64_t)a.g.units * ((a.g.N + 255) / 256);
+  if (blocks == 0) return hipSuccess;
+  if (a.rp == 16) hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

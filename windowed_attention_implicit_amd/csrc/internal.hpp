@@ -77,8 +77,10 @@ struct BwdArgs {
 // D and log2-domain LSE in windowed order, from O, dO and LSE in map layout.
 hipError_t launch_bwd_prep(const Geom& g, int esize, const void* o, const void* d_o, const float* lse,
                            float* dd, float* lse2, hipStream_t stream);
-hipError_t launch_attn_bwd_bf16(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_attn_bwd_f32(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_bwd_dkv_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_bwd_dkv_f32(const BwdArgs& a, hipStream_t stream);
+hipError_t launch_attn_bwd_dq_f32(const BwdArgs& a, hipStream_t stream);
 // Fixed-order sum over units of [units][n_rows][rp] partials -> [N][r] float32.
 hipError_t launch_reduce_pos_grads(int units, int N, int n_rows, int r, int rp, const float* part, float* out,
                                    hipStream_t stream);
