@@ -90,7 +90,8 @@ typedef struct {
  * head of this window size, so it can be computed once and cached [DE §2.A.4].
  *
  *   w          window side, 2..256
- *   mlp        host pointer; 1 <= n_freq <= 16, 1 <= hidden <= 128, 1 <= rank <= 32
+ *   mlp        host pointer; 1 <= n_freq <= 16, 1 <= hidden <= 128, 1 <= rank <= 32,
+ *              and the weights, staged in LDS, must fit 64 KB (RIB_ERR_UNSUPPORTED)
  *   out_dtype  element type of q_p and k_p
  *   q_p, k_p   (device) outputs, [w*w, rank] each
  */

@@ -95,6 +95,7 @@ struct Carve {
 
 struct FwdLayout {
   void *qw, *kw, *vw, *ow, *qp, *kp;
+  float* kmax2;
   size_t bytes;
 };
 
@@ -110,6 +111,7 @@ FwdLayout fwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
   L.ow = c.take(t);
   L.qp = c.take(pos);
   L.kp = c.take(pos);
+  L.kmax2 = (float*)c.take((size_t)g.units * key_bound_parts(g.N) * sizeof(float));
   L.bytes = c.off;
   return L;
 }
@@ -290,8 +292,7 @@ rib_status_t rib_posgen(int32_t w, const rib_mlp_t* mlp, rib_dtype_t out_dtype, 
     if (mlp->hidden < 1 || mlp->hidden > 128)
       return fail(RIB_ERR_UNSUPPORTED, "hidden=%d must be in 1..128", mlp->hidden);
     if (mlp->rank < 1 || mlp->rank > 32) return fail(RIB_ERR_UNSUPPORTED, "rank=%d must be in 1..32", mlp->rank);
-    const size_t lds = sizeof(float) * ((size_t)mlp->hidden * 4 * mlp->n_freq + mlp->hidden +
-                                        (size_t)2 * mlp->rank * mlp->hidden + 2 * mlp->rank);
+    const size_t lds = posgen_lds_bytes(*mlp);
     if (lds > 65536) return fail(RIB_ERR_UNSUPPORTED, "MLP too large for one LDS stage (%zu bytes)", lds);
     if (!mlp->w1 || !mlp->w2) return fail(RIB_ERR_INVALID_ARG, "mlp weights are NULL");
     if (!q_p || !k_p) return fail(RIB_ERR_INVALID_ARG, "q_p / k_p is NULL");
@@ -382,13 +383,15 @@ rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
       return hip_fail(e, "partition v");
     if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, q_p, es, L.qp, st)) != hipSuccess) return hip_fail(e, "pack q_p");
     if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, k_p, es, L.kp, st)) != hipSuccess) return hip_fail(e, "pack k_p");
-    t_part.end();
     FwdArgs a;
     a.g = g;
     a.c = resolve_scale(scale, shape) * kLog2e;
     a.qw = L.qw; a.kw = L.kw; a.vw = L.vw; a.qp = L.qp; a.kp = L.kp; a.ow = L.ow;
     a.lse = lse;
+    a.kmax2 = L.kmax2;
     a.rp = rp;
+    if (dtype == RIB_BF16 && (e = launch_key_bound(a, st)) != hipSuccess) return hip_fail(e, "key bound");
+    t_part.end();
     TimedGroup t_attn(RIB_KERNEL_ATTN_FWD, st);
     e = dtype == RIB_BF16 ? launch_attn_fwd_bf16(a, st) : launch_attn_fwd_f32(a, st);
     if (e != hipSuccess) return hip_fail(e, "attention forward");

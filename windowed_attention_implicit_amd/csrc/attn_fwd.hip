@@ -8,24 +8,32 @@
 // abstract).
 //
 // bf16 kernel design (CDNA4, wave64, v_mfma_f32_32x32x16_bf16):
-//  * The score tile is computed transposed, S^T = K_hat Q_hat^T: keys are the
+//  * The score tile is computed transposed, S^T = K_hat Q'^T: keys are the
 //    MFMA rows, queries the columns, so every lane owns one query and holds 16
-//    of its scores. Row max and row sum are in-lane reductions plus one swap
-//    between the two 32-lane halves.
+//    of its scores.
 //  * The concatenation is virtual: the contraction runs over two 16-channel
 //    content steps (d_c = 32) and one or two 16-channel positional steps
 //    (r padded to 16 / 32 with zeros), K_c and K_p staged side by side in LDS.
+//  * Q' = bf16(scale * log2(e) * [Q_c | Q_p]) so scores come out in the log2
+//    domain and P = exp2(S' - m) needs no multiply.
 //  * O^T = V^T P^T: P leaves the score accumulator directly as the B operand.
 //    The accumulator holds, for half h of the wave, keys 8(v/4) + 4h + v%4;
 //    V^T is stored with tokens permuted inside every 16-token group (bits 2
 //    and 3 of the token index swapped) so each lane's eight keys are one
 //    contiguous 16-byte LDS read.
+//  * Fast pass (no running max): by Cauchy-Schwarz every score of query i is
+//    at most m_i = |q'_i| * max_j |k_hat_j|, so P = exp2(S' - m_i) <= 1 never
+//    overflows and needs no rescaling. The subtraction is free: the score
+//    MFMA accumulates onto a constant -m_i. The row sum is taken with
+//    v_dot2_f32_bf16 on the bf16 P pairs that feed the PV MFMA. Per score the
+//    vector work is one exp2, half a pack and half a dot2.
+//  * Exact pass (fallback): if some row sum of a workgroup came out below
+//    2^-60 (the bound overshot so far that small terms could underflow) or is
+//    not finite, the workgroup recomputes its rows with the classic online
+//    softmax (running max, rescaling when the max grows by more than 2^8).
 //  * A workgroup is 4 waves x 64 queries; K and V^T tiles of 64 keys are
 //    double-buffered in LDS and shared by the 4 waves; workgroups of one unit
 //    are kept on one XCD (its L2 holds the unit's K and V).
-//  * Online softmax in the log2 domain with a lazy rescale: the running max
-//    only moves (and O, l are only rescaled) when some query's max grows by
-//    more than 2^8, a wave-uniform branch.
 #include "internal.hpp"
 
 namespace rib {
@@ -36,6 +44,8 @@ constexpr int kQPerWave = 64;             // two 32-query MFMA column blocks
 constexpr int kQPerBlock = kWaves * kQPerWave;
 constexpr int kKeyTile = 64;
 constexpr float kLazyTau = 8.0f;          // log2 units
+constexpr float kUnderflowGuard = 8.673617379884035e-19f;  // 2^-60
+constexpr int kKeyBoundTile = 256;        // keys per partial key-norm maximum
 
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
 
@@ -50,11 +60,19 @@ struct FwdCfg {
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
+template <bool V>
+struct BoolTag {
+  static constexpr bool value = V;
+};
+
 template <int KP>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   typedef FwdCfg<KP> C;
-  __shared__ u32x4 sK[2][C::kKChunks];
-  __shared__ u32x4 sV[2][C::kVChunks];
+  // three K / V^T tile buffers: with the score MFMAs of the next subtile issued
+  // ahead of the current subtile's softmax, a buffer is overwritten only two
+  // tiles after it was last read, so one barrier per tile suffices.
+  __shared__ u32x4 sK[3][C::kKChunks];
+  __shared__ u32x4 sV[3][C::kVChunks];
 
   const Geom& g = a.g;
   const int N = g.N, n_rows = g.n_rows;
@@ -74,14 +92,25 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const bf16* vt = (const bf16*)a.vw + (int64_t)unit * 32 * n_rows;
   const bf16* qp = (const bf16*)a.qp;
   const bf16* kp = (const bf16*)a.kp;
+  const float c = a.c;
 
-  // ---- query fragments (B operand): lane holds 8 channels of its query per step
+  // ---- per-unit key-norm bound: max over the partial maxima of the unit
+  const int nkparts = (N + kKeyBoundTile - 1) / kKeyBoundTile;
+  float km = 0.f;
+  for (int i = lane; i < nkparts; i += 64) km = fmaxf(km, a.kmax2[(int64_t)unit * nkparts + i]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) km = fmaxf(km, __shfl_xor(km, o));
+  const float kmax = sqrtf(km);
+
+  // ---- query fragments (B operand), pre-scaled into the log2 domain
   const int q0 = qb * kQPerBlock + wave * kQPerWave;
   bf16x8 qf[2][C::kSteps];
+  float mref[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int q = q0 + nb * 32 + l32;
     const bool ok = q < N;
+    float sq = 0.f;
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s) {
       u32x4 v = u32x4(0u);
@@ -89,8 +118,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
         if (s < 2) v = *(const u32x4*)(qw + (int64_t)q * 32 + s * 16 + half * 8);
         else v = *(const u32x4*)(qp + (int64_t)q * rp + (s - 2) * 16 + half * 8);
       }
-      qf[nb][s] = __builtin_bit_cast(bf16x8, v);
+      const bf16x8 raw = __builtin_bit_cast(bf16x8, v);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const bf16 e = f32_to_bf16((float)raw[j] * c);
+        qf[nb][s][j] = e;
+        sq = fmaf((float)e, (float)e, sq);
+      }
     }
+    sq += swap_halves(sq);
+    mref[nb] = sqrtf(sq) * kmax;
   }
 
   // ---- tile loader: each thread moves up to three 16-byte chunks per tile
@@ -111,92 +148,223 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     if (kp_active) sK[buf][kp_key * C::kKRow + 4 + kp_ch] = ldKp;
     sV[buf][v_row * C::kVRow + v_ch] = ldV;
   };
+  // score fragments of one 32-key subtile
+  auto load_kf = [&](int buf, int sub, bf16x8* kf) {
+#pragma unroll
+    for (int s = 0; s < C::kSteps; ++s) {
+      const int ch = s < 2 ? 2 * s + half : 4 + 2 * (s - 2) + half;
+      kf[s] = __builtin_bit_cast(bf16x8, sK[buf][(sub * 32 + l32) * C::kKRow + ch]);
+    }
+  };
+  auto mask_tail = [&](f32x16* sc, int key0) {
+    const int kbase = key0 + 4 * half;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = kbase + 8 * (v >> 2) + (v & 3);
+      if (key >= N) { sc[0][v] = -INFINITY; sc[1][v] = -INFINITY; }
+    }
+  };
+  auto pv = [&](int buf, int sub, const bf16x8 (*pf)[2], f32x16* acc) {
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8 vf = __builtin_bit_cast(bf16x8, sV[buf][l32 * C::kVRow + 4 * sub + 2 * s + half]);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb][s], acc[nb], 0, 0, 0);
+    }
+  };
 
   f32x16 acc[2];
   float m_run[2], l_run[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[nb][i] = 0.f;
-    m_run[nb] = -INFINITY;
-    l_run[nb] = 0.f;
-  }
-  const float c = a.c;
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
-  load_tile(0);
-  store_tile(0);
-  __syncthreads();
-
-  for (int t = 0; t < nkt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nkt) load_tile(t + 1);
-    const bool tail = (t + 1) * kKeyTile > N;
+  // ===== fast pass: fixed per-query bound, software-pipelined over subtiles.
+  // Each half step takes the softmax of one 32-key subtile while the score
+  // MFMAs of the next subtile and the PV MFMAs of this one run; the source
+  // order below (pinned by scheduling fences) alternates one MFMA with a
+  // slice of the exp / pack / row-sum work so both pipes stay busy within a
+  // wave. Keys past N (last tile only) have zero K rows and zero V^T columns:
+  // their P = exp2(-m) adds nothing to O and is subtracted from the row sum.
+  float pad_sub[2] = {0.f, 0.f};
+  {
+    f32x16 cinit[2];
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      // score fragments for 32 keys
+    for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        acc[nb][i] = 0.f;
+        cinit[nb][i] = -mref[nb];
+      }
+      m_run[nb] = mref[nb];
+    }
+    float lsum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+
+    // half step: softmax of sc_in, scores of subtile (kbuf, ksub) into sc_out,
+    // O += V^T(vbuf, vsub) P^T
+    auto half_step = [&](const f32x16* sc_in, int kbuf, int ksub, int vbuf, int vsub, f32x16* sc_out) {
+      bf16x8 kf[C::kSteps], vf[2];
+      load_kf(kbuf, ksub, kf);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        vf[s] = __builtin_bit_cast(bf16x8, sV[vbuf][l32 * C::kVRow + 4 * vsub + 2 * s + half]);
+      u32x4 words[2][2];
+      // P words w0, w0+1 of block (nb, s): 4 exp2, 2 packs, 2 row-sum dot2
+      auto pslice = [&](int nb, int s, int w0) {
+#pragma unroll
+        for (int w = w0; w < w0 + 2; ++w) {
+          bf16x2 pr;
+          pr[0] = f32_to_bf16(__builtin_amdgcn_exp2f(sc_in[nb][8 * s + 2 * w]));
+          pr[1] = f32_to_bf16(__builtin_amdgcn_exp2f(sc_in[nb][8 * s + 2 * w + 1]));
+          words[nb][s][w] = __builtin_bit_cast(unsigned, pr);
+          lsum[nb][w & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[nb][w & 1], false);
+        }
+      };
+      auto smfma = [&](int s, int nb) {
+        sc_out[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[nb][s], s == 0 ? cinit[nb] : sc_out[nb], 0,
+                                                             0, 0);
+      };
+      auto pvmfma = [&](int s, int nb) {
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], __builtin_bit_cast(bf16x8, words[nb][s]), acc[nb],
+                                                          0, 0, 0);
+      };
+      pslice(0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      smfma(0, 0);
+      pslice(0, 0, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      smfma(0, 1);
+      pslice(1, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      smfma(1, 0);
+      pslice(1, 0, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      smfma(1, 1);
+      pslice(0, 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      smfma(2, 0);
+      pslice(0, 1, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      smfma(2, 1);
+      pslice(1, 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 3; s < C::kSteps; ++s) {
+        smfma(s, 0);
+        smfma(s, 1);
+      }
+      pvmfma(0, 0);
+      pslice(1, 1, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      pvmfma(0, 1);
+      pvmfma(1, 0);
+      pvmfma(1, 1);
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // prologue: tiles 0 and 1 in LDS, tile 2 in registers, scores of subtile 0
+    load_tile(0);
+    store_tile(0);
+    load_tile(min(1, nkt - 1));
+    store_tile(1);
+    load_tile(min(2, nkt - 1));
+    __syncthreads();
+    f32x16 sc_a[2], sc_b[2];
+    {
       bf16x8 kf[C::kSteps];
-#pragma unroll
-      for (int s = 0; s < C::kSteps; ++s) {
-        const int ch = s < 2 ? 2 * s + half : 4 + 2 * (s - 2) + half;
-        kf[s] = __builtin_bit_cast(bf16x8, sK[buf][(sub * 32 + l32) * C::kKRow + ch]);
-      }
-      f32x16 sc[2];
+      load_kf(0, 0, kf);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
+        sc_a[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[nb][0], cinit[nb], 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sc[nb][i] = 0.f;
-#pragma unroll
-        for (int s = 0; s < C::kSteps; ++s)
-          sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[nb][s], sc[nb], 0, 0, 0);
-      }
-      if (tail) {
-        const int kbase = t * kKeyTile + sub * 32 + 4 * half;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int key = kbase + 8 * (v >> 2) + (v & 3);
-          if (key >= N) { sc[0][v] = -INFINITY; sc[1][v] = -INFINITY; }
-        }
-      }
-      // online softmax (log2 domain), lazy rescale
-      bf16x8 pf[2][2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        float mx = sc[nb][0];
-#pragma unroll
-        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[nb][v]);
-        mx = fmaxf(mx, swap_halves(mx));
-        const float m_new = fmaxf(m_run[nb], mx * c);
-        if (__any(m_new > m_run[nb] + kLazyTau)) {
-          const float alpha = (m_new == m_run[nb]) ? 1.f : exp2f(m_run[nb] - m_new);
-#pragma unroll
-          for (int i = 0; i < 16; ++i) acc[nb][i] *= alpha;
-          l_run[nb] *= alpha;
-          m_run[nb] = m_new;
-        }
-        const float mneg = -m_run[nb];
-        float lsum = 0.f;
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float p = exp2f(fmaf(sc[nb][8 * s + j], c, mneg));
-            lsum += p;
-            pf[nb][s][j] = f32_to_bf16(p);
-          }
-        }
-        l_run[nb] += lsum;
-      }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, sV[buf][l32 * C::kVRow + 4 * sub + 2 * s + half]);
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb][s], acc[nb], 0, 0, 0);
+        for (int s = 1; s < C::kSteps; ++s)
+          sc_a[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[nb][s], sc_a[nb], 0, 0, 0);
       }
     }
-    if (t + 1 < nkt) store_tile(buf ^ 1);
+    for (int t = 0; t < nkt; ++t) {
+      const int b0 = t % 3, b1 = (t + 1) % 3, b2 = (t + 2) % 3;
+      half_step(sc_a, b0, 1, b0, 0, sc_b);   // softmax (t, 0); scores (t, 1)
+      half_step(sc_b, b1, 0, b0, 1, sc_a);   // softmax (t, 1); scores (t + 1, 0)
+      store_tile(b2);                        // tile t + 2 (the last tile again past the end)
+      load_tile(min(t + 3, nkt - 1));
+      __syncthreads();
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      l_run[nb] = lsum[nb][0] + lsum[nb][1];
+      pad_sub[nb] = (float)(nkt * kKeyTile - N) * (float)f32_to_bf16(__builtin_amdgcn_exp2f(-mref[nb]));
+    }
+  }
+
+  bool bad = false;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    // both halves of the wave hold part of each row sum; the padded keys are
+    // removed once from the half-0 share
+    l_run[nb] -= half == 0 ? pad_sub[nb] : 0.f;
+    const float l_tot = l_run[nb] + swap_halves(l_run[nb]);
+    bad |= !(l_tot >= kUnderflowGuard) || !(l_tot < INFINITY);
+  }
+
+  // ===== exact pass (rare fallback): classic online softmax, double-buffered
+  if (__syncthreads_or(bad)) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) acc[nb][i] = 0.f;
+      m_run[nb] = -INFINITY;
+      l_run[nb] = 0.f;
+    }
+    load_tile(0);
+    store_tile(0);
     __syncthreads();
+    for (int t = 0; t < nkt; ++t) {
+      const int buf = t & 1;
+      if (t + 1 < nkt) load_tile(t + 1);
+      const bool tail = (t + 1) * kKeyTile > N;
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+        bf16x8 kf[C::kSteps];
+        load_kf(buf, sub, kf);
+        f32x16 sc[2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sc[nb][i] = 0.f;
+#pragma unroll
+          for (int s = 0; s < C::kSteps; ++s)
+            sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[nb][s], sc[nb], 0, 0, 0);
+        }
+        if (tail) mask_tail(sc, t * kKeyTile + sub * 32);
+        bf16x8 pf[2][2];
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          float mx = sc[nb][0];
+#pragma unroll
+          for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[nb][v]);
+          mx = fmaxf(mx, swap_halves(mx));
+          const float m_new = fmaxf(m_run[nb], mx);
+          if (__any(m_new > m_run[nb] + kLazyTau)) {
+            const float alpha = (m_new == m_run[nb]) ? 1.f : exp2f(m_run[nb] - m_new);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[nb][i] *= alpha;
+            l_run[nb] *= alpha;
+            m_run[nb] = m_new;
+          }
+          const float mneg = -m_run[nb];
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+              const float p = exp2f(sc[nb][8 * s + j] + mneg);
+              l_run[nb] += p;
+              pf[nb][s][j] = f32_to_bf16(p);
+            }
+        }
+        pv(buf, sub, pf, acc);
+      }
+      if (t + 1 < nkt) store_tile(buf ^ 1);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue: normalize, write O rows and LSE
@@ -218,6 +386,43 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       }
       if (a.lse && half == 0) a.lse[pm.pixel_head(unit, q)] = (m_run[nb] + log2f(l_tot)) * kLn2;
     }
+  }
+}
+
+// Partial key-norm maxima: block (unit, part) writes max over its kKeyBoundTile
+// keys of |[k_c | k_p]|^2 (float32) to kmax2[unit * parts + part].
+__global__ __launch_bounds__(kKeyBoundTile) void key_bound_kernel(int N, int n_rows, int rp, int parts,
+                                                                  const bf16* __restrict__ kw,
+                                                                  const bf16* __restrict__ kp,
+                                                                  float* __restrict__ kmax2) {
+  __shared__ float red[kKeyBoundTile / 64];
+  const int unit = blockIdx.x / parts;
+  const int part = blockIdx.x - unit * parts;
+  const int t = part * kKeyBoundTile + threadIdx.x;
+  float s = 0.f;
+  if (t < N) {
+    const bf16* kr = kw + ((int64_t)unit * n_rows + t) * 32;
+#pragma unroll
+    for (int c4 = 0; c4 < 4; ++c4) {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr + c4 * 8));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s = fmaf((float)v[j], (float)v[j], s);
+    }
+    for (int c4 = 0; c4 < rp / 8; ++c4) {
+      const bf16x8 v = __builtin_bit_cast(bf16x8, *(const u32x4*)(kp + (int64_t)t * rp + c4 * 8));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s = fmaf((float)v[j], (float)v[j], s);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) s = fmaxf(s, __shfl_xor(s, o));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = red[0];
+#pragma unroll
+    for (int w = 1; w < kKeyBoundTile / 64; ++w) m = fmaxf(m, red[w]);
+    kmax2[blockIdx.x] = m;
   }
 }
 
@@ -302,6 +507,16 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
 }
 
 }  // namespace
+
+hipError_t launch_key_bound(const FwdArgs& a, hipStream_t stream) {
+  if (a.g.units == 0) return hipSuccess;
+  const int parts = (a.g.N + kKeyBoundTile - 1) / kKeyBoundTile;
+  hipLaunchKernelGGL(key_bound_kernel, dim3(a.g.units * parts), dim3(kKeyBoundTile), 0, stream, a.g.N, a.g.n_rows,
+                     a.rp, parts, (const bf16*)a.kw, (const bf16*)a.kp, a.kmax2);
+  return hipGetLastError();
+}
+
+int key_bound_parts(int N) { return (N + kKeyBoundTile - 1) / kKeyBoundTile; }
 
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   const int nqb = (a.g.N + kQPerBlock - 1) / kQPerBlock;

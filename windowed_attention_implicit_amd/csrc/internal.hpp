@@ -16,6 +16,8 @@ enum class WinLayout {
 
 hipError_t launch_posgen(int w, const rib_mlp_t& mlp, rib_dtype_t out_dtype, void* q_p, void* k_p,
                          hipStream_t stream);
+// Dynamic LDS bytes the posgen kernel needs for this MLP.
+size_t posgen_lds_bytes(const rib_mlp_t& mlp);
 
 // x [B,H,W,heads,d] -> windowed buffer in `layout` (rows >= N zero-filled).
 hipError_t launch_partition(const Geom& g, int esize, WinLayout layout, const void* x, void* xw,
@@ -43,8 +45,12 @@ struct FwdArgs {
   const void* kp;       // [n_rows][rp]
   void* ow;             // [units][n_rows][32]
   float* lse;           // [B,H,W,heads] or nullptr
+  float* kmax2;         // [units][key_bound_parts(N)] partial maxima of |[k_c | k_p]|^2 (bf16 path)
   int rp;               // padded rank, 16 or 32
 };
+// Per-unit key-norm bound used by the bf16 forward (reads kw and kp, writes kmax2).
+hipError_t launch_key_bound(const FwdArgs& a, hipStream_t stream);
+int key_bound_parts(int N);
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream);
 
