@@ -199,11 +199,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     }
     float lsum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
 
-    // half step: softmax of sc_in, scores of subtile (kbuf, ksub) into sc_out,
-    // O += V^T(vbuf, vsub) P^T
-    auto half_step = [&](const f32x16* sc_in, int kbuf, int ksub, int vbuf, int vsub, f32x16* sc_out) {
-      bf16x8 kf[C::kSteps], vf[2];
-      load_kf(kbuf, ksub, kf);
+    // half step: softmax of sc_in, scores of the subtile whose K fragments are in
+    // kf into sc_out, O += V^T(vbuf, vsub) P^T. Once the last score MFMA has
+    // read kf, the fragments of the next half step's subtile (nkbuf, nksub),
+    // already in LDS, are fetched into kf so their latency hides behind the
+    // rest of this half step.
+    auto half_step = [&](const f32x16* sc_in, bf16x8* kf, int nkbuf, int nksub, int vbuf, int vsub,
+                         f32x16* sc_out) {
+      bf16x8 vf[2];
 #pragma unroll
       for (int s = 0; s < 2; ++s)
         vf[s] = __builtin_bit_cast(bf16x8, sV[vbuf][l32 * C::kVRow + 4 * vsub + 2 * s + half]);
@@ -245,13 +248,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       pslice(0, 1, 2);
       __builtin_amdgcn_sched_barrier(0);
       smfma(2, 1);
-      pslice(1, 1, 0);
-      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 3; s < C::kSteps; ++s) {
         smfma(s, 0);
         smfma(s, 1);
       }
+      __builtin_amdgcn_sched_barrier(0);
+      load_kf(nkbuf, nksub, kf);
+      pslice(1, 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
       pvmfma(0, 0);
       pslice(1, 1, 2);
       __builtin_amdgcn_sched_barrier(0);
@@ -261,7 +266,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // prologue: tiles 0 and 1 in LDS, tile 2 in registers, scores of subtile 0
+    // prologue: tiles 0 and 1 in LDS, tile 2 in registers, scores of subtile 0,
+    // K fragments of subtile 1
     load_tile(0);
     store_tile(0);
     load_tile(min(1, nkt - 1));
@@ -269,22 +275,21 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     load_tile(min(2, nkt - 1));
     __syncthreads();
     f32x16 sc_a[2], sc_b[2];
-    {
-      bf16x8 kf[C::kSteps];
-      load_kf(0, 0, kf);
+    bf16x8 kf[C::kSteps];
+    load_kf(0, 0, kf);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        sc_a[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[nb][0], cinit[nb], 0, 0, 0);
+    for (int nb = 0; nb < 2; ++nb) {
+      sc_a[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[nb][0], cinit[nb], 0, 0, 0);
 #pragma unroll
-        for (int s = 1; s < C::kSteps; ++s)
-          sc_a[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[nb][s], sc_a[nb], 0, 0, 0);
-      }
+      for (int s = 1; s < C::kSteps; ++s)
+        sc_a[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[nb][s], sc_a[nb], 0, 0, 0);
     }
+    load_kf(0, 1, kf);
     for (int t = 0; t < nkt; ++t) {
       const int b0 = t % 3, b1 = (t + 1) % 3, b2 = (t + 2) % 3;
-      half_step(sc_a, b0, 1, b0, 0, sc_b);   // softmax (t, 0); scores (t, 1)
-      half_step(sc_b, b1, 0, b0, 1, sc_a);   // softmax (t, 1); scores (t + 1, 0)
-      store_tile(b2);                        // tile t + 2 (the last tile again past the end)
+      half_step(sc_a, kf, b1, 0, b0, 0, sc_b);   // softmax (t, 0); scores (t, 1); prefetch K (t + 1, 0)
+      half_step(sc_b, kf, b1, 1, b0, 1, sc_a);   // softmax (t, 1); scores (t + 1, 0); prefetch K (t + 1, 1)
+      store_tile(b2);                            // tile t + 2 (the last tile again past the end)
       load_tile(min(t + 3, nkt - 1));
       __syncthreads();
     }
