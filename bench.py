@@ -11,10 +11,11 @@ Reported (one JSON line): TFLOP/s of algorithmic work (2 N^2 (2 d_c + r) per
 unit, padding and softmax not counted) over the whole step, windows/s, % of
 the bf16 dense MFMA peak, a roofline entry for the attention kernel (timed
 with HIP events on its own stream), per-kernel GB/s of the gathers and
-posgen, the window-size stack (windows 16/32/64/96, forward + backward), and
-the float64 CPU oracle timed on a bounded sample of units as a baseline.
+posgen, and the float64 CPU oracle timed on a bounded sample of units as a
+baseline; with --stack also the window-size stack (windows 16/32/64/96,
+forward + backward).
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--stack]
 """
 
 from __future__ import annotations
@@ -197,8 +198,9 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-units", type=int, default=4)
-    ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--cpu-units", type=int, default=40)
+    ap.add_argument("--stack", action="store_true",
+                    help="also time the window-size stack 16/32/64/96, forward + backward")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -290,7 +292,7 @@ def main():
         torch.cuda.synchronize()
         result["calibration_copy_bytes"] = 2 * n * 4
 
-    if not args.no_stack:
+    if args.stack:
         print("bench: window-size stack fwd+bwd", file=sys.stderr, flush=True)
         result["stack_fwd_bwd"] = stack_measure(max(5, args.steps // 3), 2, dev)
 
