@@ -17,6 +17,10 @@
 //  * dq: a workgroup owns 256 queries; it streams 64-key tiles of K_hat, V and
 //    K_hat^T (kappa) and accumulates dQ_hat^T += K_hat^T dS^T with one query
 //    per lane, like the forward.
+//  * The register-resident score operand (K in dkv, Q in dq) is pre-scaled by
+//    scale * log2(e), and -LSE2 / -D enter as the accumulator inputs of the
+//    score / dP MFMAs, so P = exp2(acc) and dS = P * acc: per score one exp2,
+//    one multiply and the bf16 packs, no other vector work.
 //  * Positional-gradient partials are written per unit in float32 and summed
 //    over units in a fixed order by a separate reduction.
 #include "internal.hpp"
@@ -42,6 +46,15 @@ struct BwdCfg {
 __device__ __forceinline__ bf16x8 lds_frag(const u32x4* p) { return __builtin_bit_cast(bf16x8, *p); }
 
 __device__ __forceinline__ bf16x8 zero_frag() { return __builtin_bit_cast(bf16x8, u32x4(0u)); }
+
+// bf16(c * f) element-wise: the register-resident score operand is pre-scaled by
+// scale * log2(e) so the score MFMA yields log2-domain logits directly.
+__device__ __forceinline__ bf16x8 scale_frag(bf16x8 f, float c) {
+  bf16x8 r;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r[j] = f32_to_bf16((float)f[j] * c);
+  return r;
+}
 
 // Loads the lane's 8 channels (16s + 8h ..) of row `row` of a [content 32 | pos rp] token.
 template <int KP>
@@ -94,7 +107,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
     const int key = k0 + nb * 32 + l32;
     const bool ok = key < N;
 #pragma unroll
-    for (int s = 0; s < C::kSteps; ++s) kf[nb][s] = ok ? token_frag<KP>(kw, kp, key, s, half) : zero_frag();
+    for (int s = 0; s < C::kSteps; ++s)
+      kf[nb][s] = ok ? scale_frag(token_frag<KP>(kw, kp, key, s, half), a.c) : zero_frag();
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       vf[nb][s] = ok ? __builtin_bit_cast(bf16x8, *(const u32x4*)(vw + (int64_t)key * 32 + s * 16 + half * 8))
@@ -123,8 +137,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
     lqt = *(const u32x4*)(qt + (int64_t)t_row * n_rows + q0 + t_ch * 8);
     if (p_on) lqpt = *(const u32x4*)(qpt + (int64_t)tp_row * n_rows + q0 + t_ch * 8);
     ldot = *(const u32x4*)(dot + (int64_t)t_row * n_rows + q0 + t_ch * 8);
-    if (tid < kTile) lfl = lse2[q0 + tid];
-    else if (tid < 2 * kTile) lfl = dd[q0 + tid - kTile];
+    if (tid < kTile) lfl = -lse2[q0 + tid];             // stored negated: MFMA accumulator inputs
+    else if (tid < 2 * kTile) lfl = -dd[q0 + tid - kTile];
   };
   auto store_tile = [&](int buf) {
     sQ[buf][r_tok * C::kRowC + r_ch] = lq;
@@ -155,15 +169,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int s = 0; s < 2; ++s) da[s] = lds_frag(&sDo[buf][(sub * 32 + l32) * C::kDRow + 2 * s + half]);
-      // per-query LSE and D of the lane's 16 accumulator rows
-      float lrow[16], drow[16];
+      // -LSE2 and -D of the lane's 16 accumulator rows (queries 8(v/4) + 4h + v%4)
+      f32x16 nl, nd;
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int qi = sub * 32 + 8 * gq + 4 * half;
         const f32x4 l4 = *(const f32x4*)&sL[buf][qi];
         const f32x4 d4 = *(const f32x4*)&sD[buf][qi];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) { lrow[4 * gq + i] = l4[i]; drow[4 * gq + i] = d4[i]; }
+        for (int i = 0; i < 4; ++i) { nl[4 * gq + i] = l4[i]; nd[4 * gq + i] = d4[i]; }
       }
       bf16x8 dta[2], qta[2], qpta[2];
 #pragma unroll
@@ -175,22 +189,21 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        f32x16 sc, dp;
+        // sc = S' - LSE2 (log2 domain), dp = dP - D
+        f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[0], kf[nb][0], nl, 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { sc[i] = 0.f; dp[i] = 0.f; }
-#pragma unroll
-        for (int s = 0; s < C::kSteps; ++s) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[nb][s], sc, 0, 0, 0);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[s], vf[nb][s], dp, 0, 0, 0);
+        for (int s = 1; s < C::kSteps; ++s) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[nb][s], sc, 0, 0, 0);
+        f32x16 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[0], vf[nb][0], nd, 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[1], vf[nb][1], dp, 0, 0, 0);
         bf16x8 pb[2], sb[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int v = 8 * s + j;
-            const float p = exp2f(fmaf(sc[v], c, -lrow[v]));
+            const float p = __builtin_amdgcn_exp2f(sc[v]);
             pb[s][j] = f32_to_bf16(p);
-            sb[s][j] = f32_to_bf16(p * (dp[v] - drow[v]));
+            sb[s][j] = f32_to_bf16(p * dp[v]);
           }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -270,7 +283,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     const int q = q0 + nb * 32 + l32;
     const bool ok = q < N;
 #pragma unroll
-    for (int s = 0; s < C::kSteps; ++s) qf[nb][s] = ok ? token_frag<KP>(qw, qp, q, s, half) : zero_frag();
+    for (int s = 0; s < C::kSteps; ++s)
+      qf[nb][s] = ok ? scale_frag(token_frag<KP>(qw, qp, q, s, half), a.c) : zero_frag();
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       df[nb][s] = ok ? __builtin_bit_cast(bf16x8, *(const u32x4*)(dow + (int64_t)q * 32 + s * 16 + half * 8))
@@ -278,6 +292,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     l2q[nb] = ok ? a.lse2[ub + q] : INFINITY;
     dq_d[nb] = ok ? a.dd[ub + q] : 0.f;
   }
+  // accumulator inputs: -LSE2 for the score MFMA, -D for the dP MFMA (one query per lane)
+  f32x16 nlq[2], ndq[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) { nlq[nb][i] = -l2q[nb]; ndq[nb][i] = -dq_d[nb]; }
 
   f32x16 acc_dq[2], acc_dqp[2];
 #pragma unroll
@@ -331,21 +351,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        f32x16 sc, dp;
+        f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[nb][0], nlq[nb], 0, 0, 0);
 #pragma unroll
-        for (int i = 0; i < 16; ++i) { sc[i] = 0.f; dp[i] = 0.f; }
-#pragma unroll
-        for (int s = 0; s < C::kSteps; ++s) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[nb][s], sc, 0, 0, 0);
-#pragma unroll
-        for (int s = 0; s < 2; ++s) dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[s], df[nb][s], dp, 0, 0, 0);
+        for (int s = 1; s < C::kSteps; ++s) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[nb][s], sc, 0, 0, 0);
+        f32x16 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], df[nb][0], ndq[nb], 0, 0, 0);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1], df[nb][1], dp, 0, 0, 0);
         bf16x8 sb[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int v = 8 * s + j;
-            const float p = exp2f(fmaf(sc[v], c, -l2q[nb]));
-            sb[s][j] = f32_to_bf16(p * (dp[v] - dq_d[nb]));
+            sb[s][j] = f32_to_bf16(__builtin_amdgcn_exp2f(sc[v]) * dp[v]);
           }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
