@@ -24,16 +24,21 @@
 //  * Fast pass (no running max): by Cauchy-Schwarz every score of query i is
 //    at most m_i = |q'_i| * max_j |k_hat_j|, so P = exp2(S' - m_i) <= 1 never
 //    overflows and needs no rescaling. The subtraction is free: the score
-//    MFMA accumulates onto a constant -m_i. The row sum is taken with
-//    v_dot2_f32_bf16 on the bf16 P pairs that feed the PV MFMA. Per score the
-//    vector work is one exp2, half a pack and half a dot2.
+//    MFMA accumulates onto a constant -m_i. The row sums go to the matrix
+//    pipe too: a v_mfma_f32_16x16x32_bf16 of each P block against a 0/1
+//    selector sums the exact bf16 P values the PV MFMA consumes (dot2 would
+//    occupy the matrix pipe anyway and fp32 adds cost more vector issue).
+//    Per score the vector work is one exp2 and half a pack.
 //  * Exact pass (fallback): if some row sum of a workgroup came out below
 //    2^-60 (the bound overshot so far that small terms could underflow) or is
 //    not finite, the workgroup recomputes its rows with the classic online
 //    softmax (running max, rescaling when the max grows by more than 2^8).
 //  * A workgroup is 4 waves x 64 queries; K and V^T tiles of 64 keys are
-//    double-buffered in LDS and shared by the 4 waves; workgroups of one unit
-//    are kept on one XCD (its L2 holds the unit's K and V).
+//    shared by the 4 waves through a ring of four LDS buffers filled by
+//    global-to-LDS DMA (buffer_load ... lds), issued three tiles ahead with
+//    fixed per-lane source offsets, so tile staging costs neither VGPRs nor
+//    vector instructions. Workgroups of one unit are kept on one XCD (its L2
+//    holds the unit's K and V).
 #include "internal.hpp"
 
 namespace rib {
@@ -47,16 +52,48 @@ constexpr float kLazyTau = 8.0f;          // log2 units
 constexpr float kUnderflowGuard = 8.673617379884035e-19f;  // 2^-60
 constexpr int kKeyBoundTile = 256;        // keys per partial key-norm maximum
 
+// s_waitcnt immediates (gfx9 encoding) waiting on the vector-memory counter
+// only: vmcnt in bits 3:0, expcnt (7) and lgkmcnt (15) left at their maxima.
+constexpr int kVmcntOnly = 0x0F70;
+constexpr int kVmcnt0 = kVmcntOnly | 0;
+constexpr int kVmcnt1 = kVmcntOnly | 1;
+constexpr int kVmcnt2 = kVmcntOnly | 2;
+constexpr int kVmcnt3 = kVmcntOnly | 3;
+constexpr int kVmcnt4 = kVmcntOnly | 4;
+
 __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32); }
+
+// Workgroup barrier without the release fence of __syncthreads: with tile DMA
+// in flight that fence waits for every outstanding vector-memory load, which
+// would cap the DMA lead at one tile. Callers wait explicitly for the DMA they
+// depend on; the waves write no LDS themselves. The memory clobber keeps the
+// compiler from moving LDS reads or DMA issue across it.
+__device__ __forceinline__ void barrier_dma() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int KP>  // positional 16-channel steps: 1 (r <= 16) or 2 (r <= 32)
 struct FwdCfg {
   static constexpr int kSteps = 2 + KP;             // MFMA K-steps of the score
-  static constexpr int kKRow = 2 * kSteps + 1;      // 16-byte chunks per K row in LDS (+1 pad)
-  static constexpr int kVRow = kKeyTile / 8 + 1;    // 16-byte chunks per V^T row in LDS (+1 pad)
-  static constexpr int kKChunks = kKeyTile * kKRow;
-  static constexpr int kVChunks = 32 * kVRow;
+  // One LDS tile buffer, in 16-byte chunks: K_c [64 keys][4 + 1 pad], then
+  // K_p [64 keys][2KP + 1 pad], then V^T [32 channels][8 + 1 pad] (padded to
+  // whole DMA instructions). The odd row strides keep the fragment reads
+  // free of bank conflicts.
+  static constexpr int kKcRow = 5;
+  static constexpr int kKpRow = 2 * KP + 1;
+  static constexpr int kVRow = kKeyTile / 8 + 1;
+  static constexpr int kKcOff = 0;
+  static constexpr int kKpOff = kKcOff + kKeyTile * kKcRow;
+  static constexpr int kVOff = kKpOff + kKeyTile * kKpRow;
+  static constexpr int kKcDma = kKeyTile * kKcRow / 64;          // DMA instructions per tile part
+  static constexpr int kKpDma = kKeyTile * kKpRow / 64;
+  static constexpr int kVDma = (32 * kVRow + 63) / 64;
+  static constexpr int kDma = kKcDma + kKpDma + kVDma;
+  static constexpr int kChunks = kVOff + 64 * kVDma;
+  static_assert(kKeyTile * kKcRow % 64 == 0 && kKeyTile * kKpRow % 64 == 0, "whole DMA instructions");
+  static_assert(kDma <= 4 * kWaves, "at most four DMA instructions per wave and tile");
 };
+constexpr int kBufs = 4;                  // LDS tile ring depth
+// word 3 of a raw buffer resource on gfx9-class parts (32-bit data format)
+constexpr int kRsrcWord3 = 0x00020000;
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
@@ -68,11 +105,11 @@ struct BoolTag {
 template <int KP>
 __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   typedef FwdCfg<KP> C;
-  // three K / V^T tile buffers: with the score MFMAs of the next subtile issued
-  // ahead of the current subtile's softmax, a buffer is overwritten only two
-  // tiles after it was last read, so one barrier per tile suffices.
-  __shared__ u32x4 sK[3][C::kKChunks];
-  __shared__ u32x4 sV[3][C::kVChunks];
+  // Ring of kBufs tile buffers. While tile t is processed, tiles t and t + 1
+  // are read (V^T of t, K of t and, prefetched, of t + 1) and the DMA for
+  // tile t + 3 fills the buffer tile t - 1 used; tile t + 2 must have landed
+  // by the end of tile t. Each DMA thus has two tiles of compute to arrive.
+  __shared__ u32x4 sT[kBufs][C::kChunks];
 
   const Geom& g = a.g;
   const int N = g.N, n_rows = g.n_rows;
@@ -83,7 +120,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int qb = logical - unit * nqb;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int half = lane >> 5, l32 = lane & 31;
   const int rp = 16 * KP;
 
@@ -130,31 +167,72 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     mref[nb] = sqrtf(sq) * kmax;
   }
 
-  // ---- tile loader: each thread moves up to three 16-byte chunks per tile
+  // ---- tile DMA: buffer_load ... lds writes lane l's 16 bytes to chunk l of
+  // the 64-chunk block its LDS base names. Instruction i of a tile fills
+  // chunks [64 i, 64 i + 64) of the buffer and is issued by wave i % 4; the
+  // per-lane source offsets are fixed, only the key offset moves per tile.
+  // Pad chunks fetch a duplicate of their row's first chunk.
   const int nkt = (N + kKeyTile - 1) / kKeyTile;
-  u32x4 ldK, ldKp, ldV;
-  const int kc_key = tid >> 2, kc_ch = tid & 3;                // K content: 64 keys x 4 chunks
-  const int kp_key = tid / (2 * KP), kp_ch = tid % (2 * KP);    // K pos: 64 keys x 2KP chunks
-  const bool kp_active = tid < kKeyTile * 2 * KP;
-  const int v_row = tid >> 3, v_ch = tid & 7;                   // V^T: 32 rows x 8 chunks
-  auto load_tile = [&](int t) {
+  const __amdgpu_buffer_rsrc_t rs_kc = __builtin_amdgcn_make_buffer_rsrc((void*)kw, 0, n_rows * 64, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_kp = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, n_rows * rp * 2, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc((void*)vt, 0, n_rows * 64, kRsrcWord3);
+  int dma_off[4];
+#pragma unroll
+  for (int jj = 0; jj < 4; ++jj) {
+    const int i = 4 * jj + wave;
+    const int c = 64 * i + lane;
+    int off = 0;
+    if (i < C::kKcDma) {
+      const int r = c / C::kKcRow, k = c % C::kKcRow;
+      off = r * 64 + (k < 4 ? k : 0) * 16;
+    } else if (i < C::kKcDma + C::kKpDma) {
+      const int c2 = c - C::kKpOff;
+      const int r = c2 / C::kKpRow, k = c2 % C::kKpRow;
+      off = r * rp * 2 + (k < 2 * KP ? k : 0) * 16;
+    } else {
+      const int c3 = c - C::kVOff;
+      int r = c3 / C::kVRow, k = c3 % C::kVRow;
+      if (r >= 32) r = 0, k = 0;
+      off = r * n_rows * 2 + (k < 8 ? k : 0) * 16;
+    }
+    dma_off[jj] = off;
+  }
+  const int dma_count = (C::kDma - wave + 3) / 4;   // DMA instructions of this wave per tile
+  auto dma_tile = [&](int t, int buf) {
     const int k0 = t * kKeyTile;
-    ldK = *(const u32x4*)(kw + (int64_t)(k0 + kc_key) * 32 + kc_ch * 8);
-    if (kp_active) ldKp = *(const u32x4*)(kp + (int64_t)(k0 + kp_key) * rp + kp_ch * 8);
-    ldV = *(const u32x4*)(vt + (int64_t)v_row * n_rows + k0 + v_ch * 8);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int i = 4 * jj + wave;
+      if (i < C::kDma) {
+        auto* dst = (__attribute__((address_space(3))) void*)&sT[buf][64 * i];
+        if (i < C::kKcDma)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kc, dst, 16, dma_off[jj] + k0 * 64, 0, 0, 0);
+        else if (i < C::kKcDma + C::kKpDma)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kp, dst, 16, dma_off[jj] + k0 * rp * 2, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, dst, 16, dma_off[jj] + k0 * 2, 0, 0, 0);
+      }
+    }
   };
-  auto store_tile = [&](int buf) {
-    sK[buf][kc_key * C::kKRow + kc_ch] = ldK;
-    if (kp_active) sK[buf][kp_key * C::kKRow + 4 + kp_ch] = ldKp;
-    sV[buf][v_row * C::kVRow + v_ch] = ldV;
+  // wait until only the newest tile's DMA (of this wave) may be in flight
+  auto dma_wait_older = [&]() {
+    if (dma_count == 4) __builtin_amdgcn_s_waitcnt(kVmcnt4);
+    else if (dma_count == 3) __builtin_amdgcn_s_waitcnt(kVmcnt3);
+    else if (dma_count == 2) __builtin_amdgcn_s_waitcnt(kVmcnt2);
+    else __builtin_amdgcn_s_waitcnt(kVmcnt1);
   };
   // score fragments of one 32-key subtile
   auto load_kf = [&](int buf, int sub, bf16x8* kf) {
+    const int row = sub * 32 + l32;
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s) {
-      const int ch = s < 2 ? 2 * s + half : 4 + 2 * (s - 2) + half;
-      kf[s] = __builtin_bit_cast(bf16x8, sK[buf][(sub * 32 + l32) * C::kKRow + ch]);
+      const int ch = s < 2 ? C::kKcOff + row * C::kKcRow + 2 * s + half
+                           : C::kKpOff + row * C::kKpRow + 2 * (s - 2) + half;
+      kf[s] = __builtin_bit_cast(bf16x8, sT[buf][ch]);
     }
+  };
+  auto vfrag = [&](int buf, int sub, int s) {
+    return __builtin_bit_cast(bf16x8, sT[buf][C::kVOff + l32 * C::kVRow + 4 * sub + 2 * s + half]);
   };
   auto mask_tail = [&](f32x16* sc, int key0) {
     const int kbase = key0 + 4 * half;
@@ -167,7 +245,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   auto pv = [&](int buf, int sub, const bf16x8 (*pf)[2], f32x16* acc) {
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const bf16x8 vf = __builtin_bit_cast(bf16x8, sV[buf][l32 * C::kVRow + 4 * sub + 2 * s + half]);
+      const bf16x8 vf = vfrag(buf, sub, s);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb)
         acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[nb][s], acc[nb], 0, 0, 0);
@@ -176,7 +254,6 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
 
   f32x16 acc[2];
   float m_run[2], l_run[2];
-  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
 
   // ===== fast pass: fixed per-query bound, software-pipelined over subtiles.
   // Each half step takes the softmax of one 32-key subtile while the score
@@ -197,7 +274,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       }
       m_run[nb] = mref[nb];
     }
-    float lsum[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
+    // Row sums on the matrix pipe: v_mfma_f32_16x16x32_bf16 with a 0/1 selector
+    // as A. Read as that MFMA's B operand, lane l of a P block holds query
+    // l % 16 + 16 * ((l / 16) % 2); the selector puts lane groups 0 and 2
+    // into row 0 and groups 1 and 3 into row 1, so rows 0 and 1 of the 16x16
+    // accumulator (lanes 0-15, elements 0 and 1) collect the sums of the
+    // block's queries 0-15 and 16-31 over the exact bf16 P values the PV MFMA
+    // consumes. (A dot2 on the vector pipe would wait for the matrix pipe.)
+    f32x4 lsum[2];
+    bf16x8 rsel;
+    {
+      const bf16 one = (lane & 15) == ((lane >> 4) & 1) ? (bf16)1.0f : (bf16)0.0f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) rsel[j] = one;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) lsum[nb] = f32x4(0.f);
+    }
 
     // half step: softmax of sc_in, scores of the subtile whose K fragments are in
     // kf into sc_out, O += V^T(vbuf, vsub) P^T. Once the last score MFMA has
@@ -208,10 +300,9 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
                          f32x16* sc_out) {
       bf16x8 vf[2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-        vf[s] = __builtin_bit_cast(bf16x8, sV[vbuf][l32 * C::kVRow + 4 * vsub + 2 * s + half]);
+      for (int s = 0; s < 2; ++s) vf[s] = vfrag(vbuf, vsub, s);
       u32x4 words[2][2];
-      // P words w0, w0+1 of block (nb, s): 4 exp2, 2 packs, 2 row-sum dot2
+      // P words w0, w0+1 of block (nb, s): 4 exp2, 2 packs
       auto pslice = [&](int nb, int s, int w0) {
 #pragma unroll
         for (int w = w0; w < w0 + 2; ++w) {
@@ -219,8 +310,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
           pr[0] = f32_to_bf16(__builtin_amdgcn_exp2f(sc_in[nb][8 * s + 2 * w]));
           pr[1] = f32_to_bf16(__builtin_amdgcn_exp2f(sc_in[nb][8 * s + 2 * w + 1]));
           words[nb][s][w] = __builtin_bit_cast(unsigned, pr);
-          lsum[nb][w & 1] = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lsum[nb][w & 1], false);
         }
+      };
+      auto rsmfma = [&](int s, int nb) {
+        lsum[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rsel, __builtin_bit_cast(bf16x8, words[nb][s]), lsum[nb],
+                                                           0, 0, 0);
       };
       auto smfma = [&](int s, int nb) {
         sc_out[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[nb][s], s == 0 ? cinit[nb] : sc_out[nb], 0,
@@ -239,12 +333,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       pslice(1, 0, 0);
       __builtin_amdgcn_sched_barrier(0);
       smfma(1, 0);
+      rsmfma(0, 0);
       pslice(1, 0, 2);
       __builtin_amdgcn_sched_barrier(0);
       smfma(1, 1);
       pslice(0, 1, 0);
       __builtin_amdgcn_sched_barrier(0);
       smfma(2, 0);
+      rsmfma(0, 1);
       pslice(0, 1, 2);
       __builtin_amdgcn_sched_barrier(0);
       smfma(2, 1);
@@ -258,21 +354,23 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       pslice(1, 1, 0);
       __builtin_amdgcn_sched_barrier(0);
       pvmfma(0, 0);
+      rsmfma(1, 0);
       pslice(1, 1, 2);
       __builtin_amdgcn_sched_barrier(0);
       pvmfma(0, 1);
       pvmfma(1, 0);
       pvmfma(1, 1);
+      rsmfma(1, 1);
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // prologue: tiles 0 and 1 in LDS, tile 2 in registers, scores of subtile 0,
-    // K fragments of subtile 1
-    load_tile(0);
-    store_tile(0);
-    load_tile(min(1, nkt - 1));
-    store_tile(1);
-    load_tile(min(2, nkt - 1));
+    // prologue: tiles 0 and 1 in LDS, tile 2 on its way, scores of subtile 0,
+    // K fragments of subtile 1. Tiles past the end repeat the last tile (read
+    // only by the unused scores of the subtile after the last).
+    dma_tile(0, 0);
+    dma_tile(min(1, nkt - 1), 1);
+    dma_tile(min(2, nkt - 1), 2);
+    dma_wait_older();
     __syncthreads();
     f32x16 sc_a[2], sc_b[2];
     bf16x8 kf[C::kSteps];
@@ -286,16 +384,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     }
     load_kf(0, 1, kf);
     for (int t = 0; t < nkt; ++t) {
-      const int b0 = t % 3, b1 = (t + 1) % 3, b2 = (t + 2) % 3;
+      const int b0 = t % kBufs, b1 = (t + 1) % kBufs;
+      dma_tile(min(t + 3, nkt - 1), (t + 3) % kBufs);
       half_step(sc_a, kf, b1, 0, b0, 0, sc_b);   // softmax (t, 0); scores (t, 1); prefetch K (t + 1, 0)
       half_step(sc_b, kf, b1, 1, b0, 1, sc_a);   // softmax (t, 1); scores (t + 1, 0); prefetch K (t + 1, 1)
-      store_tile(b2);                            // tile t + 2 (the last tile again past the end)
-      load_tile(min(t + 3, nkt - 1));
-      __syncthreads();
+      dma_wait_older();                          // tile t + 2 landed (this wave's part)
+      barrier_dma();
     }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
-      l_run[nb] = lsum[nb][0] + lsum[nb][1];
+      // query l32 of block nb: row l32 / 16 of lane l32 % 16; kept on half 0
+      const float r0 = __shfl(lsum[nb][0], l32 & 15), r1 = __shfl(lsum[nb][1], l32 & 15);
+      l_run[nb] = half == 0 ? (l32 < 16 ? r0 : r1) : 0.f;
       pad_sub[nb] = (float)(nkt * kKeyTile - N) * (float)f32_to_bf16(__builtin_amdgcn_exp2f(-mref[nb]));
     }
   }
@@ -319,12 +419,15 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       m_run[nb] = -INFINITY;
       l_run[nb] = 0.f;
     }
-    load_tile(0);
-    store_tile(0);
+    // drain the fast pass's DMA (tiles past the end) before reusing buffers
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+    dma_tile(0, 0);
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
     for (int t = 0; t < nkt; ++t) {
       const int buf = t & 1;
-      if (t + 1 < nkt) load_tile(t + 1);
+      if (t + 1 < nkt) dma_tile(t + 1, buf ^ 1);
       const bool tail = (t + 1) * kKeyTile > N;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
@@ -367,7 +470,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
         }
         pv(buf, sub, pf, acc);
       }
-      if (t + 1 < nkt) store_tile(buf ^ 1);
+      __builtin_amdgcn_s_waitcnt(kVmcnt0);
       __syncthreads();
     }
   }
