@@ -26,4 +26,6 @@ from .rib import (  # noqa: F401
     rib_window_attn_fwd,
     rib_window_attn_bwd,
     default_scale,
+    gelu_grad,
+    posgen_bwd,
 )

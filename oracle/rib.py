@@ -35,6 +35,9 @@ Readings where the pages are silent (each is also listed in the design notes):
   R9  V is content only; O has d_c channels
   R10 non-overlapping windows, no shift, no padding; H and W divisible by w
   R14 D_i = sum_j P_ij dP_ij (textbook softmax backward)
+  R16 the position MLP is trained with the network: the positional gradients
+      dQ_p, dK_p continue through Linear -> GELU -> Linear into dW1, db1,
+      dW2, db2 by the chain rule; GELU'(z) = Phi(z) + z phi(z) (erf form, R5)
 
 Parity pins live in ``tests/test_oracle_*.py`` (closed forms, invariants,
 library routines, brute force and hand-derived fixtures in ``tests/golden/``).
@@ -51,6 +54,7 @@ __all__ = [
     "window_partition", "window_unpartition", "unit_index", "unit_slices",
     "concat_scores", "attention_window_fwd", "attention_window_bwd",
     "rib_window_attn_fwd", "rib_window_attn_bwd", "default_scale",
+    "gelu_grad", "posgen_bwd",
 ]
 
 
@@ -131,6 +135,52 @@ def posgen(w: int, n_freq: int, w1, b1, w2, b2, rank: int):
     h = gelu(phi @ w1.T + b1)
     out = h @ w2.T + b2
     return out[:, :rank].copy(), out[:, rank:2 * rank].copy()
+
+
+def gelu_grad(z: np.ndarray) -> np.ndarray:
+    """Derivative of the exact GELU (reading R5): Phi(z) + z phi(z), with Phi the
+    standard normal CDF 0.5 (1 + erf(z / sqrt 2)) and phi its density
+    exp(-z^2 / 2) / sqrt(2 pi)."""
+    z = np.asarray(z, dtype=np.float64)
+    erf = np.vectorize(math.erf, otypes=[np.float64])
+    cdf = 0.5 * (1.0 + erf(z / math.sqrt(2.0)))
+    pdf = np.exp(-0.5 * z * z) / math.sqrt(2.0 * math.pi)
+    return cdf + z * pdf
+
+
+def posgen_bwd(w: int, n_freq: int, w1, b1, w2, b2, rank: int, dq_p, dk_p):
+    """Weight gradients of the position MLP [DE §2.A.2: a lightweight MLP maps the
+    Fourier features to Q_p, K_p], reading R16.
+
+    Given dQ_p, dK_p ([N, r] each) for the outputs of ``posgen``, with
+    phi the Fourier features (no parameters), z = phi W1^T + b1, h = GELU(z)
+    and d_out = [dQ_p | dK_p] (Q_p first, R6):
+      dW2 = d_out^T h        db2 = sum_t d_out[t]
+      dh  = d_out W2         dz  = dh * GELU'(z)
+      dW1 = dz^T phi         db1 = sum_t dz[t]
+    Returns float64 (dw1 [hidden, 4F], db1 [hidden], dw2 [2r, hidden], db2 [2r]).
+    """
+    w1 = np.asarray(w1, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    hidden = w1.shape[0]
+    if w1.shape != (hidden, 4 * n_freq) or w2.shape != (2 * rank, hidden):
+        raise ValueError("weight shapes do not match n_freq / hidden / rank")
+    b1 = np.zeros(hidden) if b1 is None else np.asarray(b1, dtype=np.float64)
+    N = w * w
+    dq_p = np.asarray(dq_p, dtype=np.float64)
+    dk_p = np.asarray(dk_p, dtype=np.float64)
+    if dq_p.shape != (N, rank) or dk_p.shape != (N, rank):
+        raise ValueError("dq_p and dk_p must be [w*w, rank]")
+    phi = fourier_features(w, n_freq)
+    z = phi @ w1.T + b1
+    h = gelu(z)
+    d_out = np.concatenate([dq_p, dk_p], axis=1)
+    dw2 = d_out.T @ h
+    db2 = d_out.sum(axis=0)
+    dz = (d_out @ w2) * gelu_grad(z)
+    dw1 = dz.T @ phi
+    db1 = dz.sum(axis=0)
+    return dw1, db1, dw2, db2
 
 
 # ----------------------------------------------------------------------------

@@ -14,6 +14,7 @@ import oracle
 import oracle.rib as orib
 import test_oracle_attention as ta
 import test_oracle_posgen as tp
+import test_oracle_posgen_bwd as tb
 
 
 def _golden():
@@ -103,6 +104,38 @@ def _partition_col_major(x, w):
     return out[:, :, perm, :]
 
 
+def _gelu_grad_cdf_only(z):
+    z = np.asarray(z, np.float64)
+    erf = np.vectorize(math.erf, otypes=[np.float64])
+    return 0.5 * (1.0 + erf(z / math.sqrt(2.0)))          # the z phi(z) term dropped
+
+
+def _gelu_grad_tanh(z):
+    z = np.asarray(z, np.float64)
+    c = math.sqrt(2 / math.pi)
+    u = c * (z + 0.044715 * z ** 3)
+    t = np.tanh(u)
+    return 0.5 * (1 + t) + 0.5 * z * (1 - t * t) * c * (1 + 3 * 0.044715 * z * z)
+
+
+def _posgen_bwd_no_gelu_grad(w, F, w1, b1, w2, b2, r, dq, dk):
+    phi = orib.fourier_features(w, F)
+    z = phi @ np.asarray(w1).T + (0 if b1 is None else np.asarray(b1))
+    h = orib.gelu(z)
+    d_out = np.hstack([dq, dk])
+    dz = d_out @ np.asarray(w2)                            # GELU' missing
+    return dz.T @ phi, dz.sum(0), d_out.T @ h, d_out.sum(0)
+
+
+def _posgen_bwd_split_swapped(w, F, w1, b1, w2, b2, r, dq, dk):
+    return orib.__dict__["_orig_posgen_bwd"](w, F, w1, b1, w2, b2, r, dk, dq)
+
+
+def _posgen_bwd_w1_transposed(w, F, w1, b1, w2, b2, r, dq, dk):
+    g = list(orib.__dict__["_orig_posgen_bwd"](w, F, w1, b1, w2, b2, r, dq, dk))
+    return g[0].T.reshape(g[0].shape), g[1], g[2], g[3]
+
+
 MUTATIONS = [
     ("concat_scores", _scores_no_bias, [(ta.test_worked_example_w2, "golden"), (ta.test_concat_identity,)]),
     ("concat_scores", _scores_transposed_bias, [(ta.test_concat_identity,), (ta.test_matches_torch_sdpa_with_additive_bias,)]),
@@ -116,6 +149,11 @@ MUTATIONS = [
     ("posgen", _posgen_swapped, [(tp.test_posgen_matches_torch_mlp, 16, 8)]),
     ("gelu", _gelu_tanh, [(tp.test_gelu_matches_torch,), (tp.test_posgen_matches_torch_mlp, 32, 16)]),
     ("window_partition", _partition_col_major, [(ta.test_partition_bijection_brute_force, 2, 6, 9, 2, 3, 3)]),
+    ("gelu_grad", _gelu_grad_cdf_only, [(tb.test_gelu_grad_closed_forms,), (tb.test_posgen_bwd_finite_differences, 3, 2, 5, 2)]),
+    ("gelu_grad", _gelu_grad_tanh, [(tb.test_gelu_grad_closed_forms,), (tb.test_posgen_bwd_matches_torch_autograd, 8, 16, 64, 8)]),
+    ("posgen_bwd", _posgen_bwd_no_gelu_grad, [(tb.test_posgen_bwd_finite_differences, 3, 2, 5, 2)]),
+    ("posgen_bwd", _posgen_bwd_split_swapped, [(tb.test_posgen_bwd_finite_differences, 3, 2, 5, 2), (tb.test_posgen_bwd_split_and_linearity,)]),
+    ("posgen_bwd", _posgen_bwd_w1_transposed, [(tb.test_posgen_bwd_matches_torch_autograd, 8, 16, 64, 8)]),
 ]
 
 
@@ -123,7 +161,8 @@ MUTATIONS = [
 def test_planted_mistake_is_caught(monkeypatch, name, bad, pins):
     orig = getattr(orib, name)
     for key, fn in (("_orig_bwd", orib.attention_window_bwd), ("_orig_fourier", orib.fourier_features),
-                    ("_orig_posgen", orib.posgen), ("_orig_partition", orib.window_partition)):
+                    ("_orig_posgen", orib.posgen), ("_orig_partition", orib.window_partition),
+                    ("_orig_posgen_bwd", orib.posgen_bwd)):
         monkeypatch.setitem(orib.__dict__, key, fn)
     monkeypatch.setattr(orib, name, bad)
     monkeypatch.setattr(oracle, name, bad)
