@@ -145,7 +145,10 @@ def cpu_baseline(wl, x, n_units: int):
 
 
 def stack_measure(steps: int, warmup: int, dev):
-    """Forward + backward over the window-size stack (16, 32, 64, 96), per layer and total."""
+    """One training step of the window-size stack (16, 32, 64, 96), per layer and total: posgen,
+    attention forward, attention backward and the position-MLP weight gradients. The weights change
+    every training step, so posgen runs every step (the forward plans keep the tokens of the same
+    weights)."""
     import torch
     import rib_synth
     import windowed_attention_implicit_amd as rib
@@ -158,12 +161,21 @@ def stack_measure(steps: int, warmup: int, dev):
         fp = rib.FwdPlan(q, k, v, qp, kp, wl.w)
         o, lse = fp.run()
         bp = rib.BwdPlan(q, k, v, qp, kp, o, lse, do, wl.w)
-        layers.append((wl, fp, bp))
+        bp.run()
+
+        def mlp_fwd(wl=wl, w1=w1, w2=w2):
+            return rib.posgen(wl.w, w1, None, w2, None, wl.r, out_dtype=torch.bfloat16)
+
+        def mlp_bwd(wl=wl, w1=w1, w2=w2, bp=bp):
+            return rib.posgen_bwd(wl.w, w1, None, w2, None, wl.r, bp.dqp, bp.dkp)
+        layers.append((wl, fp, bp, mlp_fwd, mlp_bwd))
 
     def run_all():
-        for _, fp, bp in layers:
+        for _, fp, bp, mlp_fwd, mlp_bwd in layers:
+            mlp_fwd()
             fp.run()
             bp.run()
+            mlp_bwd()
 
     def reset():
         for g in rib.KERNEL_GROUPS:
@@ -171,8 +183,11 @@ def stack_measure(steps: int, warmup: int, dev):
 
     rib.kernel_timing_enable(True)
     ms, _ = time_steps(run_all, steps, warmup, reset)
+    pg = [kernel_avg_ms(rib, g)[0] for g in ("posgen", "posgen_bwd")]
     per = []
-    for wl, fp, bp in layers:
+    for wl, fp, bp, _, mlp_bwd in layers:
+        time_steps(mlp_bwd, steps, 2, reset)
+        pgb, _ = kernel_avg_ms(rib, "posgen_bwd")
         t_f, _ = time_steps(fp.run, steps, 2, reset)
         fa, _ = kernel_avg_ms(rib, "attn_fwd")
         t_b, _ = time_steps(bp.run, steps, 2, reset)
@@ -183,13 +198,16 @@ def stack_measure(steps: int, warmup: int, dev):
                     "fwd_tflops": round(ff / t_f / 1e9, 1), "bwd_tflops": round(bf / t_b / 1e9, 1),
                     "attn_fwd_kernel_ms": fa and round(fa, 4), "bwd_dkv_kernel_ms": dkv and round(dkv, 4),
                     "bwd_dq_kernel_ms": dq and round(dq, 4),
-                    "bwd_kernels_tflops": (dkv and dq) and round(bf / (dkv + dq) / 1e9, 1)})
+                    "bwd_kernels_tflops": (dkv and dq) and round(bf / (dkv + dq) / 1e9, 1),
+                    "posgen_bwd_kernels_ms": pgb and round(pgb, 4)})
     rib.kernel_timing_enable(False)
     total = sum(fwd_flops(wl.units, wl.N, wl.d_c, wl.r) + bwd_flops(wl.units, wl.N, wl.d_c, wl.r)
-                for wl, _, _ in layers)
+                for wl, *_ in layers)
     return {"workload": "window-size stack 16/32/64/96 on a 192x192 map, batch 2, 6 heads, d_c=32, r=16, bf16, "
-                        "forward + backward", "ms_per_step": round(ms, 4),
-            "tflops": round(total / ms / 1e9, 1), "layers": per}
+                        "training step: posgen + forward + backward + position-MLP weight gradients",
+            "ms_per_step": round(ms, 4), "tflops": round(total / ms / 1e9, 1),
+            "posgen_ms_avg": pg[0] and round(pg[0], 4), "posgen_bwd_ms_avg": pg[1] and round(pg[1], 4),
+            "layers": per}
 
 
 def main():

@@ -165,6 +165,41 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
                                  rib_stream_t stream);
 
 /*
+ * rib_posgen_bwd - weight gradients of the position MLP [DE §2.A.2: a
+ * lightweight MLP maps the Fourier features to Q_p and K_p; it is trained with
+ * the network, so the positional gradients continue into its weights].
+ *
+ * With phi the Fourier features of rib_posgen (no parameters), z = W1 phi + b1,
+ * h = GELU(z) (erf form) and d_out = [dQ_p | dK_p] per token:
+ *   dW2 = sum_t d_out h^T, db2 = sum_t d_out,
+ *   dz = (W2^T d_out) * GELU'(z), GELU'(z) = Phi(z) + z phi(z) (normal CDF, density),
+ *   dW1 = sum_t dz phi^T, db1 = sum_t dz.
+ * Outputs are overwritten, not accumulated. Deterministic: up to 1024 blocks
+ * each sum a fixed set of token tiles (up to 32 tokens) into their own slot of
+ * the workspace, and a second kernel adds the slots in block order. Float32
+ * throughout.
+ *
+ *   w, mlp      as for rib_posgen (same limits; b1 / b2 may be NULL for zeros);
+ *               W1, b1, W2 and one token's tile, staged in LDS, must fit 64 KB
+ *               (every MLP rib_posgen accepts does)
+ *   dq_p, dk_p  (device) float32 [w*w, rank]: gradients w.r.t. Q_p and K_p, e.g.
+ *               the dq_p / dk_p of rib_window_attn_bwd (summed over every unit)
+ *   dw1         (device) output float32 [hidden, 4F]
+ *   db1         (device) output float32 [hidden], or NULL to skip
+ *   dw2         (device) output float32 [2r, hidden]
+ *   db2         (device) output float32 [2r], or NULL to skip
+ *   workspace   (device) at least rib_posgen_bwd_workspace_size() bytes, 4-byte
+ *               aligned, caller-owned; its contents on return are unspecified
+ * Errors: RIB_ERR_INVALID_ARG for bad sizes, NULL or misaligned pointers;
+ * RIB_ERR_WORKSPACE for a missing or short workspace; RIB_ERR_UNSUPPORTED beyond
+ * the limits above. Nothing is launched when an error is returned.
+ */
+size_t rib_posgen_bwd_workspace_size(int32_t w, const rib_mlp_t* mlp);
+rib_status_t rib_posgen_bwd(int32_t w, const rib_mlp_t* mlp, const float* dq_p, const float* dk_p,
+                            float* dw1, float* db1, float* dw2, float* db2,
+                            void* workspace, size_t workspace_bytes, rib_stream_t stream);
+
+/*
  * Kernel timing, a measurement aid: while enabled, every posgen / forward /
  * backward call brackets each of its kernel groups with HIP events recorded
  * on the call's stream. rib_kernel_timing_read() waits for the recorded
@@ -182,7 +217,8 @@ typedef enum {
   RIB_KERNEL_ATTN_BWD_DKV = 5, /* the backward dK / dV kernel alone */
   RIB_KERNEL_ATTN_BWD_DQ = 6,  /* the backward dQ kernel alone */
   RIB_KERNEL_POS_REDUCE = 7,   /* the fixed-order sum of the dQ_p / dK_p partials */
-  RIB_KERNEL_COUNT = 8
+  RIB_KERNEL_POSGEN_BWD = 8,   /* the position-MLP weight-gradient kernels (partials + sum) */
+  RIB_KERNEL_COUNT = 9
 } rib_kernel_t;
 
 rib_status_t rib_kernel_timing_enable(int32_t enable);

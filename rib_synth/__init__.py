@@ -150,6 +150,24 @@ def make_positional(N: int, r: int, dtype: str, seed: int, std: float = 0.5) -> 
     return Tensor("bf16", bf16_bits(qp)), Tensor("bf16", bf16_bits(kp))
 
 
+def make_mlp(n_freq: int, hidden: int, r: int, seed: int, std: float = 0.3, bias_std: float = 0.1) -> dict:
+    """Position-MLP weights w1 [hidden, 4F], b1, w2 [2r, hidden], b2 (float32), larger than the
+    workloads' N(0, 0.02^2) so that GELU is exercised away from its linear part."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return {
+        "w1": (std * rng.standard_normal((hidden, 4 * n_freq))).astype(np.float32),
+        "b1": (bias_std * rng.standard_normal(hidden)).astype(np.float32),
+        "w2": (std * rng.standard_normal((2 * r, hidden))).astype(np.float32),
+        "b2": (bias_std * rng.standard_normal(2 * r)).astype(np.float32),
+    }
+
+
+def make_pos_grads(N: int, r: int, seed: int) -> tuple:
+    """Stand-in upstream gradients dQ_p, dK_p: float32 N(0, 1) of shape [N, r]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return (rng.standard_normal((N, r), dtype=np.float32), rng.standard_normal((N, r), dtype=np.float32))
+
+
 def custom_workload(B, H, W, heads, d_c, w, r, dtype="bf16", backward=False, seed=0,
                     n_freq=N_FREQ, hidden=HIDDEN) -> Workload:
     """A workload of arbitrary shape (small and ragged test cases)."""

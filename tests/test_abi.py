@@ -117,6 +117,38 @@ def test_posgen_validation(L):
     assert L.rib_posgen(96, ctypes.byref(mlp), rib.RIB_BF16, None, FAKE, None) == rib.RIB_ERR_INVALID_ARG
 
 
+def test_posgen_bwd_validation(L):
+    """Every call below fails validation before any launch (FAKE is never dereferenced)."""
+    mlp = rib._Mlp(16, 64, 16, FAKE.value, None, FAKE.value, None)
+    need = L.rib_posgen_bwd_workspace_size(96, ctypes.byref(mlp))
+    # one partial set per block: min(tiles, 1024) blocks, tiles of 32 tokens at w = 96 ...
+    assert need == 4 * (96 * 96 // 32) * (64 * 64 + 64 + 32 * 64 + 32)
+    # ... and of a single token when 25 tokens could not otherwise make 128 tiles
+    small = rib._Mlp(4, 8, 2, FAKE.value, None, FAKE.value, None)
+    assert L.rib_posgen_bwd_workspace_size(5, ctypes.byref(small)) == 4 * 25 * (8 * 16 + 8 + 4 * 8 + 4)
+    assert L.rib_posgen_bwd_workspace_size(1, ctypes.byref(mlp)) == 0
+    assert L.rib_posgen_bwd_workspace_size(96, None) == 0
+
+    def call(w=96, m=mlp, dq=FAKE, dk=FAKE, dw1=FAKE, db1=FAKE, dw2=FAKE, db2=FAKE, ws=FAKE, nbytes=None):
+        return L.rib_posgen_bwd(w, None if m is None else ctypes.byref(m), dq, dk, dw1, db1, dw2, db2, ws,
+                                need if nbytes is None else nbytes, None)
+
+    assert call(w=1) == rib.RIB_ERR_INVALID_ARG
+    assert call(w=257) == rib.RIB_ERR_UNSUPPORTED
+    assert call(m=None) == rib.RIB_ERR_INVALID_ARG
+    assert call(m=rib._Mlp(16, 64, 33, FAKE.value, None, FAKE.value, None)) == rib.RIB_ERR_UNSUPPORTED
+    big = rib._Mlp(16, 128, 32, FAKE.value, None, FAKE.value, None)   # the weights alone exceed 64 KB
+    assert call(m=big) == rib.RIB_ERR_UNSUPPORTED
+    assert call(m=rib._Mlp(16, 64, 16, None, None, FAKE.value, None)) == rib.RIB_ERR_INVALID_ARG
+    assert call(dq=None) == rib.RIB_ERR_INVALID_ARG
+    assert call(dk=None) == rib.RIB_ERR_INVALID_ARG
+    assert call(dw1=None) == rib.RIB_ERR_INVALID_ARG
+    assert call(dw2=None) == rib.RIB_ERR_INVALID_ARG
+    assert call(dq=ctypes.c_void_p(FAKE.value + 2)) == rib.RIB_ERR_INVALID_ARG
+    assert call(ws=None) == rib.RIB_ERR_WORKSPACE
+    assert call(nbytes=need - 4) == rib.RIB_ERR_WORKSPACE
+
+
 def test_partition_validation(L):
     s = rib.Shape(1, 96, 96, 6, 32, 96, 1)
     assert L.rib_window_partition(ctypes.byref(s), rib.RIB_BF16, None, FAKE, None) == rib.RIB_ERR_INVALID_ARG

@@ -23,7 +23,7 @@ import torch
 __all__ = [
     "RIB_OK", "RIB_ERR_INVALID_ARG", "RIB_ERR_UNSUPPORTED", "RIB_ERR_WORKSPACE", "RIB_ERR_HIP",
     "RIB_F32", "RIB_BF16", "RibError", "lib", "lib_path", "exported_symbols",
-    "posgen", "window_partition", "window_unpartition", "window_attn_fwd", "window_attn_bwd",
+    "posgen", "posgen_bwd", "window_partition", "window_unpartition", "window_attn_fwd", "window_attn_bwd",
     "fwd_workspace_size", "bwd_workspace_size", "FwdPlan", "BwdPlan", "Shape",
     "KERNEL_GROUPS", "kernel_timing_enable", "kernel_timing_read",
 ]
@@ -57,6 +57,8 @@ _LIB = None
 _vp, _sz, _i32, _f32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
 _SIGS = {
     "rib_posgen": (_i32, [_i32, ctypes.POINTER(_Mlp), _i32, _vp, _vp, _vp]),
+    "rib_posgen_bwd_workspace_size": (_sz, [_i32, ctypes.POINTER(_Mlp)]),
+    "rib_posgen_bwd": (_i32, [_i32, ctypes.POINTER(_Mlp)] + [_vp] * 6 + [_vp, _sz, _vp]),
     "rib_window_partition": (_i32, [ctypes.POINTER(Shape), _i32, _vp, _vp, _vp]),
     "rib_window_unpartition": (_i32, [ctypes.POINTER(Shape), _i32, _vp, _vp, _vp]),
     "rib_fwd_workspace_size": (_sz, [ctypes.POINTER(Shape), _i32]),
@@ -159,6 +161,31 @@ def posgen(w: int, w1: torch.Tensor, b1, w2: torch.Tensor, b2, rank: int, n_freq
     return qp, kp
 
 
+def posgen_bwd(w: int, w1: torch.Tensor, b1, w2: torch.Tensor, b2, rank: int, dq_p: torch.Tensor,
+               dk_p: torch.Tensor, n_freq: int = 16):
+    """Position-MLP weight gradients (dW1, db1, dW2, db2), float32, from dQ_p, dK_p (float32 [w*w, rank])."""
+    _require_gpu(w1, b1, w2, b2, dq_p, dk_p)
+    for t in (w1, b1, w2, b2, dq_p, dk_p):
+        if t is not None and (t.dtype != torch.float32 or not t.is_contiguous()):
+            raise TypeError("weights and positional gradients are contiguous float32")
+    if dq_p.shape != (w * w, rank) or dk_p.shape != (w * w, rank):
+        raise ValueError("dq_p and dk_p must be [w*w, rank]")
+    hidden = w1.shape[0]
+    mlp = _Mlp(n_freq, hidden, rank, w1.data_ptr(), b1.data_ptr() if b1 is not None else None,
+               w2.data_ptr(), b2.data_ptr() if b2 is not None else None)
+    nbytes = lib().rib_posgen_bwd_workspace_size(w, ctypes.byref(mlp))
+    if nbytes == 0:
+        _check(lib().rib_posgen_bwd(w, ctypes.byref(mlp), None, None, None, None, None, None, None, 0, None))
+    ws = _workspace(nbytes, w1.device)
+    dw1 = torch.empty((hidden, 4 * n_freq), dtype=torch.float32, device=w1.device)
+    db1 = torch.empty((hidden,), dtype=torch.float32, device=w1.device)
+    dw2 = torch.empty((2 * rank, hidden), dtype=torch.float32, device=w1.device)
+    db2 = torch.empty((2 * rank,), dtype=torch.float32, device=w1.device)
+    _check(lib().rib_posgen_bwd(w, ctypes.byref(mlp), _ptr(dq_p), _ptr(dk_p), _ptr(dw1), _ptr(db1), _ptr(dw2),
+                                _ptr(db2), _ptr(ws), nbytes, _stream(w1.device)))
+    return dw1, db1, dw2, db2
+
+
 # ---------------------------------------------------------------- partition
 
 def window_partition(x: torch.Tensor, w: int) -> torch.Tensor:
@@ -248,7 +275,7 @@ def window_attn_bwd(q_c, k_c, v, q_p, k_p, o, lse, d_o, w: int, scale: float | N
 
 
 KERNEL_GROUPS = {"posgen": 0, "partition": 1, "attn_fwd": 2, "unpartition": 3, "bwd_prep": 4,
-                 "attn_bwd_dkv": 5, "attn_bwd_dq": 6, "pos_reduce": 7}
+                 "attn_bwd_dkv": 5, "attn_bwd_dq": 6, "pos_reduce": 7, "posgen_bwd": 8}
 
 
 def kernel_timing_enable(enable: bool = True):

@@ -280,24 +280,28 @@ rib_status_t rib_kernel_timing_read(rib_kernel_t kernel, double* total_ms, int64
   }
 }
 
+// Limits shared by rib_posgen and rib_posgen_bwd.
+static rib_status_t check_mlp(int32_t w, const rib_mlp_t* mlp) {
+  if (w < 2) return fail(RIB_ERR_INVALID_ARG, "window size w=%d must be >= 2", w);
+  if (w > kMaxW) return fail(RIB_ERR_UNSUPPORTED, "window size w=%d exceeds %d", w, kMaxW);
+  if (!mlp) return fail(RIB_ERR_INVALID_ARG, "mlp is NULL");
+  if (mlp->n_freq < 1 || mlp->n_freq > 16) return fail(RIB_ERR_UNSUPPORTED, "n_freq=%d must be in 1..16", mlp->n_freq);
+  if (mlp->hidden < 1 || mlp->hidden > 128) return fail(RIB_ERR_UNSUPPORTED, "hidden=%d must be in 1..128", mlp->hidden);
+  if (mlp->rank < 1 || mlp->rank > 32) return fail(RIB_ERR_UNSUPPORTED, "rank=%d must be in 1..32", mlp->rank);
+  if (!mlp->w1 || !mlp->w2) return fail(RIB_ERR_INVALID_ARG, "mlp weights are NULL");
+  if (((uintptr_t)mlp->w1 | (uintptr_t)mlp->w2 | (uintptr_t)mlp->b1 | (uintptr_t)mlp->b2) & 3u)
+    return fail(RIB_ERR_INVALID_ARG, "mlp weights must be 4-byte aligned");
+  return RIB_OK;
+}
+
 rib_status_t rib_posgen(int32_t w, const rib_mlp_t* mlp, rib_dtype_t out_dtype, void* q_p, void* k_p,
                         rib_stream_t stream) {
   try {
-    if (w < 2) return fail(RIB_ERR_INVALID_ARG, "window size w=%d must be >= 2", w);
-    if (w > kMaxW) return fail(RIB_ERR_UNSUPPORTED, "window size w=%d exceeds %d", w, kMaxW);
-    if (!mlp) return fail(RIB_ERR_INVALID_ARG, "mlp is NULL");
+    RIB_TRY(check_mlp(w, mlp));
     if (!dtype_ok(out_dtype)) return fail(RIB_ERR_INVALID_ARG, "out_dtype %d invalid", (int)out_dtype);
-    if (mlp->n_freq < 1 || mlp->n_freq > 16)
-      return fail(RIB_ERR_UNSUPPORTED, "n_freq=%d must be in 1..16", mlp->n_freq);
-    if (mlp->hidden < 1 || mlp->hidden > 128)
-      return fail(RIB_ERR_UNSUPPORTED, "hidden=%d must be in 1..128", mlp->hidden);
-    if (mlp->rank < 1 || mlp->rank > 32) return fail(RIB_ERR_UNSUPPORTED, "rank=%d must be in 1..32", mlp->rank);
     const size_t lds = posgen_lds_bytes(*mlp);
     if (lds > 65536) return fail(RIB_ERR_UNSUPPORTED, "MLP too large for one LDS stage (%zu bytes)", lds);
-    if (!mlp->w1 || !mlp->w2) return fail(RIB_ERR_INVALID_ARG, "mlp weights are NULL");
     if (!q_p || !k_p) return fail(RIB_ERR_INVALID_ARG, "q_p / k_p is NULL");
-    if (((uintptr_t)mlp->w1 | (uintptr_t)mlp->w2 | (uintptr_t)mlp->b1 | (uintptr_t)mlp->b2) & 3u)
-      return fail(RIB_ERR_INVALID_ARG, "mlp weights must be 4-byte aligned");
     if (((uintptr_t)q_p | (uintptr_t)k_p) & (uintptr_t)(esize_of(out_dtype) - 1))
       return fail(RIB_ERR_INVALID_ARG, "q_p / k_p misaligned for their element type");
     TimedGroup tg(RIB_KERNEL_POSGEN, (hipStream_t)stream);
@@ -307,6 +311,36 @@ rib_status_t rib_posgen(int32_t w, const rib_mlp_t* mlp, rib_dtype_t out_dtype, 
     return ok();
   } catch (...) {
     return fail(RIB_ERR_HIP, "unexpected C++ exception in rib_posgen");
+  }
+}
+
+size_t rib_posgen_bwd_workspace_size(int32_t w, const rib_mlp_t* mlp) {
+  if (check_mlp(w, mlp) != RIB_OK) return 0;
+  return posgen_bwd_workspace_bytes(w, *mlp);
+}
+
+rib_status_t rib_posgen_bwd(int32_t w, const rib_mlp_t* mlp, const float* dq_p, const float* dk_p, float* dw1,
+                            float* db1, float* dw2, float* db2, void* workspace, size_t workspace_bytes,
+                            rib_stream_t stream) {
+  try {
+    RIB_TRY(check_mlp(w, mlp));
+    const size_t lds = posgen_bwd_lds_bytes(*mlp);
+    if (lds > 65536) return fail(RIB_ERR_UNSUPPORTED, "MLP too large for one LDS stage (%zu bytes)", lds);
+    if (!dq_p || !dk_p) return fail(RIB_ERR_INVALID_ARG, "dq_p / dk_p is NULL");
+    if (!dw1 || !dw2) return fail(RIB_ERR_INVALID_ARG, "dw1 / dw2 is NULL");
+    if (((uintptr_t)dq_p | (uintptr_t)dk_p | (uintptr_t)dw1 | (uintptr_t)db1 | (uintptr_t)dw2 | (uintptr_t)db2 |
+         (uintptr_t)workspace) & 3u)
+      return fail(RIB_ERR_INVALID_ARG, "float arguments must be 4-byte aligned");
+    const size_t need = posgen_bwd_workspace_bytes(w, *mlp);
+    if (!workspace || workspace_bytes < need)
+      return fail(RIB_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
+    TimedGroup tg(RIB_KERNEL_POSGEN_BWD, (hipStream_t)stream);
+    hipError_t e = launch_posgen_bwd(w, *mlp, dq_p, dk_p, dw1, db1, dw2, db2, workspace, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "posgen backward launch");
+    tg.end();
+    return ok();
+  } catch (...) {
+    return fail(RIB_ERR_HIP, "unexpected C++ exception in rib_posgen_bwd");
   }
 }
 

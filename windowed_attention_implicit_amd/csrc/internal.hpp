@@ -18,6 +18,13 @@ hipError_t launch_posgen(int w, const rib_mlp_t& mlp, rib_dtype_t out_dtype, voi
                          hipStream_t stream);
 // Dynamic LDS bytes the posgen kernel needs for this MLP.
 size_t posgen_lds_bytes(const rib_mlp_t& mlp);
+// Position-MLP weight gradients from dQ_p, dK_p (float32 [w*w, rank] each):
+// per-block partial sums into `workspace`, then a fixed-order reduction.
+hipError_t launch_posgen_bwd(int w, const rib_mlp_t& mlp, const float* dq_p, const float* dk_p, float* dw1,
+                             float* db1, float* dw2, float* db2, void* workspace, hipStream_t stream);
+// LDS bytes of the smallest (one-token) tile: the MLP is supported iff this fits 64 KB.
+size_t posgen_bwd_lds_bytes(const rib_mlp_t& mlp);
+size_t posgen_bwd_workspace_bytes(int w, const rib_mlp_t& mlp);
 
 // x [B,H,W,heads,d] -> windowed buffer in `layout` (rows >= N zero-filled).
 hipError_t launch_partition(const Geom& g, int esize, WinLayout layout, const void* x, void* xw,

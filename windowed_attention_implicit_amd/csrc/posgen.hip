@@ -17,6 +17,18 @@
 // broadcast. The phase 2^k * n / (w-1) is reduced exactly in integer
 // arithmetic (mod 2(w-1)) before sinpi/cospi, so the highest frequencies keep
 // full float32 accuracy. The output is tiny and computed once per window size.
+//
+// Backward (weight gradients): the MLP is trained with the network, so the
+// positional gradients dQ_p, dK_p continue by the chain rule through
+// Linear -> GELU -> Linear: with z = W1 phi + b1, h = GELU(z) and
+// d_out = [dQ_p | dK_p], dW2 = sum_t d_out h^T, db2 = sum_t d_out,
+// dz = (W2^T d_out) * GELU'(z) with GELU'(z) = Phi(z) + z phi(z), dW1 =
+// sum_t dz phi^T, db1 = sum_t dz. A block recomputes phi, z and h for tiles
+// of up to 32 tokens, keeps its partial sums in registers across its tiles
+// and writes them once; a second kernel adds the partials of all blocks in a
+// fixed order (deterministic, no atomics).
+#include <algorithm>
+
 #include "internal.hpp"
 
 namespace rib {
@@ -24,6 +36,24 @@ namespace {
 
 constexpr int kTokPerBlock = 16;
 constexpr int kThreads = 256;
+
+// Features k, F + k, 2F + k, 3F + k of token t (sin / cos of 2^k pi x, then of
+// 2^k pi y) into f[]. The phase (2^k n) mod 2(w-1) is reduced exactly in
+// integers (|2^k n| < 2^23 for w <= 256), so sinpi / cospi see an angle / pi
+// in [0, 2) with no rounding of large arguments.
+__device__ __forceinline__ void fourier_pair(int w, int n_freq, int t, int k, float* f) {
+  const int den = w - 1, mod = 2 * den;
+  const int iy = t / w, ix = t - iy * w;
+  const int nx = 2 * ix - den, ny = 2 * iy - den;
+  const int px = ((nx * (1 << k)) % mod + mod) % mod;
+  const int py = ((ny * (1 << k)) % mod + mod) % mod;
+  const float ax = (float)px / (float)den;
+  const float ay = (float)py / (float)den;
+  f[k] = sinpif(ax);
+  f[n_freq + k] = cospif(ax);
+  f[2 * n_freq + k] = sinpif(ay);
+  f[3 * n_freq + k] = cospif(ay);
+}
 
 template <typename OutT>
 __device__ __forceinline__ void store_out(OutT* p, float v);
@@ -60,24 +90,10 @@ __global__ __launch_bounds__(kThreads) void posgen_kernel(int w, int n_freq, int
 
   const int N = w * w;
   const int t0 = blockIdx.x * kTokPerBlock;
-  const int den = w - 1;
-  const int mod = 2 * den;
   // phase 1: features of (token, frequency) pairs
   for (int i = tid; i < kTokPerBlock * n_freq; i += kThreads) {
     const int tl = i / n_freq, k = i - tl * n_freq;
-    const int t = min(t0 + tl, N - 1);
-    const int iy = t / w, ix = t - iy * w;
-    const int nx = 2 * ix - den, ny = 2 * iy - den;
-    // exact phase: (2^k * n) mod 2(w-1), non-negative; |2^k n| < 2^23 for w <= 256
-    const int px = ((nx * (1 << k)) % mod + mod) % mod;
-    const int py = ((ny * (1 << k)) % mod + mod) % mod;
-    const float ax = (float)px / (float)den;  // angle / pi, in [0, 2)
-    const float ay = (float)py / (float)den;
-    float* f = sF + tl * nf;
-    f[k] = sinpif(ax);
-    f[n_freq + k] = cospif(ax);
-    f[2 * n_freq + k] = sinpif(ay);
-    f[3 * n_freq + k] = cospif(ay);
+    fourier_pair(w, n_freq, min(t0 + tl, N - 1), k, sF + tl * nf);
   }
   __syncthreads();
   // phase 2: hidden layer, GELU with the exact erf form
@@ -103,7 +119,197 @@ __global__ __launch_bounds__(kThreads) void posgen_kernel(int w, int n_freq, int
   }
 }
 
+// ------------------------------------------------------------ backward
+constexpr int kBwdMaxTok = 32;    // tokens per tile, at most (fewer when the MLP is large)
+constexpr int kBwdMaxBlocks = 1024;
+constexpr int kBwdThreads = 1024;   // 4 waves per SIMD to hide LDS latency
+
+__host__ __device__ inline int posgen_bwd_entries(int n_freq, int hidden, int rank) {
+  return hidden * 4 * n_freq + hidden + 2 * rank * hidden + 2 * rank;
+}
+
+// One block: stage W1^T, b1, W2; for every tile of `tok` tokens it owns
+// (tiles blockIdx.x, blockIdx.x + gridDim.x, ...) recompute phi, z, h and dz
+// in LDS and add the tile's contributions to the block's own partial slot,
+// laid out [dW1 hidden x 4F][db1 hidden][dW2 2r x hidden][db2 2r]. Every
+// entry of the slot belongs to one thread, so the read-modify-writes need no
+// synchronisation and their order is fixed.
+template <int TOK>
+__global__ __launch_bounds__(kBwdThreads) void posgen_bwd_partial_kernel(int w, int n_freq, int hidden, int rank,
+                                                                      const float* __restrict__ w1,
+                                                                      const float* __restrict__ b1,
+                                                                      const float* __restrict__ w2,
+                                                                      const float* __restrict__ dqp,
+                                                                      const float* __restrict__ dkp,
+                                                                      float* __restrict__ part) {
+  extern __shared__ float smem[];
+  constexpr int tok = TOK;
+  const int nf = 4 * n_freq;
+  const int nout = 2 * rank;
+  float* sW1t = smem;                        // [nf][hidden]   (transposed W1)
+  float* sB1 = sW1t + nf * hidden;           // [hidden]
+  float* sW2 = sB1 + hidden;                 // [nout][hidden]
+  float* sF = sW2 + nout * hidden;           // [tok][nf]      features
+  float* sH = sF + tok * nf;                 // [tok][hidden]  GELU(z)
+  float* sZ = sH + tok * hidden;             // [tok][hidden]  dz
+  float* sD = sZ + tok * hidden;             // [tok][nout]    d_out
+  const int tid = threadIdx.x;
+  for (int i = tid; i < hidden * nf; i += kBwdThreads) {
+    const int j = i / nf, f = i - j * nf;
+    sW1t[f * hidden + j] = w1[i];
+  }
+  for (int i = tid; i < hidden; i += kBwdThreads) sB1[i] = b1 ? b1[i] : 0.f;
+  for (int i = tid; i < nout * hidden; i += kBwdThreads) sW2[i] = w2[i];
+
+  const int N = w * w;
+  const int ntiles = (N + tok - 1) / tok;
+  const int per = posgen_bwd_entries(n_freq, hidden, rank);
+  const int n_w1 = hidden * nf, n_b1 = n_w1 + hidden, n_w2 = n_b1 + nout * hidden;
+  float* out = part + (int64_t)blockIdx.x * per;
+  const float kInvSqrt2 = 0.70710678118654752440f;
+  const float kInvSqrt2Pi = 0.39894228040143267794f;
+
+  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int t0 = tile * tok;
+    __syncthreads();   // the previous tile's LDS values are consumed (and the weights staged)
+    for (int i = tid; i < tok * n_freq; i += kBwdThreads) {
+      const int tl = i / n_freq, k = i - tl * n_freq;
+      fourier_pair(w, n_freq, min(t0 + tl, N - 1), k, sF + tl * nf);
+    }
+    // d_out = [dQ_p | dK_p]; tokens past N contribute zero
+    for (int i = tid; i < tok * nout; i += kBwdThreads) {
+      const int tl = i / nout, o = i - tl * nout;
+      const int t = t0 + tl;
+      float v = 0.f;
+      if (t < N) v = o < rank ? dqp[(int64_t)t * rank + o] : dkp[(int64_t)t * rank + (o - rank)];
+      sD[i] = v;
+    }
+    __syncthreads();
+    // z, h = GELU(z) = z Phi(z), dz = (W2^T d_out) * (Phi(z) + z phi(z))
+    for (int i = tid; i < tok * hidden; i += kBwdThreads) {
+      const int tl = i / hidden, j = i - tl * hidden;
+      const float* f = sF + tl * nf;
+      float z = sB1[j];
+#pragma unroll 8
+      for (int q = 0; q < nf; ++q) z = fmaf(sW1t[q * hidden + j], f[q], z);
+      const float cdf = 0.5f * (1.f + erff(z * kInvSqrt2));
+      const float pdf = kInvSqrt2Pi * expf(-0.5f * z * z);
+      const float* d = sD + tl * nout;
+      float dh = 0.f;
+#pragma unroll 8
+      for (int o = 0; o < nout; ++o) dh = fmaf(d[o], sW2[o * hidden + j], dh);
+      sH[i] = z * cdf;
+      sZ[i] = dh * fmaf(z, pdf, cdf);
+    }
+    __syncthreads();
+    const bool first = tile == (int)blockIdx.x;
+    for (int e = tid; e < per; e += kBwdThreads) {
+      float a = 0.f;
+      if (e < n_w1) {                       // dW1[j][f] += sum_t dz[t][j] phi[t][f]
+        const int j = e / nf, f = e - j * nf;
+#pragma unroll
+        for (int tl = 0; tl < tok; ++tl) a = fmaf(sZ[tl * hidden + j], sF[tl * nf + f], a);
+      } else if (e < n_b1) {                // db1[j] += sum_t dz[t][j]
+        const int j = e - n_w1;
+#pragma unroll
+        for (int tl = 0; tl < tok; ++tl) a += sZ[tl * hidden + j];
+      } else if (e < n_w2) {                // dW2[o][j] += sum_t d_out[t][o] h[t][j]
+        const int o = (e - n_b1) / hidden, j = (e - n_b1) - o * hidden;
+#pragma unroll
+        for (int tl = 0; tl < tok; ++tl) a = fmaf(sD[tl * nout + o], sH[tl * hidden + j], a);
+      } else {                              // db2[o] += sum_t d_out[t][o]
+        const int o = e - n_w2;
+#pragma unroll
+        for (int tl = 0; tl < tok; ++tl) a += sD[tl * nout + o];
+      }
+      out[e] = first ? a : out[e] + a;
+    }
+  }
+}
+
+// Sums the per-block partials entry by entry in block order and scatters them
+// to dW1, db1, dW2, db2 (db1 / db2 may be null).
+__global__ __launch_bounds__(kThreads) void posgen_bwd_reduce_kernel(int nblk, int hidden, int nf, int nout,
+                                                                     const float* __restrict__ part,
+                                                                     float* __restrict__ dw1, float* __restrict__ db1,
+                                                                     float* __restrict__ dw2, float* __restrict__ db2) {
+  const int per = hidden * nf + hidden + nout * hidden + nout;
+  const int e = blockIdx.x * kThreads + threadIdx.x;
+  if (e >= per) return;
+  // fixed left-to-right order; loads fetched 16 at a time so they overlap
+  float acc = 0.f;
+  int b = 0;
+  for (; b + 16 <= nblk; b += 16) {
+    float v[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = part[(int64_t)(b + i) * per + e];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc += v[i];
+  }
+  for (; b < nblk; ++b) acc += part[(int64_t)b * per + e];
+  int k = e;
+  if (k < hidden * nf) { dw1[k] = acc; return; }
+  k -= hidden * nf;
+  if (k < hidden) { if (db1) db1[k] = acc; return; }
+  k -= hidden;
+  if (k < nout * hidden) { dw2[k] = acc; return; }
+  k -= nout * hidden;
+  if (db2) db2[k] = acc;
+}
+
+size_t bwd_lds_for(const rib_mlp_t& mlp, int tok) {
+  const size_t nf = 4 * (size_t)mlp.n_freq, nout = 2 * (size_t)mlp.rank, hd = mlp.hidden;
+  return sizeof(float) * (nf * hd + hd + nout * hd + (size_t)tok * (nf + 2 * hd + nout));
+}
+
+// Tokens per tile: the largest power of two <= 32 whose tile fits 64 KB with
+// the weights, halved further (down to 1) while that leaves fewer than 128
+// tiles, so small windows still spread over many CUs (0: nothing fits).
+int bwd_tile_tokens(const rib_mlp_t& mlp, int w) {
+  int tok = kBwdMaxTok;
+  while (tok >= 1 && bwd_lds_for(mlp, tok) > 65536) tok /= 2;
+  while (tok > 1 && (w * w + tok - 1) / tok < 128) tok /= 2;
+  return tok;
+}
+
+int bwd_blocks(int w, int tok) { return std::min((w * w + tok - 1) / tok, kBwdMaxBlocks); }
+
 }  // namespace
+
+size_t posgen_bwd_lds_bytes(const rib_mlp_t& mlp) { return bwd_lds_for(mlp, 1); }
+
+size_t posgen_bwd_workspace_bytes(int w, const rib_mlp_t& mlp) {
+  const int tok = std::max(bwd_tile_tokens(mlp, w), 1);
+  return sizeof(float) * (size_t)bwd_blocks(w, tok) * posgen_bwd_entries(mlp.n_freq, mlp.hidden, mlp.rank);
+}
+
+hipError_t launch_posgen_bwd(int w, const rib_mlp_t& mlp, const float* dq_p, const float* dk_p, float* dw1,
+                             float* db1, float* dw2, float* db2, void* workspace, hipStream_t stream) {
+  const int tok = bwd_tile_tokens(mlp, w);
+  if (tok == 0) return hipErrorInvalidValue;
+  const int nblk = bwd_blocks(w, tok);
+  const int nf = 4 * mlp.n_freq, nout = 2 * mlp.rank;
+  float* part = (float*)workspace;
+  const size_t lds = bwd_lds_for(mlp, tok);
+#define RIB_PGB_LAUNCH(T)                                                                                     \
+  hipLaunchKernelGGL(posgen_bwd_partial_kernel<T>, dim3(nblk), dim3(kBwdThreads), lds, stream, w, mlp.n_freq,   \
+                     mlp.hidden, mlp.rank, mlp.w1, mlp.b1, mlp.w2, dq_p, dk_p, part)
+  switch (tok) {
+    case 32: RIB_PGB_LAUNCH(32); break;
+    case 16: RIB_PGB_LAUNCH(16); break;
+    case 8: RIB_PGB_LAUNCH(8); break;
+    case 4: RIB_PGB_LAUNCH(4); break;
+    case 2: RIB_PGB_LAUNCH(2); break;
+    default: RIB_PGB_LAUNCH(1); break;
+  }
+#undef RIB_PGB_LAUNCH
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int per = posgen_bwd_entries(mlp.n_freq, mlp.hidden, mlp.rank);
+  hipLaunchKernelGGL(posgen_bwd_reduce_kernel, dim3((per + kThreads - 1) / kThreads), dim3(kThreads), 0, stream,
+                     nblk, mlp.hidden, nf, nout, part, dw1, db1, dw2, db2);
+  return hipGetLastError();
+}
 
 size_t posgen_lds_bytes(const rib_mlp_t& mlp) {
   const size_t nf = 4 * (size_t)mlp.n_freq, nout = 2 * (size_t)mlp.rank, hd = mlp.hidden;
