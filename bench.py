@@ -100,18 +100,36 @@ def kernel_avg_ms(rib, group):
     return (ms / n if n else None), n
 
 
-def traffic_entry():
-    """HBM bytes per launch of the attention kernel from the committed counter run,
-    only while the kernel source is the one the counters were taken on."""
+def counter_record():
+    """The committed counter run of the attention kernel (HBM bytes per launch, the shader clock and
+    MFMA-busy fraction under counters), only while the kernel source is the one it was taken on."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
         sha = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
-        if rec.get("kernel_source_sha256") != sha:
-            return None
-        return rec["hbm_bytes_per_launch"]
-    except (OSError, KeyError, ValueError):
+        return rec if rec.get("kernel_source_sha256") == sha else None
+    except (OSError, ValueError):
         return None
+
+
+def step_distribution(fn, n: int, rib):
+    """Per-step times of n more steps, each bracketed by its own events (outside the timed region):
+    p10 / median / p90 of the step and of the attention kernel launch."""
+    import numpy as np
+    import torch
+    step, attn = [], []
+    rib.kernel_timing_read("attn_fwd")
+    for _ in range(n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        b.synchronize()
+        step.append(a.elapsed_time(b))
+        t, k = rib.kernel_timing_read("attn_fwd")
+        attn.append(t / k if k else float("nan"))
+    pct = lambda xs: {f"p{p}": round(float(np.percentile(xs, p)), 5) for p in (10, 50, 90)}
+    return {"steps": n, "step_ms": pct(step), "attn_kernel_ms": pct(attn)}
 
 
 def cpu_baseline(wl, x, n_units: int):
@@ -255,6 +273,7 @@ def main():
     part_ms, _ = kernel_avg_ms(rib, "partition")
     unp_ms, _ = kernel_avg_ms(rib, "unpartition")
     pg_ms, _ = kernel_avg_ms(rib, "posgen")
+    dist = step_distribution(step.run, max(50, args.steps), rib)
     rib.kernel_timing_enable(False)
     print(f"bench: step {ms:.4f} ms, attention kernel {attn_ms:.4f} ms over {attn_n} launches",
           file=sys.stderr, flush=True)
@@ -266,7 +285,9 @@ def main():
     part_bytes = 6 * tensor_bytes + 4 * wl.N * wl.r * 2          # read + write Q, K, V; pack Q_p, K_p
     unp_bytes = 2 * tensor_bytes
     pg_bytes = 4 * (wl.hidden * 4 * wl.n_freq + 2 * wl.r * wl.hidden) + 2 * wl.N * wl.r * 2
-    traffic = traffic_entry()
+    rec = counter_record()
+    traffic = rec and rec.get("hbm_bytes_per_launch")
+    sclk = rec and rec.get("sclk_ghz_under_counters")
 
     result = {
         "metric": METRIC,
@@ -290,7 +311,13 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                      "kernel": "attn_fwd_bf16_kernel", "flops_per_launch": flops,
-                     "avg_launch_ms": round(attn_ms, 5)},
+                     "avg_launch_ms": round(attn_ms, 5),
+                     # 4096 bf16 flop/clk/CU x 256 CUs at the shader clock the kernel ran at under counters
+                     "sclk_ghz_under_counters": sclk,
+                     "peak_at_that_clock": sclk and round(4.096 * 256 * sclk, 1),
+                     "frac_at_that_clock": sclk and round(attn_tflops / (4.096 * 256 * sclk), 4),
+                     "mfma_busy_under_counters": rec and rec.get("mfma_busy_frac")},
+        "distribution": dist,
         "kernels": {
             "posgen": {"ms": pg_ms and round(pg_ms, 5), "GB/s": pg_ms and round(pg_bytes / pg_ms / 1e6, 1)},
             "partition": {"ms": round(part_ms, 5), "GB/s": round(part_bytes / part_ms / 1e6, 1),
