@@ -164,7 +164,9 @@ def test_workspace_is_linear_not_quadratic(L):
         return fn(ctypes.byref(rib.Shape(B, H, H, 6, 32, w, 16)), rib.RIB_BF16)
     for fn in (L.rib_fwd_workspace_size, L.rib_bwd_workspace_size):
         small, big = ws(2, 192, 16, fn), ws(2, 192, 96, fn)
-        assert abs(big - small) <= 0.01 * small            # same map, 36x larger windows
+        # same map, 36x larger windows: only the per-window-size parts (positional tokens, their
+        # transposes and per-unit partials, a few MB at w = 96) differ
+        assert abs(big - small) <= 0.03 * small + (4 << 20)
         assert ws(4, 192, 96, fn) <= 2 * ws(2, 192, 96, fn) + 4096
         N = 96 * 96
         assert big < 2 * 6 * N * N                          # far below one N x N matrix per unit

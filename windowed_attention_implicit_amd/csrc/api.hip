@@ -105,10 +105,12 @@ FwdLayout fwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
   const size_t pos = (size_t)g.n_rows * padded_rank(g.r) * es;
   Carve c(ws);
   FwdLayout L;
-  L.qw = c.take(t);
+  // the bf16 kernel reads Q_c and writes O in the map layout directly
+  const bool rows_qo = dt != RIB_BF16;
+  L.qw = rows_qo ? c.take(t) : nullptr;
   L.kw = c.take(t);
   L.vw = c.take(t);
-  L.ow = c.take(t);
+  L.ow = rows_qo ? c.take(t) : nullptr;
   L.qp = c.take(pos);
   L.kp = c.take(pos);
   L.kmax2 = (float*)c.take((size_t)g.units * key_bound_parts(g.N) * sizeof(float));
@@ -409,8 +411,10 @@ rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
     const int es = esize_of(dtype);
     const int rp = padded_rank(g.r);
     hipError_t e;
+    const bool bf = dtype == RIB_BF16;
     TimedGroup t_part(RIB_KERNEL_PARTITION, st);
-    if ((e = launch_partition(g, es, WinLayout::kRows, q_c, L.qw, st)) != hipSuccess) return hip_fail(e, "partition q");
+    if (!bf && (e = launch_partition(g, es, WinLayout::kRows, q_c, L.qw, st)) != hipSuccess)
+      return hip_fail(e, "partition q");
     if ((e = launch_partition(g, es, WinLayout::kRows, k_c, L.kw, st)) != hipSuccess) return hip_fail(e, "partition k");
     if ((e = launch_partition(g, es, dtype == RIB_BF16 ? WinLayout::kTransKappa : WinLayout::kRows, v, L.vw, st)) !=
         hipSuccess)
@@ -421,6 +425,7 @@ rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
     a.g = g;
     a.c = resolve_scale(scale, shape) * kLog2e;
     a.qw = L.qw; a.kw = L.kw; a.vw = L.vw; a.qp = L.qp; a.kp = L.kp; a.ow = L.ow;
+    a.q_map = q_c; a.o_map = o;
     a.lse = lse;
     a.kmax2 = L.kmax2;
     a.rp = rp;
@@ -430,9 +435,11 @@ rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
     e = dtype == RIB_BF16 ? launch_attn_fwd_bf16(a, st) : launch_attn_fwd_f32(a, st);
     if (e != hipSuccess) return hip_fail(e, "attention forward");
     t_attn.end();
-    TimedGroup t_unp(RIB_KERNEL_UNPARTITION, st);
-    if ((e = launch_unpartition(g, es, L.ow, o, st)) != hipSuccess) return hip_fail(e, "unpartition o");
-    t_unp.end();
+    if (!bf) {
+      TimedGroup t_unp(RIB_KERNEL_UNPARTITION, st);
+      if ((e = launch_unpartition(g, es, L.ow, o, st)) != hipSuccess) return hip_fail(e, "unpartition o");
+      t_unp.end();
+    }
     return ok();
   } catch (...) {
     return fail(RIB_ERR_HIP, "unexpected C++ exception in rib_window_attn_fwd");

@@ -124,7 +124,14 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const int half = lane >> 5, l32 = lane & 31;
   const int rp = 16 * KP;
 
-  const bf16* qw = (const bf16*)a.qw + (int64_t)unit * n_rows * 32;
+  // Q_c rows are read and O rows written straight in the [B, H, W, heads, d_c]
+  // map: the window addressing is folded into these once-per-wave accesses
+  // (row of token t = window base + (t / w) * W * heads + (t % w) * heads).
+  const PixelMap pm = make_pixel_map(g);
+  const int64_t map_base = pm.pixel_head(unit, 0) * 32;
+  const int64_t row_elems = (int64_t)g.W * g.heads * 32, pix_elems = (int64_t)g.heads * 32;
+  auto map_row = [&](int t) { return map_base + (int64_t)(t / g.w) * row_elems + (int64_t)(t % g.w) * pix_elems; };
+  const bf16* qmap = (const bf16*)a.q_map;
   const bf16* kw = (const bf16*)a.kw + (int64_t)unit * n_rows * 32;
   const bf16* vt = (const bf16*)a.vw + (int64_t)unit * 32 * n_rows;
   const bf16* qp = (const bf16*)a.qp;
@@ -152,7 +159,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     for (int s = 0; s < C::kSteps; ++s) {
       u32x4 v = u32x4(0u);
       if (ok) {
-        if (s < 2) v = *(const u32x4*)(qw + (int64_t)q * 32 + s * 16 + half * 8);
+        if (s < 2) v = *(const u32x4*)(qmap + map_row(q) + s * 16 + half * 8);
         else v = *(const u32x4*)(qp + (int64_t)q * rp + (s - 2) * 16 + half * 8);
       }
       const bf16x8 raw = __builtin_bit_cast(bf16x8, v);
@@ -475,9 +482,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     }
   }
 
-  // ---- epilogue: normalize, write O rows and LSE
-  bf16* ow = (bf16*)a.ow + (int64_t)unit * n_rows * 32;
-  PixelMap pm = make_pixel_map(g);
+  // ---- epilogue: normalize, write O rows (map layout) and LSE
+  bf16* omap = (bf16*)a.o_map;
   const float kLn2 = 0.69314718055994530942f;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
@@ -490,7 +496,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
         bf16 o4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) o4[i] = f32_to_bf16(acc[nb][4 * gq + i] * inv);
-        *(uint2*)(ow + (int64_t)q * 32 + 8 * gq + 4 * half) = *(const uint2*)o4;
+        *(uint2*)(omap + map_row(q) + 8 * gq + 4 * half) = *(const uint2*)o4;
       }
       if (a.lse && half == 0) a.lse[pm.pixel_head(unit, q)] = (m_run[nb] + log2f(l_tot)) * kLn2;
     }

@@ -45,12 +45,14 @@ hipError_t launch_pos_transpose(int n_rows, int rp, const void* in, void* out, h
 struct FwdArgs {
   Geom g;
   float c;              // scale * log2(e)
-  const void* qw;       // [units][n_rows][32]
+  const void* qw;       // [units][n_rows][32] (f32 path)
+  const void* q_map;    // bf16 path: Q_c in the [B, H, W, heads, 32] map
   const void* kw;       // [units][n_rows][32]
   const void* vw;       // bf16: [units][32][n_rows] kappa layout; f32: [units][n_rows][32]
   const void* qp;       // [n_rows][rp]
   const void* kp;       // [n_rows][rp]
-  void* ow;             // [units][n_rows][32]
+  void* ow;             // [units][n_rows][32] (f32 path)
+  void* o_map;          // bf16 path: O in the [B, H, W, heads, 32] map
   float* lse;           // [B,H,W,heads] or nullptr
   float* kmax2;         // [units][key_bound_parts(N)] partial maxima of |[k_c | k_p]|^2 (bf16 path)
   int rp;               // padded rank, 16 or 32
