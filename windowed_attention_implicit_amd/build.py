@@ -29,6 +29,14 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]
+# Per-file extra flags. The backward kernels keep more live state than 256
+# arch VGPRs; left to its heuristics the compiler then gives the score / dP
+# MFMAs the AGPR form and copies every result back to VGPRs for the exp and
+# the products (hundreds of v_accvgpr moves per tile). The VGPR form keeps the
+# MFMA results where the vector code reads them.
+FILE_FLAGS = {
+    "attn_bwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def _hipcc() -> str:
@@ -40,7 +48,7 @@ def _hipcc() -> str:
 
 def _compile(hipcc: str, src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc, *COMMON_FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     proc = subprocess.run(cmd, capture_output=True, text=True)
     msgs = "\n".join(l for l in (proc.stdout + proc.stderr).splitlines() if "packed-fp32-ops" not in l)
     if proc.returncode != 0:

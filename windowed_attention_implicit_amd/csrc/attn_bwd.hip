@@ -18,9 +18,15 @@
 //    K_hat^T (kappa) and accumulates dQ_hat^T += K_hat^T dS^T with one query
 //    per lane, like the forward.
 //  * The register-resident score operand (K in dkv, Q in dq) is pre-scaled by
-//    scale * log2(e), and -LSE2 / -D enter as the accumulator inputs of the
-//    score / dP MFMAs, so P = exp2(acc) and dS = P * acc: per score one exp2,
-//    one multiply and the bf16 packs, no other vector work.
+//    scale * log2(e). In dkv (one key per lane, queries along the accumulator
+//    rows) -LSE2 / -D enter as the accumulator inputs of the score / dP MFMAs,
+//    so P = exp2(acc) and dS = P * acc: per score one exp2, one multiply and
+//    the bf16 packs. In dq (one query per lane) they are lane constants and
+//    are added with one vector add each: as accumulator inputs they would need
+//    64 registers the kernel does not have.
+//  * Both kernels are compiled with the VGPR form of the MFMAs (build flag):
+//    their state exceeds 256 arch VGPRs, and the AGPR form the compiler would
+//    otherwise pick costs a register copy per score.
 //  * Positional-gradient partials are written per unit in float32 and summed
 //    over units in a fixed order by a separate reduction.
 #include "internal.hpp"
@@ -292,12 +298,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     l2q[nb] = ok ? a.lse2[ub + q] : INFINITY;
     dq_d[nb] = ok ? a.dd[ub + q] : 0.f;
   }
-  // accumulator inputs: -LSE2 for the score MFMA, -D for the dP MFMA (one query per lane)
-  f32x16 nlq[2], ndq[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) { nlq[nb][i] = -l2q[nb]; ndq[nb][i] = -dq_d[nb]; }
 
   f32x16 acc_dq[2], acc_dqp[2];
 #pragma unroll
@@ -351,18 +351,21 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
       }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[nb][0], nlq[nb], 0, 0, 0);
+        // one query per lane: -LSE2 and -D are lane constants, added by one vector add each
+        // (as accumulator inputs they would take 64 more registers than the kernel has)
+        f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[nb][0], f32x16(0.f), 0, 0, 0);
 #pragma unroll
         for (int s = 1; s < C::kSteps; ++s) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[nb][s], sc, 0, 0, 0);
-        f32x16 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], df[nb][0], ndq[nb], 0, 0, 0);
+        f32x16 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], df[nb][0], f32x16(0.f), 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1], df[nb][1], dp, 0, 0, 0);
+        const float nl = -l2q[nb], nd = -dq_d[nb];
         bf16x8 sb[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int v = 8 * s + j;
-            sb[s][j] = f32_to_bf16(__builtin_amdgcn_exp2f(sc[v]) * dp[v]);
+            sb[s][j] = f32_to_bf16(__builtin_amdgcn_exp2f(sc[v] + nl) * (dp[v] + nd));
           }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
