@@ -30,6 +30,7 @@
 //  * Positional-gradient partials are written per unit in float32 and summed
 //    over units in a fixed order by a separate reduction.
 #include "internal.hpp"
+#include "tile_dma.hpp"
 
 namespace rib {
 namespace {
@@ -42,12 +43,42 @@ constexpr int kPerBlock = 256;     // owned keys (dkv) / queries (dq) per workgr
 template <int KP>
 struct BwdCfg {
   static constexpr int kSteps = 2 + KP;           // 16-channel steps of [content | pos]
-  static constexpr int kRowC = 2 * kSteps + 1;    // chunks per Q_hat / K_hat row (+1 pad)
-  static constexpr int kDRow = 5;                 // chunks per dO / V row (4 + 1 pad)
+  static constexpr int kCRow = 5;                 // chunks per content / dO / V row in LDS (4 + 1 pad)
+  static constexpr int kPRow = 2 * KP + 1;        // chunks per positional row (2KP + 1 pad)
   static constexpr int kTRow = kTile / 8 + 1;     // chunks per transposed row (8 + 1 pad)
   static constexpr int kPosRows = 16 * KP;
-  static constexpr int kTRows = 32 + kPosRows;    // rows of a transposed [content | pos] tile
 };
+
+// LDS tile layouts (parts in DMA order). dkv streams query tiles: Q_hat
+// content and positional rows, dO rows, the channel-major kappa copies of
+// Q_hat (content, positional) and dO, and the tile's -LSE2 and -D.
+template <int KP>
+struct DkvTile {
+  static constexpr TileLayout<8> get() {
+    return {{{kTile, 4, 5}, {kTile, 2 * KP, 2 * KP + 1}, {kTile, 4, 5}, {32, 8, kTile / 8 + 1},
+             {16 * KP, 8, kTile / 8 + 1}, {32, 8, kTile / 8 + 1}, {1, 16, 16}, {1, 16, 16}}};
+  }
+};
+// dq streams key tiles: K_hat content and positional rows, V rows and the
+// channel-major kappa copies of K_hat (content, positional).
+template <int KP>
+struct DqTile {
+  static constexpr TileLayout<5> get() {
+    return {{{kTile, 4, 5}, {kTile, 2 * KP, 2 * KP + 1}, {kTile, 4, 5}, {32, 8, kTile / 8 + 1},
+             {16 * KP, 8, kTile / 8 + 1}}};
+  }
+};
+// LDS tile rings. dkv (one workgroup per CU by registers) fetches tile t + 3
+// while processing tile t; dq fits two workgroups per CU, which a 3-deep ring
+// (tile t + 2 in flight) keeps within the 160 KB of LDS.
+constexpr int kBufsDkv = 4;
+constexpr int kBufsDq = 3;
+
+// Workgroup barrier without the release fence of __syncthreads, which would
+// wait for every tile DMA in flight. Callers wait for the DMA they depend on
+// first; the waves write no LDS in the main loops. The memory clobber keeps
+// the compiler from moving LDS reads or DMA issue across it.
+__device__ __forceinline__ void barrier_dma() { asm volatile("s_barrier" ::: "memory"); }
 
 __device__ __forceinline__ bf16x8 lds_frag(const u32x4* p) { return __builtin_bit_cast(bf16x8, *p); }
 
@@ -76,12 +107,11 @@ __device__ __forceinline__ bf16x8 token_frag(const bf16* content, const bf16* po
 template <int KP>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   typedef BwdCfg<KP> C;
-  __shared__ u32x4 sQ[2][kTile * C::kRowC];
-  __shared__ u32x4 sDo[2][kTile * C::kDRow];
-  __shared__ u32x4 sQt[2][C::kTRows * C::kTRow];
-  __shared__ u32x4 sDot[2][32 * C::kTRow];
-  __shared__ float sL[2][kTile];
-  __shared__ float sD[2][kTile];
+  typedef DkvTile<KP> LP;
+  constexpr auto L = LP::get();
+  constexpr int oQc = L.offset(0), oQp = L.offset(1), oDo = L.offset(2), oQt = L.offset(3), oQpt = L.offset(4),
+                oDot = L.offset(5), oL = L.offset(6), oD = L.offset(7);
+  __shared__ u32x4 sT[kBufsDkv][L.chunks()];
 
   const Geom& g = a.g;
   const int N = g.N, n_rows = g.n_rows;
@@ -89,7 +119,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   const int logical = xcd_remap(blockIdx.x, g.units * nkb);
   const int unit = logical / nkb;
   const int kb = logical - unit * nkb;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int rp = 16 * KP;
 
   const int64_t ub = (int64_t)unit * n_rows;
@@ -127,61 +158,44 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) { acc_dv[nb][i] = 0.f; acc_dk[nb][i] = 0.f; acc_dkp[nb][i] = 0.f; }
 
-  // tile loader (per thread: one chunk of each tile part, pos parts on the first 128*KP threads)
-  const int r_tok = tid >> 2, r_ch = tid & 3;             // row tiles: 64 tokens x 4 chunks
-  const int p_tok = tid / (2 * KP), p_ch = tid % (2 * KP);// pos rows: 64 tokens x 2KP chunks
-  const bool p_on = tid < kTile * 2 * KP;
-  const int t_row = tid >> 3, t_ch = tid & 7;             // transposed tiles: 32 rows x 8 chunks
-  const int tp_row = tid >> 3;                            // pos transposed: rp rows x 8 chunks
-  u32x4 lq, lqp, ldo, lqt, lqpt, ldot;
-  float lfl = 0.f;
-  auto load_tile = [&](int t) {
-    const int q0 = t * kTile;
-    lq = *(const u32x4*)(qw + (int64_t)(q0 + r_tok) * 32 + r_ch * 8);
-    if (p_on) lqp = *(const u32x4*)(qp + (int64_t)(q0 + p_tok) * rp + p_ch * 8);
-    ldo = *(const u32x4*)(dow + (int64_t)(q0 + r_tok) * 32 + r_ch * 8);
-    lqt = *(const u32x4*)(qt + (int64_t)t_row * n_rows + q0 + t_ch * 8);
-    if (p_on) lqpt = *(const u32x4*)(qpt + (int64_t)tp_row * n_rows + q0 + t_ch * 8);
-    ldot = *(const u32x4*)(dot + (int64_t)t_row * n_rows + q0 + t_ch * 8);
-    if (tid < kTile) lfl = -lse2[q0 + tid];             // stored negated: MFMA accumulator inputs
-    else if (tid < 2 * kTile) lfl = -dd[q0 + tid - kTile];
+  // query tiles reach LDS by DMA (buffer_load ... lds), three tiles ahead
+  const int row64 = n_rows * 64, nb2 = n_rows * 2, pos_bytes = n_rows * rp * 2;
+  const DmaSrc src[8] = {
+      {qw, row64, 64, kTile * 64},        {qp, pos_bytes, rp * 2, kTile * rp * 2}, {dow, row64, 64, kTile * 64},
+      {qt, row64, nb2, kTile * 2},        {qpt, pos_bytes, nb2, kTile * 2},        {dot, row64, nb2, kTile * 2},
+      {lse2, n_rows * 4, 256, kTile * 4}, {dd, n_rows * 4, 256, kTile * 4},
   };
-  auto store_tile = [&](int buf) {
-    sQ[buf][r_tok * C::kRowC + r_ch] = lq;
-    if (p_on) sQ[buf][p_tok * C::kRowC + 4 + p_ch] = lqp;
-    sDo[buf][r_tok * C::kDRow + r_ch] = ldo;
-    sQt[buf][t_row * C::kTRow + t_ch] = lqt;
-    if (p_on) sQt[buf][(32 + tp_row) * C::kTRow + t_ch] = lqpt;
-    sDot[buf][t_row * C::kTRow + t_ch] = ldot;
-    if (tid < kTile) sL[buf][tid] = lfl;
-    else if (tid < 2 * kTile) sD[buf][tid - kTile] = lfl;
-  };
+  TileDma<L.kParts, L.slots()> dma;
+  tile_dma_init<LP>(dma, src, wave, lane);
 
   const float c = a.c;
   const int nqt = (N + kTile - 1) / kTile;
-  load_tile(0);
-  store_tile(0);
+  tile_dma_issue<LP>(dma, wave, 0, sT[0]);
+  tile_dma_issue<LP>(dma, wave, min(1, nqt - 1), sT[1]);
+  tile_dma_issue<LP>(dma, wave, min(2, nqt - 1), sT[2]);
+  tile_dma_wait<LP, 2>(wave);
   __syncthreads();
   for (int t = 0; t < nqt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nqt) load_tile(t + 1);
+    // tile t + 3 (the last tile again past the end) into the buffer tile t - 1 used
+    tile_dma_issue<LP>(dma, wave, min(t + 3, nqt - 1), sT[(t + 3) % kBufsDkv]);
+    const u32x4* T = sT[t % kBufsDkv];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
+      const int row = sub * 32 + l32;
       bf16x8 qa[C::kSteps], da[2];
 #pragma unroll
-      for (int s = 0; s < C::kSteps; ++s) {
-        const int ch = s < 2 ? 2 * s + half : 4 + 2 * (s - 2) + half;
-        qa[s] = lds_frag(&sQ[buf][(sub * 32 + l32) * C::kRowC + ch]);
-      }
+      for (int s = 0; s < C::kSteps; ++s)
+        qa[s] = s < 2 ? lds_frag(&T[oQc + row * C::kCRow + 2 * s + half])
+                      : lds_frag(&T[oQp + row * C::kPRow + 2 * (s - 2) + half]);
 #pragma unroll
-      for (int s = 0; s < 2; ++s) da[s] = lds_frag(&sDo[buf][(sub * 32 + l32) * C::kDRow + 2 * s + half]);
+      for (int s = 0; s < 2; ++s) da[s] = lds_frag(&T[oDo + row * C::kCRow + 2 * s + half]);
       // -LSE2 and -D of the lane's 16 accumulator rows (queries 8(v/4) + 4h + v%4)
       f32x16 nl, nd;
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int qi = sub * 32 + 8 * gq + 4 * half;
-        const f32x4 l4 = *(const f32x4*)&sL[buf][qi];
-        const f32x4 d4 = *(const f32x4*)&sD[buf][qi];
+        const f32x4 l4 = __builtin_bit_cast(f32x4, T[oL + qi / 4]);
+        const f32x4 d4 = __builtin_bit_cast(f32x4, T[oD + qi / 4]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) { nl[4 * gq + i] = l4[i]; nd[4 * gq + i] = d4[i]; }
       }
@@ -189,9 +203,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const int ch = 4 * sub + 2 * s + half;
-        dta[s] = lds_frag(&sDot[buf][l32 * C::kTRow + ch]);
-        qta[s] = lds_frag(&sQt[buf][l32 * C::kTRow + ch]);
-        qpta[s] = l32 < C::kPosRows ? lds_frag(&sQt[buf][(32 + l32) * C::kTRow + ch]) : zero_frag();
+        dta[s] = lds_frag(&T[oDot + l32 * C::kTRow + ch]);
+        qta[s] = lds_frag(&T[oQt + l32 * C::kTRow + ch]);
+        qpta[s] = l32 < C::kPosRows ? lds_frag(&T[oQpt + l32 * C::kTRow + ch]) : zero_frag();
       }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
@@ -219,8 +233,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
         }
       }
     }
-    if (t + 1 < nqt) store_tile(buf ^ 1);
-    __syncthreads();
+    tile_dma_wait<LP, 2>(wave);   // tile t + 1 landed (this wave's part); t + 2, t + 3 may be in flight
+    barrier_dma();
   }
 
   // epilogue: lane = key, accumulator rows = channels 8(v/4) + 4h + v%4
@@ -257,9 +271,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
 template <int KP>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   typedef BwdCfg<KP> C;
-  __shared__ u32x4 sK[2][kTile * C::kRowC];
-  __shared__ u32x4 sV[2][kTile * C::kDRow];
-  __shared__ u32x4 sKt[2][C::kTRows * C::kTRow];
+  typedef DqTile<KP> LP;
+  constexpr auto L = LP::get();
+  constexpr int oKc = L.offset(0), oKp = L.offset(1), oV = L.offset(2), oKt = L.offset(3), oKpt = L.offset(4);
+  __shared__ u32x4 sT[kBufsDq][L.chunks()];
 
   const Geom& g = a.g;
   const int N = g.N, n_rows = g.n_rows;
@@ -267,7 +282,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   const int logical = xcd_remap(blockIdx.x, g.units * nqb);
   const int unit = logical / nqb;
   const int qb = logical - unit * nqb;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, l32 = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   constexpr int rp = 16 * KP;
 
   const int64_t ub = (int64_t)unit * n_rows;
@@ -283,7 +299,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   // owned queries: B operands of S^T = K_hat Q_hat^T and dP^T = V dO^T
   const int q0 = qb * kPerBlock + wave * 64;
   bf16x8 qf[2][C::kSteps], df[2][2];
-  float l2q[2], dq_d[2];
+  float nlq[2], ndq[2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int q = q0 + nb * 32 + l32;
@@ -295,8 +311,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     for (int s = 0; s < 2; ++s)
       df[nb][s] = ok ? __builtin_bit_cast(bf16x8, *(const u32x4*)(dow + (int64_t)q * 32 + s * 16 + half * 8))
                      : zero_frag();
-    l2q[nb] = ok ? a.lse2[ub + q] : INFINITY;
-    dq_d[nb] = ok ? a.dd[ub + q] : 0.f;
+    nlq[nb] = ok ? a.lse2[ub + q] : -INFINITY;   // stored negated: -LSE2, -D
+    ndq[nb] = ok ? a.dd[ub + q] : 0.f;
   }
 
   f32x16 acc_dq[2], acc_dqp[2];
@@ -305,49 +321,39 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) { acc_dq[nb][i] = 0.f; acc_dqp[nb][i] = 0.f; }
 
-  const int r_tok = tid >> 2, r_ch = tid & 3;
-  const int p_tok = tid / (2 * KP), p_ch = tid % (2 * KP);
-  const bool p_on = tid < kTile * 2 * KP;
-  const int t_row = tid >> 3, t_ch = tid & 7;
-  u32x4 lk, lkp, lv, lkt, lkpt;
-  auto load_tile = [&](int t) {
-    const int k0 = t * kTile;
-    lk = *(const u32x4*)(kw + (int64_t)(k0 + r_tok) * 32 + r_ch * 8);
-    if (p_on) lkp = *(const u32x4*)(kp + (int64_t)(k0 + p_tok) * rp + p_ch * 8);
-    lv = *(const u32x4*)(vw + (int64_t)(k0 + r_tok) * 32 + r_ch * 8);
-    lkt = *(const u32x4*)(kt + (int64_t)t_row * n_rows + k0 + t_ch * 8);
-    if (p_on) lkpt = *(const u32x4*)(kpt + (int64_t)t_row * n_rows + k0 + t_ch * 8);
+  // key tiles reach LDS by DMA (buffer_load ... lds), two tiles ahead
+  const int row64 = n_rows * 64, nb2 = n_rows * 2, pos_bytes = n_rows * rp * 2;
+  const DmaSrc src[5] = {
+      {kw, row64, 64, kTile * 64}, {kp, pos_bytes, rp * 2, kTile * rp * 2}, {vw, row64, 64, kTile * 64},
+      {kt, row64, nb2, kTile * 2}, {kpt, pos_bytes, nb2, kTile * 2},
   };
-  auto store_tile = [&](int buf) {
-    sK[buf][r_tok * C::kRowC + r_ch] = lk;
-    if (p_on) sK[buf][p_tok * C::kRowC + 4 + p_ch] = lkp;
-    sV[buf][r_tok * C::kDRow + r_ch] = lv;
-    sKt[buf][t_row * C::kTRow + t_ch] = lkt;
-    if (p_on) sKt[buf][(32 + t_row) * C::kTRow + t_ch] = lkpt;
-  };
+  TileDma<L.kParts, L.slots()> dma;
+  tile_dma_init<LP>(dma, src, wave, lane);
 
   const float c = a.c;
   const int nkt = (N + kTile - 1) / kTile;
-  load_tile(0);
-  store_tile(0);
+  tile_dma_issue<LP>(dma, wave, 0, sT[0]);
+  tile_dma_issue<LP>(dma, wave, min(1, nkt - 1), sT[1]);
+  tile_dma_wait<LP, 1>(wave);
   __syncthreads();
   for (int t = 0; t < nkt; ++t) {
-    const int buf = t & 1;
-    if (t + 1 < nkt) load_tile(t + 1);
+    // tile t + 2 (the last tile again past the end) into the buffer tile t - 1 used
+    tile_dma_issue<LP>(dma, wave, min(t + 2, nkt - 1), sT[(t + 2) % kBufsDq]);
+    const u32x4* T = sT[t % kBufsDq];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
+      const int row = sub * 32 + l32;
       bf16x8 ka[C::kSteps], va[2], kta[2], kpta[2];
 #pragma unroll
-      for (int s = 0; s < C::kSteps; ++s) {
-        const int ch = s < 2 ? 2 * s + half : 4 + 2 * (s - 2) + half;
-        ka[s] = lds_frag(&sK[buf][(sub * 32 + l32) * C::kRowC + ch]);
-      }
+      for (int s = 0; s < C::kSteps; ++s)
+        ka[s] = s < 2 ? lds_frag(&T[oKc + row * C::kCRow + 2 * s + half])
+                      : lds_frag(&T[oKp + row * C::kPRow + 2 * (s - 2) + half]);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        va[s] = lds_frag(&sV[buf][(sub * 32 + l32) * C::kDRow + 2 * s + half]);
+        va[s] = lds_frag(&T[oV + row * C::kCRow + 2 * s + half]);
         const int ch = 4 * sub + 2 * s + half;
-        kta[s] = lds_frag(&sKt[buf][l32 * C::kTRow + ch]);
-        kpta[s] = l32 < C::kPosRows ? lds_frag(&sKt[buf][(32 + l32) * C::kTRow + ch]) : zero_frag();
+        kta[s] = lds_frag(&T[oKt + l32 * C::kTRow + ch]);
+        kpta[s] = l32 < C::kPosRows ? lds_frag(&T[oKpt + l32 * C::kTRow + ch]) : zero_frag();
       }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
@@ -358,14 +364,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
         for (int s = 1; s < C::kSteps; ++s) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[nb][s], sc, 0, 0, 0);
         f32x16 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], df[nb][0], f32x16(0.f), 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1], df[nb][1], dp, 0, 0, 0);
-        const float nl = -l2q[nb], nd = -dq_d[nb];
         bf16x8 sb[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int v = 8 * s + j;
-            sb[s][j] = f32_to_bf16(__builtin_amdgcn_exp2f(sc[v] + nl) * (dp[v] + nd));
+            sb[s][j] = f32_to_bf16(__builtin_amdgcn_exp2f(sc[v] + nlq[nb]) * (dp[v] + ndq[nb]));
           }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
@@ -374,8 +379,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
         }
       }
     }
-    if (t + 1 < nkt) store_tile(buf ^ 1);
-    __syncthreads();
+    tile_dma_wait<LP, 1>(wave);   // tile t + 1 landed (this wave's part); t + 2 may be in flight
+    barrier_dma();
   }
 
   bf16* dqw = (bf16*)a.dqw + ub * 32;
@@ -403,6 +408,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ prep
+// D_i = sum_c dO_ic O_ic and LSE2_i = LSE_i * log2(e) per window row. For the
+// bf16 kernels they are stored negated (-D, -LSE2: what those kernels add,
+// and the accumulator inputs the dkv kernel takes from LDS as they are); the
+// float32 kernels read them unnegated.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, PixelMap pm, const T* __restrict__ o,
                                                        const T* __restrict__ d_o, const float* __restrict__ lse,
@@ -412,9 +421,10 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, PixelMap pm, cons
   if (i >= total) return;
   const int unit = (int)(i / g.n_rows);
   const int t = (int)(i - (int64_t)unit * g.n_rows);
+  constexpr float sgn = sizeof(T) == 2 ? -1.f : 1.f;
   if (t >= g.N) {
     dd[i] = 0.f;
-    lse2[i] = INFINITY;
+    lse2[i] = sgn * INFINITY;   // P = 0 for padded rows
     return;
   }
   const int64_t ph = pm.pixel_head(unit, t);
@@ -423,8 +433,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, PixelMap pm, cons
   float acc = 0.f;
 #pragma unroll
   for (int ch = 0; ch < 32; ++ch) acc = fmaf((float)orow[ch], (float)grow[ch], acc);
-  dd[i] = acc;
-  lse2[i] = lse[ph] * 1.44269504088896340736f;
+  dd[i] = sgn * acc;
+  lse2[i] = sgn * (lse[ph] * 1.44269504088896340736f);
 }
 
 // ------------------------------------------------------------------ float32
