@@ -145,9 +145,10 @@ BwdLayout bwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
   L.kp = c.take(pos);
   L.qpt = bf ? c.take(pos) : nullptr;
   L.kpt = bf ? c.take(pos) : nullptr;
-  L.dqw = c.take(t);
-  L.dkw = c.take(t);
-  L.dvw = c.take(t);
+  // the bf16 kernels write dQ_c, dK_c, dV in the map layout directly
+  L.dqw = bf ? nullptr : c.take(t);
+  L.dkw = bf ? nullptr : c.take(t);
+  L.dvw = bf ? nullptr : c.take(t);
   L.lse2 = (float*)c.take(rowf);
   L.dd = (float*)c.take(rowf);
   L.dqp_part = (float*)c.take(part);
@@ -520,6 +521,7 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
     a.qp = L.qp; a.kp = L.kp; a.qpt = L.qpt; a.kpt = L.kpt;
     a.lse2 = L.lse2; a.dd = L.dd;
     a.dqw = L.dqw; a.dkw = L.dkw; a.dvw = L.dvw;
+    a.dq_map = dq_c; a.dk_map = dk_c; a.dv_map = dv;
     a.dqp_part = L.dqp_part; a.dkp_part = L.dkp_part;
     {
       TimedGroup t_dkv(RIB_KERNEL_ATTN_BWD_DKV, st);
@@ -533,11 +535,13 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
     RIB_LAUNCH(launch_reduce_pos_grads(g.units, g.N, g.n_rows, g.r, rp, L.dqp_part, dq_p, st), "reduce dq_p");
     RIB_LAUNCH(launch_reduce_pos_grads(g.units, g.N, g.n_rows, g.r, rp, L.dkp_part, dk_p, st), "reduce dk_p");
     t_red.end();
-    TimedGroup t_unp(RIB_KERNEL_UNPARTITION, st);
-    RIB_LAUNCH(launch_unpartition(g, es, L.dqw, dq_c, st), "unpartition dq");
-    RIB_LAUNCH(launch_unpartition(g, es, L.dkw, dk_c, st), "unpartition dk");
-    RIB_LAUNCH(launch_unpartition(g, es, L.dvw, dv, st), "unpartition dv");
-    t_unp.end();
+    if (!bf) {
+      TimedGroup t_unp(RIB_KERNEL_UNPARTITION, st);
+      RIB_LAUNCH(launch_unpartition(g, es, L.dqw, dq_c, st), "unpartition dq");
+      RIB_LAUNCH(launch_unpartition(g, es, L.dkw, dk_c, st), "unpartition dk");
+      RIB_LAUNCH(launch_unpartition(g, es, L.dvw, dv, st), "unpartition dv");
+      t_unp.end();
+    }
 #undef RIB_LAUNCH
     return ok();
   } catch (...) {

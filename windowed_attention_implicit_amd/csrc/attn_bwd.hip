@@ -237,9 +237,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
     barrier_dma();
   }
 
-  // epilogue: lane = key, accumulator rows = channels 8(v/4) + 4h + v%4
-  bf16* dkw = (bf16*)a.dkw + ub * 32;
-  bf16* dvw = (bf16*)a.dvw + ub * 32;
+  // epilogue: lane = key, accumulator rows = channels 8(v/4) + 4h + v%4; dK_c and dV rows go
+  // straight to the [B, H, W, heads, 32] map (row of token t = window base + (t / w) W heads +
+  // (t % w) heads)
+  const int64_t map_base = make_pixel_map(g).pixel_head(unit, 0) * 32;
+  const int64_t row_elems = (int64_t)g.W * g.heads * 32, pix_elems = (int64_t)g.heads * 32;
+  bf16* dkm = (bf16*)a.dk_map;
+  bf16* dvm = (bf16*)a.dv_map;
   float* dkp = a.dkp_part + ub * rp;
   const float scale = a.scale;
 #pragma unroll
@@ -255,8 +259,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
         k4[i] = f32_to_bf16(acc_dk[nb][4 * gq + i] * scale);
       }
       const int ch = 8 * gq + 4 * half;
-      *(uint2*)(dvw + (int64_t)key * 32 + ch) = *(const uint2*)v4;
-      *(uint2*)(dkw + (int64_t)key * 32 + ch) = *(const uint2*)k4;
+      const int64_t row = map_base + (int64_t)(key / g.w) * row_elems + (int64_t)(key % g.w) * pix_elems;
+      *(uint2*)(dvm + row + ch) = *(const uint2*)v4;
+      *(uint2*)(dkm + row + ch) = *(const uint2*)k4;
       if (ch < rp) {
         f32x4 p4;
 #pragma unroll
@@ -383,7 +388,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     barrier_dma();
   }
 
-  bf16* dqw = (bf16*)a.dqw + ub * 32;
+  // dQ_c rows go straight to the [B, H, W, heads, 32] map
+  const int64_t map_base = make_pixel_map(g).pixel_head(unit, 0) * 32;
+  const int64_t row_elems = (int64_t)g.W * g.heads * 32, pix_elems = (int64_t)g.heads * 32;
+  bf16* dqm = (bf16*)a.dq_map;
   float* dqp = a.dqp_part + ub * rp;
   const float scale = a.scale;
 #pragma unroll
@@ -396,7 +404,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) q4[i] = f32_to_bf16(acc_dq[nb][4 * gq + i] * scale);
       const int ch = 8 * gq + 4 * half;
-      *(uint2*)(dqw + (int64_t)q * 32 + ch) = *(const uint2*)q4;
+      *(uint2*)(dqm + map_base + (int64_t)(q / g.w) * row_elems + (int64_t)(q % g.w) * pix_elems + ch) =
+          *(const uint2*)q4;
       if (ch < rp) {
         f32x4 p4;
 #pragma unroll
@@ -575,9 +584,21 @@ __global__ __launch_bounds__(256) void reduce_pos_grads_kernel(int units, int N,
   const int col = blockIdx.x * 32 + (threadIdx.x & 31);
   const int slice = threadIdx.x >> 5;
   const int ncols = N * rp;
+  // slice k adds units k, k + 8, k + 16, ... in that order; the loads are fetched eight at a time
+  // so that they overlap (thousands of units at small windows)
   float acc = 0.f;
-  if (col < ncols)
-    for (int u = slice; u < units; u += 8) acc += part[(int64_t)u * n_rows * rp + col];
+  if (col < ncols) {
+    const int64_t stride = (int64_t)n_rows * rp;
+    int u = slice;
+    for (; u + 56 < units; u += 64) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = part[(int64_t)(u + 8 * i) * stride + col];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc += v[i];
+    }
+    for (; u < units; u += 8) acc += part[(int64_t)u * stride + col];
+  }
   red[slice][threadIdx.x & 31] = acc;
   __syncthreads();
   if (slice == 0 && col < ncols) {

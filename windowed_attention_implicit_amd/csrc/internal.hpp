@@ -82,10 +82,13 @@ struct BwdArgs {
   const void* kpt;      // [rp][n_rows] kappa (bf16 only)
   const float* lse2;    // [units][n_rows]  log2-domain LSE
   const float* dd;      // [units][n_rows]  D_i = sum_c dO_ic O_ic
-  // outputs (windowed)
+  // outputs: windowed (float32 path) or in the [B, H, W, heads, 32] map (bf16 path)
   void* dqw;            // [units][n_rows][32]
   void* dkw;            // [units][n_rows][32]
   void* dvw;            // [units][n_rows][32]
+  void* dq_map;
+  void* dk_map;
+  void* dv_map;
   float* dqp_part;      // [units][n_rows][rp]
   float* dkp_part;      // [units][n_rows][rp]
 };
