@@ -28,4 +28,7 @@ from .rib import (  # noqa: F401
     default_scale,
     gelu_grad,
     posgen_bwd,
+    rpb_bias,
+    rpb_attention_window_fwd,
+    rpb_window_attn_fwd,
 )

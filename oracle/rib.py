@@ -35,6 +35,10 @@ Readings where the pages are silent (each is also listed in the design notes):
   R9  V is content only; O has d_c channels
   R10 non-overlapping windows, no shift, no padding; H and W divisible by w
   R14 D_i = sum_j P_ij dP_ij (textbook softmax backward)
+  R17 the RPB comparison (the bias RIB replaces, S = QK^T + B): one table of
+      (2w-1)^2 entries per head, B[i, j] = table[(y_i - y_j + w - 1)(2w - 1)
+      + (x_i - x_j + w - 1)]; the bias is added after the scale; default
+      scale 1/sqrt(d_c)
   R16 the position MLP is trained with the network: the positional gradients
       dQ_p, dK_p continue through Linear -> GELU -> Linear into dW1, db1,
       dW2, db2 by the chain rule; GELU'(z) = Phi(z) + z phi(z) (erf form, R5)
@@ -55,6 +59,7 @@ __all__ = [
     "concat_scores", "attention_window_fwd", "attention_window_bwd",
     "rib_window_attn_fwd", "rib_window_attn_bwd", "default_scale",
     "gelu_grad", "posgen_bwd",
+    "rpb_bias", "rpb_attention_window_fwd", "rpb_window_attn_fwd",
 ]
 
 
@@ -336,6 +341,54 @@ def rib_window_attn_fwd(q_c, k_c, v, q_p, k_p, w: int, scale: float | None = Non
         o, lse, _ = attention_window_fwd(
             _window_tokens(q_c, b, wy, wx, head, w), _window_tokens(k_c, b, wy, wx, head, w),
             _window_tokens(v, b, wy, wx, head, w), q_p, k_p, scale)
+        O[b, wy * w:(wy + 1) * w, wx * w:(wx + 1) * w, head, :] = o.reshape(w, w, d_c)
+        L[b, wy * w:(wy + 1) * w, wx * w:(wx + 1) * w, head] = lse.reshape(w, w)
+    return O, L
+
+
+def rpb_bias(w: int, table) -> np.ndarray:
+    """N x N relative-position bias of one head from its table (the RPB the pages contrast RIB with,
+    S = QK^T + B [EN "Problem Statement"; ES §1]), reading R17: token t = iy*w + ix (R2) and
+    B[i, j] = table[(y_i - y_j + w - 1) * (2w - 1) + (x_i - x_j + w - 1)]."""
+    table = np.asarray(table, dtype=np.float64)
+    if table.shape != ((2 * w - 1) ** 2,):
+        raise ValueError("table must hold (2w - 1)^2 entries")
+    t = np.arange(w * w)
+    iy, ix = t // w, t % w
+    idx = (iy[:, None] - iy[None, :] + w - 1) * (2 * w - 1) + (ix[:, None] - ix[None, :] + w - 1)
+    return table[idx]
+
+
+def rpb_attention_window_fwd(qc, kc, v, bias, scale: float):
+    """softmax(scale Q_c K_c^T + B) V for one window and head (R17). Returns (O, LSE)."""
+    S = scale * (np.asarray(qc, np.float64) @ np.asarray(kc, np.float64).T) + np.asarray(bias, np.float64)
+    m = S.max(axis=1, keepdims=True)
+    E = np.exp(S - m)
+    l = E.sum(axis=1, keepdims=True)
+    return (E / l) @ np.asarray(v, np.float64), m[:, 0] + np.log(l[:, 0])
+
+
+def rpb_window_attn_fwd(q_c, k_c, v, table, w: int, scale: float | None = None, units=None):
+    """RPB window attention over a [B, H, W, heads, d_c] map with tables [heads, (2w - 1)^2] (R17).
+
+    Same windowing as ``rib_window_attn_fwd``; returns (O, LSE) with NaN for units not computed.
+    """
+    B, H, W, heads, d_c = q_c.shape
+    _check_divisible(H, W, w)
+    table = np.asarray(table, dtype=np.float64)
+    if table.shape != (heads, (2 * w - 1) ** 2):
+        raise ValueError("table must be [heads, (2w - 1)^2]")
+    if scale is None:
+        scale = 1.0 / math.sqrt(d_c)
+    O = np.full((B, H, W, heads, d_c), np.nan)
+    L = np.full((B, H, W, heads), np.nan)
+    biases = {}
+    for (b, wy, wx, head) in (units if units is not None else _all_units(B, H, W, w, heads)):
+        if head not in biases:
+            biases[head] = rpb_bias(w, table[head])
+        o, lse = rpb_attention_window_fwd(_window_tokens(q_c, b, wy, wx, head, w),
+                                          _window_tokens(k_c, b, wy, wx, head, w),
+                                          _window_tokens(v, b, wy, wx, head, w), biases[head], scale)
         O[b, wy * w:(wy + 1) * w, wx * w:(wx + 1) * w, head, :] = o.reshape(w, w, d_c)
         L[b, wy * w:(wy + 1) * w, wx * w:(wx + 1) * w, head] = lse.reshape(w, w)
     return O, L

@@ -15,6 +15,7 @@ import oracle.rib as orib
 import test_oracle_attention as ta
 import test_oracle_posgen as tp
 import test_oracle_posgen_bwd as tb
+import test_oracle_rpb as tr
 
 
 def _golden():
@@ -136,6 +137,24 @@ def _posgen_bwd_w1_transposed(w, F, w1, b1, w2, b2, r, dq, dk):
     return g[0].T.reshape(g[0].shape), g[1], g[2], g[3]
 
 
+def _rpb_bias_reversed(w, table):
+    t = np.arange(w * w)
+    iy, ix = t // w, t % w
+    idx = (iy[None, :] - iy[:, None] + w - 1) * (2 * w - 1) + (ix[None, :] - ix[:, None] + w - 1)   # j - i
+    return np.asarray(table, np.float64)[idx]
+
+
+def _rpb_bias_xy_swapped(w, table):
+    t = np.arange(w * w)
+    iy, ix = t // w, t % w
+    idx = (ix[:, None] - ix[None, :] + w - 1) * (2 * w - 1) + (iy[:, None] - iy[None, :] + w - 1)
+    return np.asarray(table, np.float64)[idx]
+
+
+def _rpb_fwd_scaled_bias(qc, kc, v, bias, scale):
+    return orib.__dict__["_orig_rpb_fwd"](qc, kc, v, scale * np.asarray(bias), scale)
+
+
 MUTATIONS = [
     ("concat_scores", _scores_no_bias, [(ta.test_worked_example_w2, "golden"), (ta.test_concat_identity,)]),
     ("concat_scores", _scores_transposed_bias, [(ta.test_concat_identity,), (ta.test_matches_torch_sdpa_with_additive_bias,)]),
@@ -154,6 +173,9 @@ MUTATIONS = [
     ("posgen_bwd", _posgen_bwd_no_gelu_grad, [(tb.test_posgen_bwd_finite_differences, 3, 2, 5, 2)]),
     ("posgen_bwd", _posgen_bwd_split_swapped, [(tb.test_posgen_bwd_finite_differences, 3, 2, 5, 2), (tb.test_posgen_bwd_split_and_linearity,)]),
     ("posgen_bwd", _posgen_bwd_w1_transposed, [(tb.test_posgen_bwd_matches_torch_autograd, 8, 16, 64, 8)]),
+    ("rpb_bias", _rpb_bias_reversed, [(tr.test_rpb_bias_brute_force, 3), (tr.test_rpb_linear_table_equals_rib_with_rank3_tokens,)]),
+    ("rpb_bias", _rpb_bias_xy_swapped, [(tr.test_rpb_bias_brute_force, 3), (tr.test_rpb_linear_table_equals_rib_with_rank3_tokens,)]),
+    ("rpb_attention_window_fwd", _rpb_fwd_scaled_bias, [(tr.test_rpb_matches_torch_sdpa_with_additive_mask,), (tr.test_rpb_linear_table_equals_rib_with_rank3_tokens,)]),
 ]
 
 
@@ -162,7 +184,7 @@ def test_planted_mistake_is_caught(monkeypatch, name, bad, pins):
     orig = getattr(orib, name)
     for key, fn in (("_orig_bwd", orib.attention_window_bwd), ("_orig_fourier", orib.fourier_features),
                     ("_orig_posgen", orib.posgen), ("_orig_partition", orib.window_partition),
-                    ("_orig_posgen_bwd", orib.posgen_bwd)):
+                    ("_orig_posgen_bwd", orib.posgen_bwd), ("_orig_rpb_fwd", orib.rpb_attention_window_fwd)):
         monkeypatch.setitem(orib.__dict__, key, fn)
     monkeypatch.setattr(orib, name, bad)
     monkeypatch.setattr(oracle, name, bad)
