@@ -13,8 +13,9 @@ unit, padding and softmax not counted) over the whole step, windows/s, % of
 the bf16 dense MFMA peak, a roofline entry for the attention kernel (timed
 with HIP events on its own stream), per-kernel GB/s of the gathers and
 posgen, and the float64 CPU oracle timed on a bounded sample of units as a
-baseline; with --stack also the window-size stack (windows 16/32/64/96,
-forward + backward).
+baseline; the relative-position-bias comparison kernel on the same inputs
+(--no-rpb skips it); with --stack also the window-size stack (windows
+16/32/64/96, forward + backward).
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--stack]
 """
@@ -229,6 +230,37 @@ def stack_measure(steps: int, warmup: int, dev):
             "layers": per}
 
 
+def rpb_compare(wl, x, dev, steps: int, rib_attn_ms: float):
+    """The relative-position-bias attention that RIB replaces, on the same Q_c, K_c, V: the RPB
+    kernel (bias gathered per score from an fp16 (2w-1)^2 table in LDS) against the RIB attention
+    kernel, and the parameter / materialized-bias memory of both forms."""
+    import torch
+    import rib_synth
+    import windowed_attention_implicit_amd as rib
+    q, k, v = (to_gpu(x[n], dev) for n in ("q_c", "k_c", "v"))
+    table = torch.from_numpy(rib_synth.make_rpb_table(wl.heads, wl.w, seed=96)).to(dev)
+    plan = rib.RpbFwdPlan(q, k, v, table, wl.w)
+
+    def reset():
+        for g in rib.KERNEL_GROUPS:
+            rib.kernel_timing_read(g)
+
+    rib.kernel_timing_enable(True)
+    ms, _ = time_steps(plan.run, steps, 3, reset)
+    kern, _ = kernel_avg_ms(rib, "rpb_attn_fwd")
+    rib.kernel_timing_enable(False)
+    content_flops = 2 * wl.units * wl.N * wl.N * 2 * wl.d_c
+    n_tab = (2 * wl.w - 1) ** 2
+    return {"workload": "same Q_c, K_c, V as the headline workload; N(0,1) tables [heads, (2w-1)^2]",
+            "rpb_call_ms": round(ms, 4), "rpb_attn_kernel_ms": kern and round(kern, 4),
+            "rib_attn_kernel_ms": round(rib_attn_ms, 4),
+            "rpb_over_rib_kernel_time": kern and round(kern / rib_attn_ms, 3),
+            "rpb_content_tflops": kern and round(content_flops / kern / 1e9, 1),
+            "rpb_table_params_per_layer": wl.heads * n_tab,
+            "rib_mlp_params_per_layer": wl.hidden * 4 * wl.n_freq + wl.hidden + 2 * wl.r * wl.hidden + 2 * wl.r,
+            "materialized_bias_bytes_bf16": wl.heads * wl.N * wl.N * 2}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +270,8 @@ def main():
     ap.add_argument("--cpu-units", type=int, default=40)
     ap.add_argument("--stack", action="store_true",
                     help="also time the window-size stack 16/32/64/96, forward + backward")
+    ap.add_argument("--no-rpb", action="store_true",
+                    help="skip the relative-position-bias comparison kernel")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -339,6 +373,10 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         result["calibration_copy_bytes"] = 2 * n * 4
+
+    if not args.no_rpb:
+        print("bench: RPB comparison kernel", file=sys.stderr, flush=True)
+        result["rpb_compare"] = rpb_compare(wl, x, dev, max(10, args.steps // 2), attn_ms)
 
     if args.stack:
         print("bench: window-size stack fwd+bwd", file=sys.stderr, flush=True)

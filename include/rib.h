@@ -10,6 +10,7 @@
  * Scaling Super-Resolution Transformer with FlashAttention", arXiv 2603.06738):
  *   [EN]  gist.science/paper/2603.06738, "Technical Summary"
  *   [DE]  gist.science/de/paper/2603.06738, "Technische Zusammenfassung"
+ *   [ES]  gist.science/es/paper/2603.06738, "Resumen tecnico"
  *   [ZH]  gist.science/zh/paper/2603.06738, technical part
  *   [ABS] khansong-paper-with-me.hf.space, the paper's abstract
  *
@@ -199,6 +200,43 @@ rib_status_t rib_posgen_bwd(int32_t w, const rib_mlp_t* mlp, const float* dq_p, 
                             float* dw1, float* db1, float* dw2, float* db2,
                             void* workspace, size_t workspace_bytes, rib_stream_t stream);
 
+/* Bytes of device workspace rib_rpb_window_attn_fwd needs (0 when invalid). */
+size_t rib_rpb_fwd_workspace_size(const rib_shape_t* shape, rib_dtype_t dtype);
+
+/*
+ * rib_rpb_window_attn_fwd - the relative-position-bias (RPB) attention that
+ * RIB replaces [EN "Problem Statement": an additive bias B indexed by relative
+ * position breaks the fused kernel's plain QK^T structure and its table grows
+ * with the window area; ES §1], as a comparison kernel on the same shapes.
+ *
+ * For every unit (batch, window, head h), over the N = w*w tokens of the window:
+ *   O = softmax(scale * Q_c K_c^T + B_h) V,
+ *   B_h[i, j] = table[h][(y_i - y_j + w - 1) * (2w - 1) + (x_i - x_j + w - 1)]
+ * with token t = y*w + x. The bias is gathered per score from the table (no
+ * N x N bias or score matrix in memory); the table is staged per workgroup in
+ * LDS as fp16 after multiplication by log2(e), so entries must satisfy
+ * |b| < 45000 and carry fp16 rounding (relative 2^-11).
+ *
+ *   shape          as for rib_window_attn_fwd; shape->r is ignored. d_c = 32;
+ *                  w is limited by LDS: the (2w-1)^2 fp16 table plus the tile
+ *                  ring must fit one CU's 160 KB (w <= 121), else
+ *                  RIB_ERR_UNSUPPORTED
+ *   dtype          RIB_BF16 only (RIB_ERR_UNSUPPORTED otherwise)
+ *   scale          <= 0 selects 1/sqrt(d_c)
+ *   q_c, k_c, v    (device) [B, H, W, heads, d_c] bfloat16
+ *   table          (device) [heads, (2w-1)^2] float32
+ *   o              (device) output [B, H, W, heads, d_c] bfloat16
+ *   lse            (device) output [B, H, W, heads] float32 or NULL
+ *   workspace      (device) at least rib_rpb_fwd_workspace_size() bytes,
+ *                  256-byte aligned; contents on return unspecified
+ * Errors as for rib_window_attn_fwd.
+ */
+rib_status_t rib_rpb_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, float scale,
+                                     const void* q_c, const void* k_c, const void* v,
+                                     const float* table, void* o, float* lse,
+                                     void* workspace, size_t workspace_bytes,
+                                     rib_stream_t stream);
+
 /*
  * Kernel timing, a measurement aid: while enabled, every posgen / forward /
  * backward call brackets each of its kernel groups with HIP events recorded
@@ -218,7 +256,8 @@ typedef enum {
   RIB_KERNEL_ATTN_BWD_DQ = 6,  /* the backward dQ kernel alone */
   RIB_KERNEL_POS_REDUCE = 7,   /* the fixed-order sum of the dQ_p / dK_p partials */
   RIB_KERNEL_POSGEN_BWD = 8,   /* the position-MLP weight-gradient kernels (partials + sum) */
-  RIB_KERNEL_COUNT = 9
+  RIB_KERNEL_RPB_ATTN_FWD = 9, /* the RPB comparison attention kernel alone */
+  RIB_KERNEL_COUNT = 10
 } rib_kernel_t;
 
 rib_status_t rib_kernel_timing_enable(int32_t enable);

@@ -168,6 +168,12 @@ def make_pos_grads(N: int, r: int, seed: int) -> tuple:
     return (rng.standard_normal((N, r), dtype=np.float32), rng.standard_normal((N, r), dtype=np.float32))
 
 
+def make_rpb_table(heads: int, w: int, seed: int, std: float = 1.0) -> np.ndarray:
+    """Relative-position-bias tables of the RPB comparison: float32 N(0, std^2), [heads, (2w - 1)^2]."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return (std * rng.standard_normal((heads, (2 * w - 1) ** 2))).astype(np.float32)
+
+
 def custom_workload(B, H, W, heads, d_c, w, r, dtype="bf16", backward=False, seed=0,
                     n_freq=N_FREQ, hidden=HIDDEN) -> Workload:
     """A workload of arbitrary shape (small and ragged test cases)."""

@@ -90,6 +90,33 @@ def test_fwd_validation(L):
     assert _fwd(L, rib.Shape(0, 192, 192, 6, 32, 96, 16), ptrs=[None] * 6, ws=None, ws_bytes=0) == rib.RIB_OK
 
 
+def test_rpb_validation(L):
+    good = rib.Shape(2, 192, 192, 6, 32, 96, 0)     # r is ignored by the RPB kernel
+
+    def call(shape, ws_bytes=1 << 40, dtype=rib.RIB_BF16, nulls=(), ws=FAKE, table=FAKE):
+        p = [None if i in nulls else FAKE for i in range(3)]
+        return L.rib_rpb_window_attn_fwd(ctypes.byref(shape), dtype, 0.0, *p, table, FAKE, None, ws, ws_bytes,
+                                         None)
+
+    need = L.rib_rpb_fwd_workspace_size(ctypes.byref(good), rib.RIB_BF16)
+    # K and V^T windowed copies, the fp16 tables and per-key offsets: linear, no N x N bias
+    assert 2 * 2 * 192 * 192 * 6 * 32 * 2 <= need <= 2 * 2 * 192 * 192 * 6 * 32 * 2 + (1 << 20)
+    assert call(good, dtype=rib.RIB_F32) == rib.RIB_ERR_UNSUPPORTED
+    assert b"bfloat16" in L.rib_last_error()
+    assert L.rib_rpb_fwd_workspace_size(ctypes.byref(good), rib.RIB_F32) == 0
+    assert call(rib.Shape(1, 122, 122, 1, 32, 122, 0)) == rib.RIB_ERR_UNSUPPORTED      # table too large for LDS
+    assert b"LDS" in L.rib_last_error()
+    assert call(rib.Shape(1, 121, 121, 1, 32, 121, 0), ws=None) == rib.RIB_ERR_WORKSPACE   # w = 121 fits
+    assert call(rib.Shape(2, 192, 192, 6, 64, 96, 0)) == rib.RIB_ERR_UNSUPPORTED        # d_c
+    assert call(rib.Shape(2, 190, 192, 6, 32, 96, 0)) == rib.RIB_ERR_INVALID_ARG        # H % w
+    assert call(good, table=None) == rib.RIB_ERR_INVALID_ARG
+    assert b"table" in L.rib_last_error()
+    assert call(good, nulls=(1,)) == rib.RIB_ERR_INVALID_ARG
+    assert call(good, ws_bytes=need - 1) == rib.RIB_ERR_WORKSPACE
+    assert call(good, ws=MISALIGNED, ws_bytes=need) == rib.RIB_ERR_INVALID_ARG
+    assert call(rib.Shape(0, 192, 192, 6, 32, 96, 0), nulls=(0, 1, 2), ws=None, ws_bytes=0, table=None) == rib.RIB_OK
+
+
 def test_bwd_validation(L):
     good = rib.Shape(2, 192, 192, 6, 32, 64, 16)
     need = L.rib_bwd_workspace_size(ctypes.byref(good), rib.RIB_BF16)

@@ -6,10 +6,12 @@ kernels of librib.so. There is no fallback: if the library is missing or no
 GPU is present, the compute entry points raise.
 
 Entry points (same names as the C ABI, without the ``rib_`` prefix):
-  posgen, window_partition, window_unpartition, window_attn_fwd,
-  window_attn_bwd, fwd_workspace_size, bwd_workspace_size
-plus ``FwdPlan`` / ``BwdPlan``, which preallocate workspace and outputs so a
-call can be repeated without allocating.
+  posgen, posgen_bwd, window_partition, window_unpartition, window_attn_fwd,
+  window_attn_bwd, fwd_workspace_size, bwd_workspace_size,
+  rpb_window_attn_fwd, rpb_fwd_workspace_size (the relative-position-bias
+  comparison kernel)
+plus ``FwdPlan`` / ``BwdPlan`` / ``RpbFwdPlan``, which preallocate workspace
+and outputs so a call can be repeated without allocating.
 """
 
 from __future__ import annotations
@@ -25,6 +27,7 @@ __all__ = [
     "RIB_F32", "RIB_BF16", "RibError", "lib", "lib_path", "exported_symbols",
     "posgen", "posgen_bwd", "window_partition", "window_unpartition", "window_attn_fwd", "window_attn_bwd",
     "fwd_workspace_size", "bwd_workspace_size", "FwdPlan", "BwdPlan", "Shape",
+    "rpb_window_attn_fwd", "rpb_fwd_workspace_size", "RpbFwdPlan",
     "KERNEL_GROUPS", "kernel_timing_enable", "kernel_timing_read",
 ]
 
@@ -65,6 +68,8 @@ _SIGS = {
     "rib_bwd_workspace_size": (_sz, [ctypes.POINTER(Shape), _i32]),
     "rib_window_attn_fwd": (_i32, [ctypes.POINTER(Shape), _i32, _f32] + [_vp] * 7 + [_vp, _sz, _vp]),
     "rib_window_attn_bwd": (_i32, [ctypes.POINTER(Shape), _i32, _f32] + [_vp] * 13 + [_vp, _sz, _vp]),
+    "rib_rpb_fwd_workspace_size": (_sz, [ctypes.POINTER(Shape), _i32]),
+    "rib_rpb_window_attn_fwd": (_i32, [ctypes.POINTER(Shape), _i32, _f32] + [_vp] * 6 + [_vp, _sz, _vp]),
     "rib_kernel_timing_enable": (_i32, [_i32]),
     "rib_kernel_timing_read": (_i32, [_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     "rib_status_string": (ctypes.c_char_p, [_i32]),
@@ -274,8 +279,52 @@ def window_attn_bwd(q_c, k_c, v, q_p, k_p, o, lse, d_o, w: int, scale: float | N
     return BwdPlan(q_c, k_c, v, q_p, k_p, o, lse, d_o, w, scale).run()
 
 
+# ---------------------------------------------------------------- RPB comparison
+
+def rpb_fwd_workspace_size(shape: Shape, dtype: torch.dtype) -> int:
+    return int(lib().rib_rpb_fwd_workspace_size(ctypes.byref(shape), _dtype_code(dtype)))
+
+
+class RpbFwdPlan:
+    """Preallocated call of the relative-position-bias comparison kernel:
+    O = softmax(scale Q_c K_c^T + B) V with B gathered from ``table`` [heads, (2w-1)^2] (float32)."""
+
+    def __init__(self, q_c, k_c, v, table, w: int, scale: float | None = None, want_lse: bool = True):
+        _require_gpu(q_c, k_c, v, table)
+        self.shape = _shape_of(q_c, w, 0)
+        self.dtype = _dtype_code(q_c.dtype)
+        for t in (k_c, v):
+            if t.dtype != q_c.dtype:
+                raise TypeError("Q_c, K_c and V must share one dtype")
+        if table.dtype != torch.float32 or table.shape != (q_c.shape[3], (2 * w - 1) ** 2):
+            raise ValueError("table must be float32 [heads, (2w - 1)^2]")
+        self.inputs = (q_c, k_c, v, table)
+        self.scale = 0.0 if scale is None else float(scale)
+        self.o = torch.empty_like(q_c)
+        s = self.shape
+        self.lse = torch.empty((s.B, s.H, s.W, s.heads), dtype=torch.float32, device=q_c.device) if want_lse else None
+        self.ws_bytes = rpb_fwd_workspace_size(self.shape, q_c.dtype)
+        if self.ws_bytes == 0:   # the shape or dtype is rejected: report why
+            _check(lib().rib_rpb_window_attn_fwd(ctypes.byref(self.shape), self.dtype, self.scale, None, None, None,
+                                                 None, None, None, None, 0, None))
+        self.ws = _workspace(self.ws_bytes, q_c.device)
+
+    def run(self, stream=None):
+        q_c, k_c, v, table = self.inputs
+        st = _stream(q_c.device) if stream is None else ctypes.c_void_p(stream)
+        _check(lib().rib_rpb_window_attn_fwd(ctypes.byref(self.shape), self.dtype, self.scale, _ptr(q_c), _ptr(k_c),
+                                             _ptr(v), _ptr(table), _ptr(self.o), _ptr(self.lse), _ptr(self.ws),
+                                             self.ws_bytes, st))
+        return self.o, self.lse
+
+
+def rpb_window_attn_fwd(q_c, k_c, v, table, w: int, scale: float | None = None, want_lse: bool = True):
+    """RPB comparison attention; returns (O, LSE or None). bfloat16 only; scale defaults to 1/sqrt(d_c)."""
+    return RpbFwdPlan(q_c, k_c, v, table, w, scale, want_lse).run()
+
+
 KERNEL_GROUPS = {"posgen": 0, "partition": 1, "attn_fwd": 2, "unpartition": 3, "bwd_prep": 4,
-                 "attn_bwd_dkv": 5, "attn_bwd_dq": 6, "pos_reduce": 7, "posgen_bwd": 8}
+                 "attn_bwd_dkv": 5, "attn_bwd_dq": 6, "pos_reduce": 7, "posgen_bwd": 8, "rpb_attn_fwd": 9}
 
 
 def kernel_timing_enable(enable: bool = True):

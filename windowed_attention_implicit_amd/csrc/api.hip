@@ -118,6 +118,43 @@ FwdLayout fwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
   return L;
 }
 
+// RPB comparison forward: windowed K (rows) and V^T (kappa), key-norm maxima,
+// the fp16 tables, their maxima and the per-key table offsets.
+struct RpbLayout {
+  void *kw, *vw;
+  float* kmax2;
+  _Float16* tab16;
+  float* tmax;
+  int* kidx;
+  size_t bytes;
+};
+
+RpbLayout rpb_layout(const Geom& g, void* ws) {
+  const size_t t = (size_t)g.units * g.n_rows * g.d_c * 2;
+  Carve c(ws);
+  RpbLayout L;
+  L.kw = c.take(t);
+  L.vw = c.take(t);
+  L.kmax2 = (float*)c.take((size_t)g.units * key_bound_parts(g.N) * sizeof(float));
+  L.tab16 = (_Float16*)c.take((size_t)g.heads * rpb_table_stride(g.w) * 2);
+  L.tmax = (float*)c.take((size_t)g.heads * sizeof(float));
+  L.kidx = (int*)c.take((size_t)g.n_rows * sizeof(int));
+  L.bytes = c.off;
+  return L;
+}
+
+constexpr size_t kLdsPerCu = 160 * 1024;
+
+rib_status_t check_rpb(const rib_shape_t* s, rib_dtype_t dt) {
+  RIB_TRY(check_shape(s, dt, false));
+  if (dt != RIB_BF16) return fail(RIB_ERR_UNSUPPORTED, "the RPB kernel is bfloat16 only");
+  if (s->d_c != 32) return fail(RIB_ERR_UNSUPPORTED, "d_c=%d: only d_c = 32 is implemented", s->d_c);
+  if (rpb_fwd_lds_bytes(s->w) > kLdsPerCu)
+    return fail(RIB_ERR_UNSUPPORTED, "window size w=%d: the RPB table and tiles need %zu bytes of LDS (max %zu)", s->w,
+                rpb_fwd_lds_bytes(s->w), kLdsPerCu);
+  return RIB_OK;
+}
+
 struct BwdLayout {
   void *qw, *kw, *vw, *dow, *qt, *kt, *dot, *qp, *kp, *qpt, *kpt, *dqw, *dkw, *dvw;
   float *lse2, *dd, *dqp_part, *dkp_part;
@@ -444,6 +481,58 @@ rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
     return ok();
   } catch (...) {
     return fail(RIB_ERR_HIP, "unexpected C++ exception in rib_window_attn_fwd");
+  }
+}
+
+size_t rib_rpb_fwd_workspace_size(const rib_shape_t* shape, rib_dtype_t dtype) {
+  if (check_rpb(shape, dtype) != RIB_OK) return 0;
+  Geom g = make_geom(*shape);
+  return rpb_layout(g, nullptr).bytes;
+}
+
+rib_status_t rib_rpb_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, float scale, const void* q_c,
+                                     const void* k_c, const void* v, const float* table, void* o, float* lse,
+                                     void* workspace, size_t workspace_bytes, rib_stream_t stream) {
+  try {
+    RIB_TRY(check_rpb(shape, dtype));
+    if (!(scale == scale) || isinf(scale)) return fail(RIB_ERR_INVALID_ARG, "scale is not finite");
+    if (shape->B == 0) return ok();
+    RIB_TRY(check_ptr(q_c, "q_c"));
+    RIB_TRY(check_ptr(k_c, "k_c"));
+    RIB_TRY(check_ptr(v, "v"));
+    RIB_TRY(check_ptr(o, "o"));
+    if (!table || ((uintptr_t)table & 3u)) return fail(RIB_ERR_INVALID_ARG, "table is NULL or not 4-byte aligned");
+    if (lse && ((uintptr_t)lse & 3u)) return fail(RIB_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+    Geom g = make_geom(*shape);
+    const size_t need = rpb_layout(g, nullptr).bytes;
+    if (!workspace || workspace_bytes < need)
+      return fail(RIB_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
+    if ((uintptr_t)workspace & 255u) return fail(RIB_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
+    RpbLayout L = rpb_layout(g, workspace);
+    hipStream_t st = (hipStream_t)stream;
+    hipError_t e;
+    TimedGroup t_part(RIB_KERNEL_PARTITION, st);
+    if ((e = launch_partition(g, 2, WinLayout::kRows, k_c, L.kw, st)) != hipSuccess) return hip_fail(e, "partition k");
+    if ((e = launch_partition(g, 2, WinLayout::kTransKappa, v, L.vw, st)) != hipSuccess)
+      return hip_fail(e, "partition v");
+    if ((e = launch_rpb_prep(g, table, L.tab16, L.tmax, L.kidx, st)) != hipSuccess) return hip_fail(e, "rpb prep");
+    FwdArgs a;
+    a.g = g;
+    a.c = (scale > 0.f ? scale : 1.0f / sqrtf((float)shape->d_c)) * kLog2e;
+    a.qw = nullptr; a.kw = L.kw; a.vw = L.vw; a.qp = nullptr; a.kp = nullptr; a.ow = nullptr;
+    a.q_map = q_c; a.o_map = o;
+    a.lse = lse;
+    a.kmax2 = L.kmax2;
+    a.rp = 0;
+    a.rpb_tab16 = L.tab16; a.rpb_max = L.tmax; a.rpb_kidx = L.kidx; a.rpb_stride = rpb_table_stride(g.w);
+    if ((e = launch_key_bound(a, st)) != hipSuccess) return hip_fail(e, "key bound");
+    t_part.end();
+    TimedGroup t_attn(RIB_KERNEL_RPB_ATTN_FWD, st);
+    if ((e = launch_attn_fwd_rpb(a, st)) != hipSuccess) return hip_fail(e, "rpb attention forward");
+    t_attn.end();
+    return ok();
+  } catch (...) {
+    return fail(RIB_ERR_HIP, "unexpected C++ exception in rib_rpb_window_attn_fwd");
   }
 }
 

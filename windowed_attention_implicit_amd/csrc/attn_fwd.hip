@@ -46,7 +46,6 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kQPerWave = 64;             // two 32-query MFMA column blocks
-constexpr int kQPerBlock = kWaves * kQPerWave;
 constexpr int kKeyTile = 64;
 constexpr float kLazyTau = 8.0f;          // log2 units
 constexpr float kUnderflowGuard = 8.673617379884035e-19f;  // 2^-60
@@ -70,15 +69,19 @@ __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32)
 // compiler from moving LDS reads or DMA issue across it.
 __device__ __forceinline__ void barrier_dma() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int KP>  // positional 16-channel steps: 1 (r <= 16) or 2 (r <= 32)
+// KP: positional 16-channel steps, 1 (r <= 16) or 2 (r <= 32); 0 with RPB:
+// the relative-position-bias comparison variant (content-only scores plus a
+// bias gathered from a per-head table).
+template <int KP, bool RPB = false>
 struct FwdCfg {
+  static_assert(!RPB || KP == 0, "the RPB variant has no positional channels");
   static constexpr int kSteps = 2 + KP;             // MFMA K-steps of the score
   // One LDS tile buffer, in 16-byte chunks: K_c [64 keys][4 + 1 pad], then
   // K_p [64 keys][2KP + 1 pad], then V^T [32 channels][8 + 1 pad] (padded to
-  // whole DMA instructions). The odd row strides keep the fragment reads
-  // free of bank conflicts.
+  // whole DMA instructions), then (RPB) the 64 keys' table byte offsets. The
+  // odd row strides keep the fragment reads free of bank conflicts.
   static constexpr int kKcRow = 5;
-  static constexpr int kKpRow = 2 * KP + 1;
+  static constexpr int kKpRow = KP ? 2 * KP + 1 : 0;
   static constexpr int kVRow = kKeyTile / 8 + 1;
   static constexpr int kKcOff = 0;
   static constexpr int kKpOff = kKcOff + kKeyTile * kKcRow;
@@ -86,10 +89,16 @@ struct FwdCfg {
   static constexpr int kKcDma = kKeyTile * kKcRow / 64;          // DMA instructions per tile part
   static constexpr int kKpDma = kKeyTile * kKpRow / 64;
   static constexpr int kVDma = (32 * kVRow + 63) / 64;
-  static constexpr int kDma = kKcDma + kKpDma + kVDma;
-  static constexpr int kChunks = kVOff + 64 * kVDma;
+  static constexpr int kIdxOff = kVOff + 64 * kVDma;
+  static constexpr int kIdxDma = RPB ? 1 : 0;                   // 64 int32 = 16 chunks (+48 zeroed)
+  static constexpr int kDma = kKcDma + kKpDma + kVDma + kIdxDma;
+  static constexpr int kChunks = kIdxOff + 64 * kIdxDma;
+  // waves per workgroup: the RPB table fills most of a CU's LDS, so its
+  // workgroups are twice as wide to keep two waves per SIMD
+  static constexpr int kWv = RPB ? 2 * kWaves : kWaves;
+  static constexpr int kQPerBlock = kWv * kQPerWave;
   static_assert(kKeyTile * kKcRow % 64 == 0 && kKeyTile * kKpRow % 64 == 0, "whole DMA instructions");
-  static_assert(kDma <= 4 * kWaves, "at most four DMA instructions per wave and tile");
+  static_assert(kDma <= 4 * kWv && kDma >= kWv, "one to four DMA instructions per wave and tile");
 };
 constexpr int kBufs = 4;                  // LDS tile ring depth
 // word 3 of a raw buffer resource on gfx9-class parts (32-bit data format)
@@ -102,9 +111,9 @@ struct BoolTag {
   static constexpr bool value = V;
 };
 
-template <int KP>
-__global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
-  typedef FwdCfg<KP> C;
+template <int KP, bool RPB = false>
+__global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_kernel(FwdArgs a) {
+  typedef FwdCfg<KP, RPB> C;
   // Ring of kBufs tile buffers. While tile t is processed, tiles t and t + 1
   // are read (V^T of t, K of t and, prefetched, of t + 1) and the DMA for
   // tile t + 3 fills the buffer tile t - 1 used; tile t + 2 must have landed
@@ -113,7 +122,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
 
   const Geom& g = a.g;
   const int N = g.N, n_rows = g.n_rows;
-  const int nqb = (N + kQPerBlock - 1) / kQPerBlock;
+  const int nqb = (N + C::kQPerBlock - 1) / C::kQPerBlock;
   const int total = g.units * nqb;
   const int logical = xcd_remap(blockIdx.x, total);
   const int unit = logical / nqb;
@@ -146,8 +155,24 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   for (int o = 32; o > 0; o >>= 1) km = fmaxf(km, __shfl_xor(km, o));
   const float kmax = sqrtf(km);
 
+  // ---- RPB: the head's table, prepared in fp16 log2 units (entries padded to
+  // whole 1 KiB DMA blocks), is copied into LDS by DMA before the first tile;
+  // its maximum joins the softmax bound.
+  extern __shared__ _Float16 sTab[];
+  float bmax = 0.f;
+  if constexpr (RPB) {
+    const int head = unit % g.heads;
+    const int tblocks = a.rpb_stride / 512;
+    const _Float16* tab = a.rpb_tab16 + (int64_t)head * a.rpb_stride;
+    const __amdgpu_buffer_rsrc_t rs_t = __builtin_amdgcn_make_buffer_rsrc((void*)tab, 0, a.rpb_stride * 2, kRsrcWord3);
+    for (int i = wave; i < tblocks; i += C::kWv)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_t, (__attribute__((address_space(3))) void*)&sTab[512 * i], 16,
+                                               lane * 16 + i * 1024, 0, 0, 0);
+    bmax = a.rpb_max[head];
+  }
+
   // ---- query fragments (B operand), pre-scaled into the log2 domain
-  const int q0 = qb * kQPerBlock + wave * kQPerWave;
+  const int q0 = qb * C::kQPerBlock + wave * kQPerWave;
   bf16x8 qf[2][C::kSteps];
   float mref[2];
 #pragma unroll
@@ -171,7 +196,22 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       }
     }
     sq += swap_halves(sq);
-    mref[nb] = sqrtf(sq) * kmax;
+    mref[nb] = sqrtf(sq) * kmax + bmax;
+  }
+  // RPB: the bias of query q and key k is table[(w-1)(2w-1) + (w-1) + QI(q) - QI(k)] with
+  // QI(t) = (t / w)(2w-1) + t % w. Per column block the lane keeps the LDS byte address of
+  // its query's part; the key part arrives with every tile as the byte offset -2 QI(k)
+  // (0 for padded keys, which are masked).
+  unsigned tab_base[2] = {0u, 0u};
+  if constexpr (RPB) {
+    const int w2 = 2 * g.w - 1;
+    const unsigned lds0 = (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)sTab;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int q = min(q0 + nb * 32 + l32, N - 1);
+      const int qi = (q / g.w) * w2 + q % g.w;
+      tab_base[nb] = lds0 + 2u * (unsigned)((g.w - 1) * w2 + (g.w - 1) + qi);
+    }
   }
 
   // ---- tile DMA: buffer_load ... lds writes lane l's 16 bytes to chunk l of
@@ -183,10 +223,11 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   const __amdgpu_buffer_rsrc_t rs_kc = __builtin_amdgcn_make_buffer_rsrc((void*)kw, 0, n_rows * 64, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_kp = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, n_rows * rp * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc((void*)vt, 0, n_rows * 64, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_i = __builtin_amdgcn_make_buffer_rsrc((void*)a.rpb_kidx, 0, n_rows * 4, kRsrcWord3);
   int dma_off[4];
 #pragma unroll
   for (int jj = 0; jj < 4; ++jj) {
-    const int i = 4 * jj + wave;
+    const int i = C::kWv * jj + wave;
     const int c = 64 * i + lane;
     int off = 0;
     if (i < C::kKcDma) {
@@ -196,28 +237,32 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       const int c2 = c - C::kKpOff;
       const int r = c2 / C::kKpRow, k = c2 % C::kKpRow;
       off = r * rp * 2 + (k < 2 * KP ? k : 0) * 16;
-    } else {
+    } else if (i < C::kKcDma + C::kKpDma + C::kVDma) {
       const int c3 = c - C::kVOff;
       int r = c3 / C::kVRow, k = c3 % C::kVRow;
       if (r >= 32) r = 0, k = 0;
       off = r * n_rows * 2 + (k < 8 ? k : 0) * 16;
+    } else {
+      off = lane < 16 ? lane * 16 : (int)0x80000000;   // 64 key offsets; the rest of the block reads zeros
     }
     dma_off[jj] = off;
   }
-  const int dma_count = (C::kDma - wave + 3) / 4;   // DMA instructions of this wave per tile
+  const int dma_count = (C::kDma - wave + C::kWv - 1) / C::kWv;   // DMA instructions of this wave per tile
   auto dma_tile = [&](int t, int buf) {
     const int k0 = t * kKeyTile;
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
-      const int i = 4 * jj + wave;
+      const int i = C::kWv * jj + wave;
       if (i < C::kDma) {
         auto* dst = (__attribute__((address_space(3))) void*)&sT[buf][64 * i];
         if (i < C::kKcDma)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kc, dst, 16, dma_off[jj] + k0 * 64, 0, 0, 0);
         else if (i < C::kKcDma + C::kKpDma)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kp, dst, 16, dma_off[jj] + k0 * rp * 2, 0, 0, 0);
-        else
+        else if (i < C::kKcDma + C::kKpDma + C::kVDma)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, dst, 16, dma_off[jj] + k0 * 2, 0, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_i, dst, 16, dma_off[jj] + k0 * 4, 0, 0, 0);
       }
     }
   };
@@ -240,6 +285,32 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   };
   auto vfrag = [&](int buf, int sub, int s) {
     return __builtin_bit_cast(bf16x8, sT[buf][C::kVOff + l32 * C::kVRow + 4 * sub + 2 * s + half]);
+  };
+  // RPB: the log2-domain bias of the lane's 16 accumulator rows (keys 8(v/4) + 4h + v%4 of
+  // subtile sub) for both column blocks, gathered from the LDS table ...
+  auto gather_bias = [&](int buf, int sub, _Float16 (*bh)[16]) {
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const u32x4 k4 = sT[buf][C::kIdxOff + (sub * 32 + 8 * g4 + 4 * half) / 4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb)
+          bh[nb][4 * g4 + i] = *(const __attribute__((address_space(3))) _Float16*)(size_t)(tab_base[nb] + k4[i]);
+    }
+  };
+  // ... and the score MFMA's accumulator init from it: bias + mneg, -inf for keys >= N
+  auto bias_cinit = [&](const _Float16 (*bh)[16], const float* mneg, int key0, f32x16* ci) {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) ci[nb][v] = (float)bh[nb][v] + mneg[nb];
+    if (key0 + 32 > N) {
+      const int kbase = key0 + 4 * half;
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (kbase + 8 * (v >> 2) + (v & 3) >= N) ci[0][v] = ci[1][v] = -INFINITY;
+    }
   };
   auto mask_tail = [&](f32x16* sc, int key0) {
     const int kbase = key0 + 4 * half;
@@ -269,15 +340,19 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   // slice of the exp / pack / row-sum work so both pipes stay busy within a
   // wave. Keys past N (last tile only) have zero K rows and zero V^T columns:
   // their P = exp2(-m) adds nothing to O and is subtracted from the row sum.
+  // With RPB the accumulator init carries each score's bias too (rebuilt per
+  // subtile) and padded keys start at -inf, so their P is zero.
   float pad_sub[2] = {0.f, 0.f};
   {
     f32x16 cinit[2];
+    const float mneg[2] = {-mref[0], -mref[1]};
+    _Float16 bh[2][16];
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         acc[nb][i] = 0.f;
-        cinit[nb][i] = -mref[nb];
+        cinit[nb][i] = mneg[nb];
       }
       m_run[nb] = mref[nb];
     }
@@ -303,7 +378,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     // read kf, the fragments of the next half step's subtile (nkbuf, nksub),
     // already in LDS, are fetched into kf so their latency hides behind the
     // rest of this half step.
-    auto half_step = [&](const f32x16* sc_in, bf16x8* kf, int nkbuf, int nksub, int vbuf, int vsub,
+    auto half_step = [&](const f32x16* sc_in, bf16x8* kf, int nkbuf, int nksub, int nkey0, int vbuf, int vsub,
                          f32x16* sc_out) {
       bf16x8 vf[2];
 #pragma unroll
@@ -346,18 +421,18 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       smfma(1, 1);
       pslice(0, 1, 0);
       __builtin_amdgcn_sched_barrier(0);
-      smfma(2, 0);
+      if constexpr (C::kSteps > 2) smfma(2, 0);
       rsmfma(0, 1);
       pslice(0, 1, 2);
       __builtin_amdgcn_sched_barrier(0);
-      smfma(2, 1);
 #pragma unroll
-      for (int s = 3; s < C::kSteps; ++s) {
-        smfma(s, 0);
+      for (int s = 2; s < C::kSteps; ++s) {
+        if (s > 2) smfma(s, 0);
         smfma(s, 1);
       }
       __builtin_amdgcn_sched_barrier(0);
       load_kf(nkbuf, nksub, kf);
+      if constexpr (RPB) gather_bias(nkbuf, nksub, bh);
       pslice(1, 1, 0);
       __builtin_amdgcn_sched_barrier(0);
       pvmfma(0, 0);
@@ -368,6 +443,7 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       pvmfma(1, 0);
       pvmfma(1, 1);
       rsmfma(1, 1);
+      if constexpr (RPB) bias_cinit(bh, mneg, nkey0, cinit);
       __builtin_amdgcn_sched_barrier(0);
     };
 
@@ -382,6 +458,10 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
     f32x16 sc_a[2], sc_b[2];
     bf16x8 kf[C::kSteps];
     load_kf(0, 0, kf);
+    if constexpr (RPB) {
+      gather_bias(0, 0, bh);
+      bias_cinit(bh, mneg, 0, cinit);
+    }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       sc_a[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[0], qf[nb][0], cinit[nb], 0, 0, 0);
@@ -390,11 +470,16 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
         sc_a[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[nb][s], sc_a[nb], 0, 0, 0);
     }
     load_kf(0, 1, kf);
+    if constexpr (RPB) {
+      gather_bias(0, 1, bh);
+      bias_cinit(bh, mneg, 32, cinit);
+    }
     for (int t = 0; t < nkt; ++t) {
       const int b0 = t % kBufs, b1 = (t + 1) % kBufs;
+      const int k1 = (t + 1) * kKeyTile;
       dma_tile(min(t + 3, nkt - 1), (t + 3) % kBufs);
-      half_step(sc_a, kf, b1, 0, b0, 0, sc_b);   // softmax (t, 0); scores (t, 1); prefetch K (t + 1, 0)
-      half_step(sc_b, kf, b1, 1, b0, 1, sc_a);   // softmax (t, 1); scores (t + 1, 0); prefetch K (t + 1, 1)
+      half_step(sc_a, kf, b1, 0, k1, b0, 0, sc_b);        // softmax (t, 0); scores (t, 1); prefetch (t + 1, 0)
+      half_step(sc_b, kf, b1, 1, k1 + 32, b0, 1, sc_a);   // softmax (t, 1); scores (t + 1, 0); prefetch (t + 1, 1)
       dma_wait_older();                          // tile t + 2 landed (this wave's part)
       barrier_dma();
     }
@@ -403,7 +488,8 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
       // query l32 of block nb: row l32 / 16 of lane l32 % 16; kept on half 0
       const float r0 = __shfl(lsum[nb][0], l32 & 15), r1 = __shfl(lsum[nb][1], l32 & 15);
       l_run[nb] = half == 0 ? (l32 < 16 ? r0 : r1) : 0.f;
-      pad_sub[nb] = (float)(nkt * kKeyTile - N) * (float)f32_to_bf16(__builtin_amdgcn_exp2f(-mref[nb]));
+      if constexpr (!RPB)
+        pad_sub[nb] = (float)(nkt * kKeyTile - N) * (float)f32_to_bf16(__builtin_amdgcn_exp2f(-mref[nb]));
     }
   }
 
@@ -441,10 +527,17 @@ __global__ __launch_bounds__(256, 2) void attn_fwd_bf16_kernel(FwdArgs a) {
         bf16x8 kf[C::kSteps];
         load_kf(buf, sub, kf);
         f32x16 sc[2];
+        if constexpr (RPB) {
+          _Float16 bh[2][16];
+          const float zero[2] = {0.f, 0.f};
+          gather_bias(buf, sub, bh);
+          bias_cinit(bh, zero, t * kKeyTile + sub * 32, sc);
+        }
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
+          if constexpr (!RPB)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sc[nb][i] = 0.f;
+            for (int i = 0; i < 16; ++i) sc[nb][i] = 0.f;
 #pragma unroll
           for (int s = 0; s < C::kSteps; ++s)
             sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[nb][s], sc[nb], 0, 0, 0);
@@ -540,6 +633,39 @@ __global__ __launch_bounds__(kKeyBoundTile) void key_bound_kernel(int N, int n_r
   }
 }
 
+// RPB preparation. Block h < heads converts table row h to fp16 in log2 units
+// (zero-padded to `stride` entries) and writes its maximum; block `heads`
+// writes the per-key byte offsets -2 ((k / w)(2w - 1) + k % w) for k < N and
+// 0 for the padded rows.
+__global__ __launch_bounds__(256) void rpb_prep_kernel(const float* __restrict__ table, int heads, int entries,
+                                                       int stride, int w, int N, int n_rows,
+                                                       _Float16* __restrict__ tab16, float* __restrict__ tmax,
+                                                       int* __restrict__ kidx) {
+  __shared__ float red[4];
+  if ((int)blockIdx.x < heads) {
+    const float* src = table + (int64_t)blockIdx.x * entries;
+    _Float16* dst = tab16 + (int64_t)blockIdx.x * stride;
+    constexpr float kLog2e = 1.44269504088896340736f;
+    float mx = -INFINITY;
+    for (int i = threadIdx.x; i < stride; i += 256) {
+      _Float16 h = (_Float16)0.f;
+      if (i < entries) {
+        h = (_Float16)(src[i] * kLog2e);
+        mx = fmaxf(mx, (float)h);
+      }
+      dst[i] = h;
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) tmax[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  } else {
+    const int w2 = 2 * w - 1;
+    for (int t = threadIdx.x; t < n_rows; t += 256) kidx[t] = t < N ? -2 * ((t / w) * w2 + t % w) : 0;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // float32 kernel: one thread per query, K/V tiles of 64 keys in LDS, exact
 // online softmax per tile. Used for float32 runs (correctness-sized work).
@@ -632,8 +758,36 @@ hipError_t launch_key_bound(const FwdArgs& a, hipStream_t stream) {
 
 int key_bound_parts(int N) { return (N + kKeyBoundTile - 1) / kKeyBoundTile; }
 
+int rpb_table_stride(int w) {
+  const int entries = (2 * w - 1) * (2 * w - 1);
+  return (entries + 511) / 512 * 512;
+}
+
+size_t rpb_fwd_lds_bytes(int w) {
+  // tile ring + table + a margin for the compiler's own static LDS (256 bytes today)
+  return sizeof(u32x4) * kBufs * FwdCfg<0, true>::kChunks + 2 * (size_t)rpb_table_stride(w) + 512;
+}
+
+hipError_t launch_rpb_prep(const Geom& g, const float* table, _Float16* tab16, float* tmax, int* kidx,
+                           hipStream_t stream) {
+  const int entries = (2 * g.w - 1) * (2 * g.w - 1);
+  hipLaunchKernelGGL(rpb_prep_kernel, dim3(g.heads + 1), dim3(256), 0, stream, table, g.heads, entries,
+                     rpb_table_stride(g.w), g.w, g.N, g.n_rows, tab16, tmax, kidx);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd_rpb(const FwdArgs& a, hipStream_t stream) {
+  typedef FwdCfg<0, true> C;
+  const int nqb = (a.g.N + C::kQPerBlock - 1) / C::kQPerBlock;
+  const int64_t blocks = (int64_t)a.g.units * nqb;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_fwd_bf16_kernel<0, true>), dim3((unsigned)blocks), dim3(64 * C::kWv),
+                     2 * (size_t)a.rpb_stride, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
-  const int nqb = (a.g.N + kQPerBlock - 1) / kQPerBlock;
+  const int nqb = (a.g.N + FwdCfg<1>::kQPerBlock - 1) / FwdCfg<1>::kQPerBlock;
   const int64_t blocks = (int64_t)a.g.units * nqb;
   if (blocks == 0) return hipSuccess;
   if (a.rp == 16)

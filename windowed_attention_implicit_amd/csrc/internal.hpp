@@ -55,13 +55,25 @@ struct FwdArgs {
   void* o_map;          // bf16 path: O in the [B, H, W, heads, 32] map
   float* lse;           // [B,H,W,heads] or nullptr
   float* kmax2;         // [units][key_bound_parts(N)] partial maxima of |[k_c | k_p]|^2 (bf16 path)
-  int rp;               // padded rank, 16 or 32
+  int rp;               // padded rank, 16 or 32 (0: the RPB comparison kernel)
+  // RPB comparison kernel only (from launch_rpb_prep)
+  const _Float16* rpb_tab16 = nullptr;  // [heads][rpb_stride] table * log2(e), fp16, zero-padded
+  const float* rpb_max = nullptr;       // [heads] maximum of each fp16 row
+  const int* rpb_kidx = nullptr;        // [n_rows] per-key LDS byte offsets into the table
+  int rpb_stride = 0;                   // rpb_table_stride(w)
 };
 // Per-unit key-norm bound used by the bf16 forward (reads kw and kp, writes kmax2).
 hipError_t launch_key_bound(const FwdArgs& a, hipStream_t stream);
 int key_bound_parts(int N);
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream);
+// RPB comparison kernel: table [heads][(2w-1)^2] float32 -> fp16 log2-unit rows,
+// row maxima and per-key offsets; then the attention (K/V windowed as for bf16).
+int rpb_table_stride(int w);
+size_t rpb_fwd_lds_bytes(int w);
+hipError_t launch_rpb_prep(const Geom& g, const float* table, _Float16* tab16, float* tmax, int* kidx,
+                           hipStream_t stream);
+hipError_t launch_attn_fwd_rpb(const FwdArgs& a, hipStream_t stream);
 
 struct BwdArgs {
   Geom g;
