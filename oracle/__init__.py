@@ -31,4 +31,7 @@ from .rib import (  # noqa: F401
     rpb_bias,
     rpb_attention_window_fwd,
     rpb_window_attn_fwd,
+    cla_depthwise3x3,
+    cla_gate,
+    cla_apply,
 )

@@ -42,6 +42,14 @@ Readings where the pages are silent (each is also listed in the design notes):
   R16 the position MLP is trained with the network: the positional gradients
       dQ_p, dK_p continue through Linear -> GELU -> Linear into dW1, db1,
       dW2, db2 by the chain rule; GELU'(z) = Phi(z) + z phi(z) (erf form, R5)
+  R18 the CLA gate (depth-wise 3x3 conv, point-wise 1x1 conv, sigmoid -> G,
+      O' = O * G): its input X is the attention block's input map
+      [B, H, W, C] with C = heads * d_c channels; both convs carry a bias;
+      the 3x3 conv is a cross-correlation over the whole map (not per window)
+      with zero padding 1 ("same" size); tap w_dw[c, ky, kx] weights
+      X[y + ky - 1, x + kx - 1, c]; the 1x1 conv is Z = D W_pw^T + b_pw with
+      W_pw [C_out, C_in]; channel c of G gates head c // d_c, channel
+      c % d_c of O
 
 Parity pins live in ``tests/test_oracle_*.py`` (closed forms, invariants,
 library routines, brute force and hand-derived fixtures in ``tests/golden/``).
@@ -60,6 +68,7 @@ __all__ = [
     "rib_window_attn_fwd", "rib_window_attn_bwd", "default_scale",
     "gelu_grad", "posgen_bwd",
     "rpb_bias", "rpb_attention_window_fwd", "rpb_window_attn_fwd",
+    "cla_depthwise3x3", "cla_gate", "cla_apply",
 ]
 
 
@@ -423,3 +432,53 @@ def rib_window_attn_bwd(q_c, k_c, v, q_p, k_p, d_o, w: int, scale: float | None 
         dqp += g[3]
         dkp += g[4]
     return dQ, dK, dV, dqp, dkp
+
+
+# ----------------------------------------------------------------------------
+# Convolutional local attention (CLA) gate
+# ----------------------------------------------------------------------------
+
+def cla_depthwise3x3(x, w_dw, b_dw=None) -> np.ndarray:
+    """Depth-wise 3x3 convolution of a [B, H, W, C] map, zero padding 1 (R18): the first stage of the
+    CLA path [EN §2.B; ZH §2.B: a 3x3 depth-wise conv]. D[y, x, c] = b[c] + sum_{ky, kx}
+    w_dw[c, ky, kx] X[y + ky - 1, x + kx - 1, c], taps outside the map reading 0."""
+    x = np.asarray(x, dtype=np.float64)
+    B, H, W, C = x.shape
+    w_dw = np.asarray(w_dw, dtype=np.float64)
+    if w_dw.shape != (C, 3, 3):
+        raise ValueError("w_dw must be [C, 3, 3]")
+    xp = np.zeros((B, H + 2, W + 2, C))
+    xp[:, 1:H + 1, 1:W + 1, :] = x
+    d = np.zeros((B, H, W, C))
+    for ky in range(3):
+        for kx in range(3):
+            d += w_dw[:, ky, kx] * xp[:, ky:ky + H, kx:kx + W, :]
+    if b_dw is not None:
+        d += np.asarray(b_dw, dtype=np.float64)
+    return d
+
+
+def cla_gate(x, w_dw, b_dw, w_pw, b_pw) -> np.ndarray:
+    """Gating map G = sigmoid(PW_1x1(DW_3x3(X))) of the CLA path [EN §2.B: depth-wise conv, point-wise
+    conv, sigmoid -> gating map; DE §2.B: G; ZH §2.B: 3x3 depth-wise, 1x1 point-wise] on a [B, H, W, C]
+    map (R18). Returns G [B, H, W, C] (float64)."""
+    d = cla_depthwise3x3(x, w_dw, b_dw)
+    w_pw = np.asarray(w_pw, dtype=np.float64)
+    C = d.shape[-1]
+    if w_pw.shape != (C, C):
+        raise ValueError("w_pw must be [C, C]")
+    z = d @ w_pw.T
+    if b_pw is not None:
+        z += np.asarray(b_pw, dtype=np.float64)
+    return 1.0 / (1.0 + np.exp(-z))
+
+
+def cla_apply(o, g) -> np.ndarray:
+    """O' = O * G [DE §2.B]: the attention output [B, H, W, heads, d_c] gated element-wise by
+    G [B, H, W, heads * d_c], channel c of G on head c // d_c, channel c % d_c of O (R18)."""
+    o = np.asarray(o, dtype=np.float64)
+    B, H, W, heads, d_c = o.shape
+    g = np.asarray(g, dtype=np.float64)
+    if g.shape != (B, H, W, heads * d_c):
+        raise ValueError("g must be [B, H, W, heads * d_c]")
+    return o * g.reshape(B, H, W, heads, d_c)

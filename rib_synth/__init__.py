@@ -174,6 +174,25 @@ def make_rpb_table(heads: int, w: int, seed: int, std: float = 1.0) -> np.ndarra
     return (std * rng.standard_normal((heads, (2 * w - 1) ** 2))).astype(np.float32)
 
 
+def make_cla(C: int, seed: int) -> dict:
+    """CLA gate weights (float32): depth-wise taps w_dw [C, 3, 3] ~ N(0, (1/3)^2) and bias b_dw [C],
+    point-wise w_pw [C_out, C_in] ~ N(0, 1/C) and bias b_pw [C] (biases N(0, 0.1^2)), i.e. fan-in
+    scaled so that the gate's pre-activation of an N(0, 1) map is of order 1."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return {
+        "w_dw": (rng.standard_normal((C, 3, 3)) / 3.0).astype(np.float32),
+        "b_dw": (0.1 * rng.standard_normal(C)).astype(np.float32),
+        "w_pw": (rng.standard_normal((C, C)) / np.sqrt(C)).astype(np.float32),
+        "b_pw": (0.1 * rng.standard_normal(C)).astype(np.float32),
+    }
+
+
+def make_map(B: int, H: int, W: int, C: int, dtype: str, seed: int) -> Tensor:
+    """A [B, H, W, C] N(0, 1) feature map (the CLA gate's input X)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return _activation(rng, (B, H, W, C), dtype)
+
+
 def custom_workload(B, H, W, heads, d_c, w, r, dtype="bf16", backward=False, seed=0,
                     n_freq=N_FREQ, hidden=HIDDEN) -> Workload:
     """A workload of arbitrary shape (small and ragged test cases)."""

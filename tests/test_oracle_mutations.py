@@ -16,6 +16,7 @@ import test_oracle_attention as ta
 import test_oracle_posgen as tp
 import test_oracle_posgen_bwd as tb
 import test_oracle_rpb as tr
+import test_oracle_cla as tc
 
 
 def _golden():
@@ -155,6 +156,30 @@ def _rpb_fwd_scaled_bias(qc, kc, v, bias, scale):
     return orib.__dict__["_orig_rpb_fwd"](qc, kc, v, scale * np.asarray(bias), scale)
 
 
+def _cla_dw_flipped(x, w_dw, b_dw=None):
+    return orib.__dict__["_orig_cla_dw"](x, np.asarray(w_dw)[:, ::-1, ::-1], b_dw)   # convolution, not correlation
+
+
+def _cla_dw_wraparound(x, w_dw, b_dw=None):
+    x = np.asarray(x, dtype=np.float64)
+    w_dw = np.asarray(w_dw, dtype=np.float64)
+    d = np.zeros(x.shape)
+    for ky in range(3):
+        for kx in range(3):
+            d += w_dw[:, ky, kx] * np.roll(x, (1 - ky, 1 - kx), axis=(1, 2))
+    return d if b_dw is None else d + np.asarray(b_dw)
+
+
+def _cla_gate_pw_transposed(x, w_dw, b_dw, w_pw, b_pw):
+    return orib.__dict__["_orig_cla_gate"](x, w_dw, b_dw, np.asarray(w_pw).T, b_pw)
+
+
+def _cla_apply_channels_transposed(o, g):
+    o = np.asarray(o, dtype=np.float64)
+    B, H, W, heads, d_c = o.shape
+    return o * np.asarray(g).reshape(B, H, W, d_c, heads).swapaxes(3, 4)
+
+
 MUTATIONS = [
     ("concat_scores", _scores_no_bias, [(ta.test_worked_example_w2, "golden"), (ta.test_concat_identity,)]),
     ("concat_scores", _scores_transposed_bias, [(ta.test_concat_identity,), (ta.test_matches_torch_sdpa_with_additive_bias,)]),
@@ -176,6 +201,10 @@ MUTATIONS = [
     ("rpb_bias", _rpb_bias_reversed, [(tr.test_rpb_bias_brute_force, 3), (tr.test_rpb_linear_table_equals_rib_with_rank3_tokens,)]),
     ("rpb_bias", _rpb_bias_xy_swapped, [(tr.test_rpb_bias_brute_force, 3), (tr.test_rpb_linear_table_equals_rib_with_rank3_tokens,)]),
     ("rpb_attention_window_fwd", _rpb_fwd_scaled_bias, [(tr.test_rpb_matches_torch_sdpa_with_additive_mask,), (tr.test_rpb_linear_table_equals_rib_with_rank3_tokens,)]),
+    ("cla_depthwise3x3", _cla_dw_flipped, [(tc.test_cla_matches_torch_conv2d, 2, 7, 9, 12), (tc.test_cla_brute_force_pixels,)]),
+    ("cla_depthwise3x3", _cla_dw_wraparound, [(tc.test_cla_constant_map_border_counts,), (tc.test_cla_brute_force_pixels,)]),
+    ("cla_gate", _cla_gate_pw_transposed, [(tc.test_cla_matches_torch_conv2d, 2, 7, 9, 12), (tc.test_cla_brute_force_pixels,)]),
+    ("cla_apply", _cla_apply_channels_transposed, [(tc.test_cla_apply_channel_mapping,)]),
 ]
 
 
@@ -184,7 +213,8 @@ def test_planted_mistake_is_caught(monkeypatch, name, bad, pins):
     orig = getattr(orib, name)
     for key, fn in (("_orig_bwd", orib.attention_window_bwd), ("_orig_fourier", orib.fourier_features),
                     ("_orig_posgen", orib.posgen), ("_orig_partition", orib.window_partition),
-                    ("_orig_posgen_bwd", orib.posgen_bwd), ("_orig_rpb_fwd", orib.rpb_attention_window_fwd)):
+                    ("_orig_posgen_bwd", orib.posgen_bwd), ("_orig_rpb_fwd", orib.rpb_attention_window_fwd),
+                    ("_orig_cla_dw", orib.cla_depthwise3x3), ("_orig_cla_gate", orib.cla_gate)):
         monkeypatch.setitem(orib.__dict__, key, fn)
     monkeypatch.setattr(orib, name, bad)
     monkeypatch.setattr(oracle, name, bad)
