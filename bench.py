@@ -261,6 +261,63 @@ def rpb_compare(wl, x, dev, steps: int, rib_attn_ms: float):
             "materialized_bias_bytes_bf16": wl.heads * wl.N * wl.N * 2}
 
 
+def cla_measure(wl, x, step, dev, steps: int):
+    """The CLA gate on the headline map (C = heads * d_c = 192) and the forward with O' = O * G fused into
+    the attention kernel's output stage."""
+    import torch
+    import rib_synth
+    import windowed_attention_implicit_amd as rib
+    C = wl.heads * wl.d_c
+    xm = to_gpu(rib_synth.make_map(wl.B, wl.H, wl.W, C, "bf16", seed=192), dev)
+    w = {k: torch.from_numpy(v).to(dev) for k, v in rib_synth.make_cla(C, seed=193).items()}
+    g = rib.cla_gate(xm, w["w_dw"], w["b_dw"], w["w_pw"], w["b_pw"], wl.heads)
+    plan = step.plan
+    q, k, v, qp, kp = plan.inputs
+    o_gated = torch.empty_like(plan.o)
+    L = rib.lib()
+
+    def gate():
+        rib.cla_gate(xm, w["w_dw"], w["b_dw"], w["w_pw"], w["b_pw"], wl.heads, out=g)
+
+    def gated():
+        rib._check(L.rib_window_attn_fwd_gated(ctypes.byref(plan.shape), plan.dtype, plan.scale, rib._ptr(q),
+                                               rib._ptr(k), rib._ptr(v), rib._ptr(qp), rib._ptr(kp), rib._ptr(g),
+                                               rib._ptr(o_gated), rib._ptr(plan.lse), rib._ptr(plan.ws),
+                                               plan.ws_bytes, rib._stream(dev)))
+
+    def reset():
+        for grp in rib.KERNEL_GROUPS:
+            rib.kernel_timing_read(grp)
+
+    rib.kernel_timing_enable(True)
+    time_steps(gate, steps, 3, reset)
+    gate_ms, _ = kernel_avg_ms(rib, "cla_gate")
+    # gated and ungated launches alternate, so both see the same clock and cache state
+    for _ in range(3):
+        plan.run()
+        gated()
+    torch.cuda.synchronize()
+    reset()
+    t_plain = t_gated = 0.0
+    for _ in range(steps):
+        plan.run()
+        t_plain += rib.kernel_timing_read("attn_fwd")[0]
+        gated()
+        t_gated += rib.kernel_timing_read("attn_fwd")[0]
+    rib.kernel_timing_enable(False)
+    gated_ms, rib_attn_ms = t_gated / steps, t_plain / steps
+    tensor_bytes = wl.B * wl.H * wl.W * C * 2
+    pixels = wl.B * wl.H * wl.W
+    flops = pixels * (2 * 9 * C + 2 * C * C)
+    return {"workload": f"gate of a [{wl.B}, {wl.H}, {wl.W}, {C}] bf16 map; gated forward on the headline inputs",
+            "gate_kernel_ms": gate_ms and round(gate_ms, 5),
+            "gate_GB/s": gate_ms and round(2 * tensor_bytes / gate_ms / 1e6, 1),
+            "gate_frac_hbm": gate_ms and round(2 * tensor_bytes / gate_ms / 1e6 / PEAK_HBM_GBS, 3),
+            "gate_tflops": gate_ms and round(flops / gate_ms / 1e9, 1),
+            "gated_attn_kernel_ms": round(gated_ms, 4),
+            "ungated_attn_kernel_ms_same_loop": round(rib_attn_ms, 4)}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -373,6 +430,9 @@ def main():
         b.copy_(a)
         torch.cuda.synchronize()
         result["calibration_copy_bytes"] = 2 * n * 4
+
+    print("bench: CLA gate", file=sys.stderr, flush=True)
+    result["cla"] = cla_measure(wl, x, step, dev, max(10, args.steps // 2))
 
     if not args.no_rpb:
         print("bench: RPB comparison kernel", file=sys.stderr, flush=True)

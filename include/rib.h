@@ -139,6 +139,46 @@ rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
                                  void* workspace, size_t workspace_bytes,
                                  rib_stream_t stream);
 
+/*
+ * rib_cla_gate - the gating map of convolutional local attention (CLA) [EN §2.B: a
+ * depth-wise conv, a point-wise conv and a sigmoid produce a map that modulates the
+ * attention output; DE §2.B: G, O' = O (.) G; ZH §2.B: 3x3 depth-wise, 1x1 point-wise].
+ *
+ * On the map X [B, H, W, C], C = heads * d_c:
+ *   D[y, x, c] = b_dw[c] + sum_{ky, kx in 0..2} w_dw[c, ky, kx] X[y + ky - 1, x + kx - 1, c]
+ *                (cross-correlation over the whole map, zero outside it),
+ *   G[y, x, o] = sigmoid(b_pw[o] + sum_c w_pw[o, c] D[y, x, c]).
+ * Channel c of G lines up with head c / d_c, channel c % d_c of an attention output in
+ * [B, H, W, heads, d_c] (rib_window_attn_fwd_gated). The bf16 path rounds D and the
+ * point-wise weights to bf16 for the matrix cores and accumulates in float32.
+ *
+ *   shape        B, H, W, heads, d_c are used (w and r are ignored); C must be a
+ *                multiple of 32 in [32, 256] (RIB_ERR_UNSUPPORTED otherwise)
+ *   x            (device) [B, H, W, C], dtype
+ *   w_dw, b_dw   (device) float32 [C, 3, 3] and [C] (b_dw may be NULL for zeros)
+ *   w_pw, b_pw   (device) float32 [C, C] (out, in) and [C] (b_pw may be NULL)
+ *   g            (device) output [B, H, W, C], dtype
+ * No workspace. Errors as for rib_window_attn_fwd.
+ */
+rib_status_t rib_cla_gate(const rib_shape_t* shape, rib_dtype_t dtype, const void* x,
+                          const float* w_dw, const float* b_dw, const float* w_pw,
+                          const float* b_pw, void* g, rib_stream_t stream);
+
+/*
+ * rib_window_attn_fwd_gated - rib_window_attn_fwd followed by the CLA modulation
+ * O' = O (.) G [DE §2.B], fused into the attention kernel's output stage (no extra pass
+ * over O). `gate` (device, required) is [B, H, W, heads, d_c] in dtype, e.g. the output of
+ * rib_cla_gate; `o` receives O'; `lse` (optional) is that of the ungated attention.
+ * Workspace: rib_fwd_workspace_size(). This is a forward (inference) entry: training
+ * needs the ungated O for the backward, so it calls rib_window_attn_fwd and gates apart.
+ */
+rib_status_t rib_window_attn_fwd_gated(const rib_shape_t* shape, rib_dtype_t dtype, float scale,
+                                       const void* q_c, const void* k_c, const void* v,
+                                       const void* q_p, const void* k_p, const void* gate,
+                                       void* o, float* lse,
+                                       void* workspace, size_t workspace_bytes,
+                                       rib_stream_t stream);
+
 /* Bytes of device workspace rib_window_attn_bwd needs (0 when invalid). */
 size_t rib_bwd_workspace_size(const rib_shape_t* shape, rib_dtype_t dtype);
 
@@ -257,7 +297,8 @@ typedef enum {
   RIB_KERNEL_POS_REDUCE = 7,   /* the fixed-order sum of the dQ_p / dK_p partials */
   RIB_KERNEL_POSGEN_BWD = 8,   /* the position-MLP weight-gradient kernels (partials + sum) */
   RIB_KERNEL_RPB_ATTN_FWD = 9, /* the RPB comparison attention kernel alone */
-  RIB_KERNEL_COUNT = 10
+  RIB_KERNEL_CLA_GATE = 10,    /* the CLA gate kernel */
+  RIB_KERNEL_COUNT = 11
 } rib_kernel_t;
 
 rib_status_t rib_kernel_timing_enable(int32_t enable);

@@ -117,6 +117,32 @@ def test_rpb_validation(L):
     assert call(rib.Shape(0, 192, 192, 6, 32, 96, 0), nulls=(0, 1, 2), ws=None, ws_bytes=0, table=None) == rib.RIB_OK
 
 
+def test_cla_validation(L):
+    good = rib.Shape(2, 192, 192, 6, 32, 96, 16)
+
+    def gate(shape, dtype=rib.RIB_BF16, x=FAKE, w_dw=FAKE, w_pw=FAKE, g=FAKE):
+        return L.rib_cla_gate(ctypes.byref(shape), dtype, x, w_dw, None, w_pw, None, g, None)
+
+    assert gate(rib.Shape(1, 8, 8, 9, 32, 2, 1)) == rib.RIB_ERR_UNSUPPORTED      # C = 288 > 256
+    assert b"multiples of 32" in L.rib_last_error()
+    assert gate(rib.Shape(1, 8, 8, 3, 16, 2, 1)) == rib.RIB_ERR_UNSUPPORTED      # C = 48
+    assert gate(rib.Shape(1, 0, 8, 2, 32, 2, 1)) == rib.RIB_ERR_INVALID_ARG
+    assert gate(good, dtype=5) == rib.RIB_ERR_INVALID_ARG
+    assert gate(good, w_dw=None) == rib.RIB_ERR_INVALID_ARG
+    assert gate(good, g=MISALIGNED) == rib.RIB_ERR_INVALID_ARG
+    assert gate(rib.Shape(0, 8, 8, 2, 32, 2, 1), x=None, g=None) == rib.RIB_OK
+    # the gated forward validates like the plain forward and requires the gate
+    need = L.rib_fwd_workspace_size(ctypes.byref(good), rib.RIB_BF16)
+    args = [FAKE] * 5
+    assert L.rib_window_attn_fwd_gated(ctypes.byref(good), rib.RIB_BF16, 0.0, *args, None, FAKE, None, FAKE, need,
+                                       None) == rib.RIB_ERR_INVALID_ARG
+    assert b"gate" in L.rib_last_error()
+    assert L.rib_window_attn_fwd_gated(ctypes.byref(good), rib.RIB_BF16, 0.0, *args, MISALIGNED, FAKE, None, FAKE,
+                                       need, None) == rib.RIB_ERR_INVALID_ARG
+    assert L.rib_window_attn_fwd_gated(ctypes.byref(good), rib.RIB_BF16, 0.0, *args, FAKE, FAKE, None, FAKE,
+                                       need - 1, None) == rib.RIB_ERR_WORKSPACE
+
+
 def test_bwd_validation(L):
     good = rib.Shape(2, 192, 192, 6, 32, 64, 16)
     need = L.rib_bwd_workspace_size(ctypes.byref(good), rib.RIB_BF16)

@@ -9,7 +9,8 @@ Entry points (same names as the C ABI, without the ``rib_`` prefix):
   posgen, posgen_bwd, window_partition, window_unpartition, window_attn_fwd,
   window_attn_bwd, fwd_workspace_size, bwd_workspace_size,
   rpb_window_attn_fwd, rpb_fwd_workspace_size (the relative-position-bias
-  comparison kernel)
+  comparison kernel), cla_gate, window_attn_fwd_gated (the CLA gating map and
+  the forward with O' = O * G fused into its output stage)
 plus ``FwdPlan`` / ``BwdPlan`` / ``RpbFwdPlan``, which preallocate workspace
 and outputs so a call can be repeated without allocating.
 """
@@ -28,6 +29,7 @@ __all__ = [
     "posgen", "posgen_bwd", "window_partition", "window_unpartition", "window_attn_fwd", "window_attn_bwd",
     "fwd_workspace_size", "bwd_workspace_size", "FwdPlan", "BwdPlan", "Shape",
     "rpb_window_attn_fwd", "rpb_fwd_workspace_size", "RpbFwdPlan",
+    "cla_gate", "window_attn_fwd_gated",
     "KERNEL_GROUPS", "kernel_timing_enable", "kernel_timing_read",
 ]
 
@@ -69,6 +71,8 @@ _SIGS = {
     "rib_window_attn_fwd": (_i32, [ctypes.POINTER(Shape), _i32, _f32] + [_vp] * 7 + [_vp, _sz, _vp]),
     "rib_window_attn_bwd": (_i32, [ctypes.POINTER(Shape), _i32, _f32] + [_vp] * 13 + [_vp, _sz, _vp]),
     "rib_rpb_fwd_workspace_size": (_sz, [ctypes.POINTER(Shape), _i32]),
+    "rib_cla_gate": (_i32, [ctypes.POINTER(Shape), _i32] + [_vp] * 6 + [_vp]),
+    "rib_window_attn_fwd_gated": (_i32, [ctypes.POINTER(Shape), _i32, _f32] + [_vp] * 8 + [_vp, _sz, _vp]),
     "rib_rpb_window_attn_fwd": (_i32, [ctypes.POINTER(Shape), _i32, _f32] + [_vp] * 6 + [_vp, _sz, _vp]),
     "rib_kernel_timing_enable": (_i32, [_i32]),
     "rib_kernel_timing_read": (_i32, [_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
@@ -247,6 +251,45 @@ def window_attn_fwd(q_c, k_c, v, q_p, k_p, w: int, scale: float | None = None, w
     return FwdPlan(q_c, k_c, v, q_p, k_p, w, scale, want_lse).run()
 
 
+def window_attn_fwd_gated(q_c, k_c, v, q_p, k_p, gate, w: int, scale: float | None = None,
+                          want_lse: bool = True):
+    """O' = O * G with O the RIB attention output; ``gate`` [B, H, W, heads, d_c] (or [B, H, W, C]) in the
+    activations' dtype, e.g. from ``cla_gate``. Returns (O', LSE of the ungated attention or None)."""
+    plan = FwdPlan(q_c, k_c, v, q_p, k_p, w, scale, want_lse)
+    _require_gpu(gate)
+    if gate.dtype != q_c.dtype or gate.numel() != q_c.numel():
+        raise ValueError("gate must match the feature map's dtype and size")
+    _check(lib().rib_window_attn_fwd_gated(ctypes.byref(plan.shape), plan.dtype, plan.scale, _ptr(q_c), _ptr(k_c),
+                                           _ptr(v), _ptr(q_p), _ptr(k_p), _ptr(gate), _ptr(plan.o), _ptr(plan.lse),
+                                           _ptr(plan.ws), plan.ws_bytes, _stream(q_c.device)))
+    return plan.o, plan.lse
+
+
+def cla_gate(x: torch.Tensor, w_dw: torch.Tensor, b_dw, w_pw: torch.Tensor, b_pw, heads: int,
+             out: torch.Tensor | None = None) -> torch.Tensor:
+    """CLA gating map G = sigmoid(PW_1x1(DW_3x3(X))) of a [B, H, W, C] map (C = heads * d_c); returns G
+    [B, H, W, C] in x's dtype (written into ``out`` when given). Weights float32: w_dw [C, 3, 3],
+    b_dw [C] or None, w_pw [C, C], b_pw [C] or None."""
+    _require_gpu(x, w_dw, b_dw, w_pw, b_pw, out)
+    if x.dim() != 4:
+        raise ValueError("x is [B, H, W, C]")
+    B, H, W, C = x.shape
+    if C % heads:
+        raise ValueError("C must be a multiple of heads")
+    for t in (w_dw, b_dw, w_pw, b_pw):
+        if t is not None and t.dtype != torch.float32:
+            raise TypeError("CLA weights are float32")
+    if w_dw.shape != (C, 3, 3) or w_pw.shape != (C, C):
+        raise ValueError("w_dw must be [C, 3, 3] and w_pw [C, C]")
+    s = Shape(B, H, W, heads, C // heads, 2, 1)
+    if out is not None and (out.dtype != x.dtype or out.shape != x.shape):
+        raise ValueError("out must match x's dtype and shape")
+    g = torch.empty_like(x) if out is None else out
+    _check(lib().rib_cla_gate(ctypes.byref(s), _dtype_code(x.dtype), _ptr(x), _ptr(w_dw), _ptr(b_dw), _ptr(w_pw),
+                              _ptr(b_pw), _ptr(g), _stream(x.device)))
+    return g
+
+
 class BwdPlan:
     """Preallocated backward call: workspace and the five gradients for one shape."""
 
@@ -324,7 +367,8 @@ def rpb_window_attn_fwd(q_c, k_c, v, table, w: int, scale: float | None = None, 
 
 
 KERNEL_GROUPS = {"posgen": 0, "partition": 1, "attn_fwd": 2, "unpartition": 3, "bwd_prep": 4,
-                 "attn_bwd_dkv": 5, "attn_bwd_dq": 6, "pos_reduce": 7, "posgen_bwd": 8, "rpb_attn_fwd": 9}
+                 "attn_bwd_dkv": 5, "attn_bwd_dq": 6, "pos_reduce": 7, "posgen_bwd": 8, "rpb_attn_fwd": 9,
+                 "cla_gate": 10}
 
 
 def kernel_timing_enable(enable: bool = True):

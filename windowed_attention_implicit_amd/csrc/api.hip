@@ -425,10 +425,11 @@ size_t rib_bwd_workspace_size(const rib_shape_t* shape, rib_dtype_t dtype) {
   return bwd_layout(g, dtype, nullptr).bytes;
 }
 
-rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, float scale, const void* q_c,
-                                 const void* k_c, const void* v, const void* q_p, const void* k_p, void* o,
-                                 float* lse, void* workspace, size_t workspace_bytes, rib_stream_t stream) {
-  try {
+static rib_status_t attn_fwd_impl(const rib_shape_t* shape, rib_dtype_t dtype, float scale, const void* q_c,
+                                  const void* k_c, const void* v, const void* q_p, const void* k_p,
+                                  const void* gate, void* o, float* lse, void* workspace, size_t workspace_bytes,
+                                  rib_stream_t stream) {
+  {
     RIB_TRY(check_shape(shape, dtype, true));
     if (!(scale == scale) || isinf(scale)) return fail(RIB_ERR_INVALID_ARG, "scale is not finite");
     if (shape->B == 0) return ok();
@@ -438,6 +439,7 @@ rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
     RIB_TRY(check_ptr(q_p, "q_p"));
     RIB_TRY(check_ptr(k_p, "k_p"));
     RIB_TRY(check_ptr(o, "o"));
+    if (gate) RIB_TRY(check_ptr(gate, "gate"));
     if (lse && ((uintptr_t)lse & 3u)) return fail(RIB_ERR_INVALID_ARG, "lse is not 4-byte aligned");
     Geom g = make_geom(*shape);
     const size_t need = fwd_layout(g, dtype, nullptr).bytes;
@@ -467,6 +469,7 @@ rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
     a.lse = lse;
     a.kmax2 = L.kmax2;
     a.rp = rp;
+    a.gate = gate;
     if (dtype == RIB_BF16 && (e = launch_key_bound(a, st)) != hipSuccess) return hip_fail(e, "key bound");
     t_part.end();
     TimedGroup t_attn(RIB_KERNEL_ATTN_FWD, st);
@@ -479,8 +482,64 @@ rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
       t_unp.end();
     }
     return ok();
+  }
+}
+
+rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, float scale, const void* q_c,
+                                 const void* k_c, const void* v, const void* q_p, const void* k_p, void* o,
+                                 float* lse, void* workspace, size_t workspace_bytes, rib_stream_t stream) {
+  try {
+    return attn_fwd_impl(shape, dtype, scale, q_c, k_c, v, q_p, k_p, nullptr, o, lse, workspace, workspace_bytes,
+                         stream);
   } catch (...) {
     return fail(RIB_ERR_HIP, "unexpected C++ exception in rib_window_attn_fwd");
+  }
+}
+
+rib_status_t rib_window_attn_fwd_gated(const rib_shape_t* shape, rib_dtype_t dtype, float scale, const void* q_c,
+                                       const void* k_c, const void* v, const void* q_p, const void* k_p,
+                                       const void* gate, void* o, float* lse, void* workspace,
+                                       size_t workspace_bytes, rib_stream_t stream) {
+  try {
+    if (!gate) return fail(RIB_ERR_INVALID_ARG, "gate is NULL (use rib_window_attn_fwd for ungated attention)");
+    return attn_fwd_impl(shape, dtype, scale, q_c, k_c, v, q_p, k_p, gate, o, lse, workspace, workspace_bytes,
+                         stream);
+  } catch (...) {
+    return fail(RIB_ERR_HIP, "unexpected C++ exception in rib_window_attn_fwd_gated");
+  }
+}
+
+rib_status_t rib_cla_gate(const rib_shape_t* shape, rib_dtype_t dtype, const void* x, const float* w_dw,
+                          const float* b_dw, const float* w_pw, const float* b_pw, void* g, rib_stream_t stream) {
+  try {
+    if (!shape) return fail(RIB_ERR_INVALID_ARG, "shape is NULL");
+    if (!dtype_ok(dtype)) return fail(RIB_ERR_INVALID_ARG, "dtype %d is not RIB_F32 or RIB_BF16", (int)dtype);
+    if (shape->B < 0 || shape->H <= 0 || shape->W <= 0 || shape->heads <= 0 || shape->d_c <= 0)
+      return fail(RIB_ERR_INVALID_ARG, "B must be >= 0 and H, W, heads, d_c > 0");
+    const int64_t C64 = (int64_t)shape->heads * shape->d_c;
+    if (C64 > 4096 || !cla_channels_supported((int)C64))
+      return fail(RIB_ERR_UNSUPPORTED, "C = heads * d_c = %lld: the gate supports multiples of 32 up to 256",
+                  (long long)C64);
+    if ((int64_t)shape->B * shape->H * shape->W * C64 > ((int64_t)1 << 40))
+      return fail(RIB_ERR_UNSUPPORTED, "feature map too large");
+    if (shape->B == 0) return ok();
+    RIB_TRY(check_ptr(x, "x"));
+    RIB_TRY(check_ptr(g, "g"));
+    if (!w_dw || ((uintptr_t)w_dw & 3u)) return fail(RIB_ERR_INVALID_ARG, "w_dw is NULL or not 4-byte aligned");
+    if (!w_pw || ((uintptr_t)w_pw & 3u)) return fail(RIB_ERR_INVALID_ARG, "w_pw is NULL or not 4-byte aligned");
+    if (b_dw && ((uintptr_t)b_dw & 3u)) return fail(RIB_ERR_INVALID_ARG, "b_dw is not 4-byte aligned");
+    if (b_pw && ((uintptr_t)b_pw & 3u)) return fail(RIB_ERR_INVALID_ARG, "b_pw is not 4-byte aligned");
+    GateArgs a;
+    a.x = x; a.w_dw = w_dw; a.b_dw = b_dw; a.w_pw = w_pw; a.b_pw = b_pw; a.g = g;
+    a.B = shape->B; a.H = shape->H; a.W = shape->W; a.C = (int)C64;
+    hipStream_t st = (hipStream_t)stream;
+    TimedGroup t(RIB_KERNEL_CLA_GATE, st);
+    hipError_t e = launch_cla_gate(a, esize_of(dtype), st);
+    if (e != hipSuccess) return hip_fail(e, "cla gate");
+    t.end();
+    return ok();
+  } catch (...) {
+    return fail(RIB_ERR_HIP, "unexpected C++ exception in rib_cla_gate");
   }
 }
 

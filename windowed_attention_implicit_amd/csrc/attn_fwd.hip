@@ -111,7 +111,9 @@ struct BoolTag {
   static constexpr bool value = V;
 };
 
-template <int KP, bool RPB = false>
+// GATE: O' = O * G with G read in the map layout (its loads are issued before the key loop,
+// so their latency hides behind it)
+template <int KP, bool RPB = false, bool GATE = false>
 __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   typedef FwdCfg<KP, RPB> C;
   // Ring of kBufs tile buffers. While tile t is processed, tiles t and t + 1
@@ -197,6 +199,17 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
     }
     sq += swap_halves(sq);
     mref[nb] = sqrtf(sq) * kmax + bmax;
+  }
+  uint2 gpre[2][4];
+  if constexpr (GATE) {
+    const bf16* gmap = (const bf16*)a.gate;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int q = q0 + nb * 32 + l32;
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq)
+        gpre[nb][gq] = q < N ? *(const uint2*)(gmap + map_row(q) + 8 * gq + 4 * half) : make_uint2(0u, 0u);
+    }
   }
   // RPB: the bias of query q and key k is table[(w-1)(2w-1) + (w-1) + QI(q) - QI(k)] with
   // QI(t) = (t / w)(2w-1) + t % w. Per column block the lane keeps the LDS byte address of
@@ -575,7 +588,8 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
     }
   }
 
-  // ---- epilogue: normalize, write O rows (map layout) and LSE
+  // ---- epilogue: normalize, optionally gate (O' = O * G, G in the same map layout), write O
+  // rows (map layout) and the LSE of the ungated attention
   bf16* omap = (bf16*)a.o_map;
   const float kLn2 = 0.69314718055994530942f;
 #pragma unroll
@@ -586,10 +600,18 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
     if (q < N) {
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
+        const int64_t at = map_row(q) + 8 * gq + 4 * half;
+        float gv[4] = {inv, inv, inv, inv};
+        if constexpr (GATE) {
+          bf16 g4[4];
+          *(uint2*)g4 = gpre[nb][gq];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) gv[i] = inv * (float)g4[i];
+        }
         bf16 o4[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) o4[i] = f32_to_bf16(acc[nb][4 * gq + i] * inv);
-        *(uint2*)(omap + map_row(q) + 8 * gq + 4 * half) = *(const uint2*)o4;
+        for (int i = 0; i < 4; ++i) o4[i] = f32_to_bf16(acc[nb][4 * gq + i] * gv[i]);
+        *(uint2*)(omap + at) = *(const uint2*)o4;
       }
       if (a.lse && half == 0) a.lse[pm.pixel_head(unit, q)] = (m_run[nb] + log2f(l_tot)) * kLn2;
     }
@@ -737,12 +759,11 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   if (q < N) {
     float* ow = (float*)a.ow + (int64_t)unit * n_rows * D + (int64_t)q * D;
     const float inv = 1.f / l;
+    const PixelMap pm = make_pixel_map(g);
+    const float* gt = a.gate ? (const float*)a.gate + pm.pixel_head(unit, q) * D : nullptr;
 #pragma unroll
-    for (int i = 0; i < D; ++i) ow[i] = o[i] * inv;
-    if (a.lse) {
-      PixelMap pm = make_pixel_map(g);
-      a.lse[pm.pixel_head(unit, q)] = (m + log2f(l)) * 0.69314718055994530942f;
-    }
+    for (int i = 0; i < D; ++i) ow[i] = gt ? o[i] * inv * gt[i] : o[i] * inv;
+    if (a.lse) a.lse[pm.pixel_head(unit, q)] = (m + log2f(l)) * 0.69314718055994530942f;
   }
 }
 
@@ -790,10 +811,16 @@ hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   const int nqb = (a.g.N + FwdCfg<1>::kQPerBlock - 1) / FwdCfg<1>::kQPerBlock;
   const int64_t blocks = (int64_t)a.g.units * nqb;
   if (blocks == 0) return hipSuccess;
-  if (a.rp == 16)
+  if (a.gate) {
+    if (a.rp == 16)
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<1, false, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<2, false, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  } else if (a.rp == 16) {
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  else
+  } else {
     hipLaunchKernelGGL(attn_fwd_bf16_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 

@@ -61,6 +61,8 @@ struct FwdArgs {
   const float* rpb_max = nullptr;       // [heads] maximum of each fp16 row
   const int* rpb_kidx = nullptr;        // [n_rows] per-key LDS byte offsets into the table
   int rpb_stride = 0;                   // rpb_table_stride(w)
+  // optional CLA gate [B, H, W, heads, d_c] (same dtype as O): O' = O * G in the epilogue
+  const void* gate = nullptr;
 };
 // Per-unit key-norm bound used by the bf16 forward (reads kw and kp, writes kmax2).
 hipError_t launch_key_bound(const FwdArgs& a, hipStream_t stream);
@@ -74,6 +76,19 @@ size_t rpb_fwd_lds_bytes(int w);
 hipError_t launch_rpb_prep(const Geom& g, const float* table, _Float16* tab16, float* tmax, int* kidx,
                            hipStream_t stream);
 hipError_t launch_attn_fwd_rpb(const FwdArgs& a, hipStream_t stream);
+
+// CLA gate G = sigmoid(PW_1x1(DW_3x3(X))) on a [B, H, W, C] map.
+struct GateArgs {
+  const void* x;        // [B, H, W, C], bf16 or float32
+  const float* w_dw;    // [C, 3, 3]
+  const float* b_dw;    // [C] or nullptr
+  const float* w_pw;    // [C, C] (out, in)
+  const float* b_pw;    // [C] or nullptr
+  void* g;              // [B, H, W, C], same dtype as x
+  int B, H, W, C;
+};
+bool cla_channels_supported(int C);
+hipError_t launch_cla_gate(const GateArgs& a, int esize, hipStream_t stream);
 
 struct BwdArgs {
   Geom g;
