@@ -102,6 +102,24 @@ def kernel_avg_ms(rib, group):
     return (ms / n if n else None), n
 
 
+def cold_kernel_ms(fn, rib, groups, dev, n: int = 10):
+    """Average kernel time of each group with the 256 MB last-level cache (MALL) flushed before every
+    call: a 512 MiB buffer is overwritten between calls, so the inputs come from HBM."""
+    import torch
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    tot = {g: 0.0 for g in groups}
+    for _ in range(n):
+        flush.fill_(1)
+        torch.cuda.synchronize()
+        for g in groups:
+            rib.kernel_timing_read(g)
+        fn()
+        for g in groups:
+            tot[g] += rib.kernel_timing_read(g)[0]
+    del flush
+    return {g: tot[g] / n for g in groups}
+
+
 def counter_record():
     """The committed counter run of the attention kernel (HBM bytes per launch, the shader clock and
     MFMA-busy fraction under counters), only while the kernel source is the one it was taken on."""
@@ -314,8 +332,8 @@ def cla_measure(wl, x, step, dev, steps: int):
             "gate_GB/s": gate_ms and round(2 * tensor_bytes / gate_ms / 1e6, 1),
             "gate_frac_hbm": gate_ms and round(2 * tensor_bytes / gate_ms / 1e6 / PEAK_HBM_GBS, 3),
             "gate_tflops": gate_ms and round(flops / gate_ms / 1e9, 1),
-            "gated_attn_kernel_ms": round(gated_ms, 4),
-            "ungated_attn_kernel_ms_same_loop": round(rib_attn_ms, 4)}
+            "gated_attn_kernel_ms": round(gated_ms, 5),
+            "ungated_attn_kernel_ms_same_loop": round(rib_attn_ms, 5)}
 
 
 def main():
@@ -366,6 +384,7 @@ def main():
     unp_ms, _ = kernel_avg_ms(rib, "unpartition")
     pg_ms, _ = kernel_avg_ms(rib, "posgen")
     dist = step_distribution(step.run, max(50, args.steps), rib)
+    cold = cold_kernel_ms(step.run, rib, ("posgen", "partition"), dev)
     rib.kernel_timing_enable(False)
     print(f"bench: step {ms:.4f} ms, attention kernel {attn_ms:.4f} ms over {attn_n} launches",
           file=sys.stderr, flush=True)
@@ -376,7 +395,8 @@ def main():
     tensor_bytes = wl.B * wl.H * wl.W * wl.heads * wl.d_c * 2
     # the gathers of K and V (read + write each) and the packing of Q_p, K_p; Q_c is read and O written
     # in the map layout by the attention kernel itself
-    part_bytes = 4 * tensor_bytes + 4 * wl.N * wl.r * 2
+    # + the key-norm bound, which reads the windowed K_c once more
+    part_bytes = 5 * tensor_bytes + 4 * wl.N * wl.r * 2
     pg_bytes = 4 * (wl.hidden * 4 * wl.n_freq + 2 * wl.r * wl.hidden) + 2 * wl.N * wl.r * 2
     rec = counter_record()
     traffic = rec and rec.get("hbm_bytes_per_launch")
@@ -400,6 +420,7 @@ def main():
                    "B": wl.B, "H": wl.H, "W": wl.W, "heads": wl.heads, "d_c": wl.d_c, "w": wl.w, "r": wl.r,
                    "windows": wl.windows, "units": wl.units, "parallelism": "single GPU"},
         "windows_per_s": round(wl.windows / (ms / 1e3), 1),
+        "window_heads_per_s": round(wl.units / (ms / 1e3), 1),
         "pct_of_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
         "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
@@ -412,9 +433,14 @@ def main():
                      "mfma_busy_under_counters": rec and rec.get("mfma_busy_frac")},
         "distribution": dist,
         "kernels": {
-            "posgen": {"ms": pg_ms and round(pg_ms, 5), "GB/s": pg_ms and round(pg_bytes / pg_ms / 1e6, 1)},
+            "posgen": {"ms": pg_ms and round(pg_ms, 5), "GB/s": pg_ms and round(pg_bytes / pg_ms / 1e6, 1),
+                       "cold_ms": round(cold["posgen"], 5)},
             "partition": {"ms": round(part_ms, 5), "GB/s": round(part_bytes / part_ms / 1e6, 1),
-                          "frac_hbm": round(part_bytes / part_ms / 1e6 / PEAK_HBM_GBS, 3)},
+                          "frac_hbm": round(part_bytes / part_ms / 1e6 / PEAK_HBM_GBS, 3),
+                          "cold_ms": round(cold["partition"], 5),
+                          "cold_GB/s": round(part_bytes / cold["partition"] / 1e6, 1),
+                          "note": "GB/s over one read + one write of K_c and V, Q_p/K_p packing and the key-norm "
+                                  "read; cold_* with the 256 MB MALL flushed before each call"},
             "attn_fwd": {"ms": round(attn_ms, 5), "TFLOP/s": round(attn_tflops, 1)},
             "unpartition": ({"ms": None, "note": "none: O rows are written in the map layout by the attention "
                                                  "kernel"} if unp_ms is None else

@@ -9,7 +9,8 @@
 //    contiguous run, so the three halo rows (34 pixels each) load with 16-byte coalesced
 //    reads and the gate tile stores the same way (staged through LDS). The next tile's halo
 //    is loaded into registers while the current one is computed (the LDS-only barriers leave
-//    those loads in flight).
+//    those loads in flight). Each XCD walks its own contiguous band of tiles, so the rows a
+//    tile shares with the tiles above and below it are L2 hits on that XCD.
 //  * Depth-wise 3x3 on the vector unit in fp32: a thread owns two adjacent channels and eight
 //    consecutive pixels, with its 18 taps and 2 biases in registers for the whole launch.
 //  * Point-wise 1x1 on the matrix unit: G^T[out][px] = W_pw[out][:] . D[px][:] as
@@ -28,6 +29,7 @@ namespace rib {
 namespace {
 
 constexpr int kGatePx = 32;   // pixels per tile (one MFMA column block)
+constexpr int kXcds = 8;      // accelerator dies; workgroups are dealt to them round-robin
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
@@ -107,8 +109,13 @@ __global__ __launch_bounds__(128 * CB) void cla_gate_bf16_kernel(GateArgs a) {
         pre[j] = *(const u32x4*)(x + ((int64_t)(by + r - 1) * W + xx) * C + 8 * k);
     }
   };
-  if ((int)blockIdx.x < ntiles) fetch(blockIdx.x);
-  for (int tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+  // workgroup b runs on XCD b % 8 (round-robin dispatch); the grid is a multiple of 8
+  const int xcd = blockIdx.x % kXcds, lw = blockIdx.x / kXcds, nw = gridDim.x / kXcds;
+  const int band = (ntiles + kXcds - 1) / kXcds;
+  const int t_end = min(ntiles, (xcd + 1) * band);
+  const int t_first = xcd * band + lw;
+  if (t_first < t_end) fetch(t_first);
+  for (int tile = t_first; tile < t_end; tile += nw) {
     const int xt = tile % ntx;
     const int by = tile / ntx;               // b * H + y
     const int x0 = xt * kGatePx;
@@ -120,7 +127,7 @@ __global__ __launch_bounds__(128 * CB) void cla_gate_bf16_kernel(GateArgs a) {
       if (i < kHaloChunks) *(u32x4*)&sX[8 * i] = pre[j];
     }
     lds_barrier();
-    if (tile + (int)gridDim.x < ntiles) fetch(tile + gridDim.x);
+    if (tile + nw < t_end) fetch(tile + nw);
     // ---- depth-wise 3x3 (fp32), rounded to bf16 into D; a 3 x 3 window of halo values slides
     // along the thread's pixels (three new LDS reads per pixel)
     {
@@ -250,7 +257,8 @@ hipError_t launch_gate_cb(const GateArgs& a, int tiles, hipStream_t stream) {
   if (e == hipSuccess)
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cla_gate_bf16_kernel<CB>, 128 * CB, 0);
   if (e != hipSuccess) return e;
-  const int grid = (int)std::min<int64_t>(tiles, (int64_t)std::max(cus, 1) * std::max(per_cu, 1));
+  const int64_t slots = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
+  const int grid = (int)std::max<int64_t>(kXcds, std::min<int64_t>(tiles, slots) / kXcds * kXcds);
   hipLaunchKernelGGL(cla_gate_bf16_kernel<CB>, dim3(grid), dim3(128 * CB), 0, stream, a);
   return hipGetLastError();
 }
