@@ -145,3 +145,38 @@ def test_fwd_bias_cancels_content():
     mean = v.reshape(64, 32).mean(0)
     err = (o.reshape(64, 32) - mean).abs().max().item()
     assert err <= 1e-5, err
+
+
+def _many_items_workload(seed):
+    """w = 24 on a 192 x 192 map with 3 heads: 192 windows x heads, each with 3 query blocks and a
+    ragged 9th key tile, small enough for the oracle to check every output."""
+    return rib_synth.custom_workload(1, 192, 192, 3, 32, 24, 16, "bf16", seed=seed)
+
+
+def test_fwd_many_items_full():
+    dev = device()
+    wl = _many_items_workload(21)
+    x = rib_synth.make_inputs(wl)
+    o, lse, rqp, rkp = _run(wl, x, dev)
+    _compare(wl, x, o, lse, rqp, rkp, tag="w24 map192 full")
+    o2, lse2, _, _ = _run(wl, x, dev)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)) and torch.equal(lse, lse2)
+
+
+def test_fwd_exact_pass_forced():
+    """Channel 0 of token 0's key is 40 in every window while every query has 0 there and 8 in
+    channel 1: the per-query bound |q'| max|k| overshoots the largest score by ~75 log2 units, the
+    row sums fall below 2^-60, and every workgroup recomputes its rows with the exact pass."""
+    dev = device()
+    wl = _many_items_workload(22)
+    x = rib_synth.make_inputs(wl)
+    q = x["q_c"].data.view(np.int16).copy()
+    k = x["k_c"].data.view(np.int16).copy()
+    bf = lambda v: int(rib_synth.bf16_bits(np.array([v], np.float32))[0].view(np.int16))
+    q[..., 0] = bf(0.0)
+    q[..., 1] = bf(8.0)
+    k[:, ::24, ::24, :, 0] = bf(40.0)    # token 0 of every 24 x 24 window
+    x["q_c"] = rib_synth.Tensor("bf16", q.view(x["q_c"].data.dtype))
+    x["k_c"] = rib_synth.Tensor("bf16", k.view(x["k_c"].data.dtype))
+    o, lse, rqp, rkp = _run(wl, x, dev)
+    _compare(wl, x, o, lse, rqp, rkp, tag="exact pass")
