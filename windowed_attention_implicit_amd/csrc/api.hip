@@ -111,8 +111,10 @@ FwdLayout fwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
   L.kw = c.take(t);
   L.vw = c.take(t);
   L.ow = rows_qo ? c.take(t) : nullptr;
-  L.qp = c.take(pos);
-  L.kp = c.take(pos);
+  // the bf16 kernel reads Q_p, K_p in place when no padding is needed (r = 16 or 32)
+  const bool pack = rows_qo || g.r != padded_rank(g.r);
+  L.qp = pack ? c.take(pos) : nullptr;
+  L.kp = pack ? c.take(pos) : nullptr;
   L.kmax2 = (float*)c.take((size_t)g.units * key_bound_parts(g.N) * sizeof(float));
   L.bytes = c.off;
   return L;
@@ -459,12 +461,18 @@ static rib_status_t attn_fwd_impl(const rib_shape_t* shape, rib_dtype_t dtype, f
     if ((e = launch_partition(g, es, dtype == RIB_BF16 ? WinLayout::kTransKappa : WinLayout::kRows, v, L.vw, st)) !=
         hipSuccess)
       return hip_fail(e, "partition v");
-    if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, q_p, es, L.qp, st)) != hipSuccess) return hip_fail(e, "pack q_p");
-    if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, k_p, es, L.kp, st)) != hipSuccess) return hip_fail(e, "pack k_p");
+    if (L.qp) {
+      if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, q_p, es, L.qp, st)) != hipSuccess)
+        return hip_fail(e, "pack q_p");
+      if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, k_p, es, L.kp, st)) != hipSuccess)
+        return hip_fail(e, "pack k_p");
+    }
     FwdArgs a;
     a.g = g;
     a.c = resolve_scale(scale, shape) * kLog2e;
-    a.qw = L.qw; a.kw = L.kw; a.vw = L.vw; a.qp = L.qp; a.kp = L.kp; a.ow = L.ow;
+    a.qw = L.qw; a.kw = L.kw; a.vw = L.vw; a.ow = L.ow;
+    a.qp = L.qp ? L.qp : q_p;
+    a.kp = L.kp ? L.kp : k_p;
     a.q_map = q_c; a.o_map = o;
     a.lse = lse;
     a.kmax2 = L.kmax2;

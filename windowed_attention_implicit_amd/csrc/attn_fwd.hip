@@ -234,7 +234,8 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
   // Pad chunks fetch a duplicate of their row's first chunk.
   const int nkt = (N + kKeyTile - 1) / kKeyTile;
   const __amdgpu_buffer_rsrc_t rs_kc = __builtin_amdgcn_make_buffer_rsrc((void*)kw, 0, n_rows * 64, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rs_kp = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, n_rows * rp * 2, kRsrcWord3);
+  // K_p has N rows (rows past N read zero): either the packed copy or the caller's buffer
+  const __amdgpu_buffer_rsrc_t rs_kp = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, N * rp * 2, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc((void*)vt, 0, n_rows * 64, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_i = __builtin_amdgcn_make_buffer_rsrc((void*)a.rpb_kidx, 0, n_rows * 4, kRsrcWord3);
   int dma_off[4];
