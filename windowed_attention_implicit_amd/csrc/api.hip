@@ -648,20 +648,21 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
     if ((e = (call)) != hipSuccess) return hip_fail(e, what); \
   } while (0)
     TimedGroup t_part(RIB_KERNEL_PARTITION, st);
-    RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, q_c, L.qw, st), "partition q");
-    RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, k_c, L.kw, st), "partition k");
-    RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, v, L.vw, st), "partition v");
-    RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, d_o, L.dow, st), "partition do");
     if (bf) {
-      RIB_LAUNCH(launch_partition(g, es, WinLayout::kTransKappa, q_c, L.qt, st), "partition q^T");
-      RIB_LAUNCH(launch_partition(g, es, WinLayout::kTransKappa, k_c, L.kt, st), "partition k^T");
-      RIB_LAUNCH(launch_partition(g, es, WinLayout::kTransKappa, d_o, L.dot, st), "partition do^T");
-    }
-    RIB_LAUNCH(launch_pack_pos(g.N, g.n_rows, g.r, rp, es, q_p, es, L.qp, st), "pack q_p");
-    RIB_LAUNCH(launch_pack_pos(g.N, g.n_rows, g.r, rp, es, k_p, es, L.kp, st), "pack k_p");
-    if (bf) {
-      RIB_LAUNCH(launch_pos_transpose(g.n_rows, rp, L.qp, L.qpt, st), "q_p^T");
-      RIB_LAUNCH(launch_pos_transpose(g.n_rows, rp, L.kp, L.kpt, st), "k_p^T");
+      // Q_c, K_c and dO are needed in both windowed layouts: one pass over the map each
+      RIB_LAUNCH(launch_partition_rows_kappa(g, q_c, L.qw, L.qt, st), "partition q");
+      RIB_LAUNCH(launch_partition_rows_kappa(g, k_c, L.kw, L.kt, st), "partition k");
+      RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, v, L.vw, st), "partition v");
+      RIB_LAUNCH(launch_partition_rows_kappa(g, d_o, L.dow, L.dot, st), "partition do");
+      RIB_LAUNCH(launch_pack_pos_dual(g.N, g.n_rows, g.r, rp, q_p, L.qp, L.qpt, st), "pack q_p");
+      RIB_LAUNCH(launch_pack_pos_dual(g.N, g.n_rows, g.r, rp, k_p, L.kp, L.kpt, st), "pack k_p");
+    } else {
+      RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, q_c, L.qw, st), "partition q");
+      RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, k_c, L.kw, st), "partition k");
+      RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, v, L.vw, st), "partition v");
+      RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, d_o, L.dow, st), "partition do");
+      RIB_LAUNCH(launch_pack_pos(g.N, g.n_rows, g.r, rp, es, q_p, es, L.qp, st), "pack q_p");
+      RIB_LAUNCH(launch_pack_pos(g.N, g.n_rows, g.r, rp, es, k_p, es, L.kp, st), "pack k_p");
     }
     t_part.end();
     TimedGroup t_prep(RIB_KERNEL_BWD_PREP, st);

@@ -29,6 +29,9 @@ size_t posgen_bwd_workspace_bytes(int w, const rib_mlp_t& mlp);
 // x [B,H,W,heads,d] -> windowed buffer in `layout` (rows >= N zero-filled).
 hipError_t launch_partition(const Geom& g, int esize, WinLayout layout, const void* x, void* xw,
                             hipStream_t stream);
+// bf16, d = 32: x -> both the kRows and the kTransKappa buffer in one pass.
+hipError_t launch_partition_rows_kappa(const Geom& g, const void* x, void* xw_rows, void* xw_kappa,
+                                       hipStream_t stream);
 // windowed kRows buffer -> x [B,H,W,heads,d].
 hipError_t launch_unpartition(const Geom& g, int esize, const void* xw, void* x, hipStream_t stream);
 // Public plain gather / scatter ([units][N][d], no padding).
@@ -39,8 +42,10 @@ hipError_t launch_unpartition_plain(const Geom& g, int esize, const void* xw, vo
 // precision (rows >= N and columns >= r zero). In and out may differ in type.
 hipError_t launch_pack_pos(int N, int n_rows, int r, int rp, int in_esize, const void* in, int out_esize,
                            void* out, hipStream_t stream);
-// Transposed, kappa-permuted copy of a padded [n_rows, rp] bf16 buffer: [rp, n_rows].
-hipError_t launch_pos_transpose(int n_rows, int rp, const void* in, void* out, hipStream_t stream);
+// bf16 [N, r] -> the padded [n_rows, rp] rows and their transposed, kappa-permuted copy
+// [rp, n_rows] in one pass.
+hipError_t launch_pack_pos_dual(int N, int n_rows, int r, int rp, const void* in, void* out, void* out_t,
+                                hipStream_t stream);
 
 struct FwdArgs {
   Geom g;

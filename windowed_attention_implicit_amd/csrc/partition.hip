@@ -74,9 +74,12 @@ __device__ __forceinline__ int kappa16(int p) { return (p & ~12) | ((p & 4) << 1
 
 // map -> channel-major kappa layout [units][32][n_rows], bf16, d = 32. One block
 // per (unit, 64-token group): 64 tokens x 64 bytes are staged in LDS, then
-// every thread writes 8 consecutive kappa positions of one channel.
+// every thread writes 8 consecutive kappa positions of one channel. With `rows`
+// the same pass also writes the token-major rows layout [units][n_rows][32]
+// (rows >= N zero), so a tensor needed in both layouts is read once.
 __global__ __launch_bounds__(256) void gather_trans_kappa_kernel(PixelMap pm, int N, int n_rows,
-                                                                 const bf16* __restrict__ x, bf16* __restrict__ xt) {
+                                                                 const bf16* __restrict__ x, bf16* __restrict__ xt,
+                                                                 bf16* __restrict__ rows) {
   __shared__ bf16 tile[64][32 + 2];
   const int groups = n_rows / 64;
   const int u = blockIdx.x / groups;
@@ -87,6 +90,7 @@ __global__ __launch_bounds__(256) void gather_trans_kappa_kernel(PixelMap pm, in
     const int t = g0 + tok;
     u32x4 v = u32x4(0u);
     if (t < N) v = *(const u32x4*)(x + pm.pixel_head(u, t) * 32 + c * 8);
+    if (rows) *(u32x4*)(rows + ((int64_t)u * n_rows + t) * 32 + c * 8) = v;
     const bf16* pv = (const bf16*)&v;
 #pragma unroll
     for (int j = 0; j < 8; ++j) tile[tok][c * 8 + j] = pv[j];
@@ -112,12 +116,17 @@ __global__ void pack_pos_kernel(int N, int n_rows, int r, int rp, const InT* __r
   out[i] = (OutT)v;
 }
 
-__global__ void pos_transpose_kernel(int n_rows, int rp, const bf16* __restrict__ in, bf16* __restrict__ out) {
+// [N, r] positional tokens -> the zero-padded [n_rows, rp] rows and their kappa transpose
+// [rp, n_rows] in one pass (bf16): element (t, j) goes to rows[t][j] and to kappa
+// position kappa16(t) of channel j (kappa16 is its own inverse).
+__global__ void pack_pos_dual_kernel(int N, int n_rows, int r, int rp, const bf16* __restrict__ in,
+                                     bf16* __restrict__ out, bf16* __restrict__ outt) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n_rows * rp) return;
-  int j = i / n_rows, p = i - j * n_rows;
-  int t = (p & ~15) | kappa16(p & 15);
-  out[i] = in[(int64_t)t * rp + j];
+  int t = i / rp, j = i - t * rp;
+  const bf16 v = (t < N && j < r) ? in[(int64_t)t * r + j] : (bf16)0.f;
+  out[i] = v;
+  outt[(int64_t)j * n_rows + ((t & ~15) | kappa16(t & 15))] = v;
 }
 
 ChunkGeom chunk_geom(const Geom& g, int esize, int n_rows) {
@@ -145,8 +154,16 @@ hipError_t launch_partition(const Geom& g, int esize, WinLayout layout, const vo
   } else {
     if (g.units == 0) return hipSuccess;
     hipLaunchKernelGGL(gather_trans_kappa_kernel, dim3((unsigned)((int64_t)g.units * (g.n_rows / 64))), dim3(256), 0,
-                       stream, make_pixel_map(g), g.N, g.n_rows, (const bf16*)x, (bf16*)xw);
+                       stream, make_pixel_map(g), g.N, g.n_rows, (const bf16*)x, (bf16*)xw, (bf16*)nullptr);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_partition_rows_kappa(const Geom& g, const void* x, void* xw_rows, void* xw_kappa,
+                                       hipStream_t stream) {
+  if (g.units == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_trans_kappa_kernel, dim3((unsigned)((int64_t)g.units * (g.n_rows / 64))), dim3(256), 0,
+                     stream, make_pixel_map(g), g.N, g.n_rows, (const bf16*)x, (bf16*)xw_kappa, (bf16*)xw_rows);
   return hipGetLastError();
 }
 
@@ -192,10 +209,12 @@ hipError_t launch_pack_pos(int N, int n_rows, int r, int rp, int in_esize, const
   return hipGetLastError();
 }
 
-hipError_t launch_pos_transpose(int n_rows, int rp, const void* in, void* out, hipStream_t stream) {
+hipError_t launch_pack_pos_dual(int N, int n_rows, int r, int rp, const void* in, void* out, void* out_t,
+                                hipStream_t stream) {
   const int n = n_rows * rp;
-  hipLaunchKernelGGL(pos_transpose_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, n_rows, rp, (const bf16*)in,
-                     (bf16*)out);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(pack_pos_dual_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, N, n_rows, r, rp,
+                     (const bf16*)in, (bf16*)out, (bf16*)out_t);
   return hipGetLastError();
 }
 
