@@ -34,7 +34,9 @@
  *    launches nothing and returns a non-zero status; rib_last_error() then
  *    holds a message (per host thread). No C++ exception crosses this ABI.
  *  - Empty inputs (B == 0) are valid and launch nothing.
- *  - Supported today: d_c = 32; 1 <= r <= 32; 2 <= w <= 256.
+ *  - Supported today: d_c = 32 or 64; 1 <= r <= 32; 2 <= w <= 256. bfloat16 at
+ *    d_c = 32 runs on the matrix-core kernels; float32 runs and d_c = 64 run on
+ *    plain per-token kernels sized for correctness, not speed.
  */
 #ifndef RIB_H
 #define RIB_H

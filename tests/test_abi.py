@@ -72,7 +72,8 @@ def test_fwd_validation(L):
     assert _fwd(L, rib.Shape(2, 192, 192, 6, 32, 1, 16)) == rib.RIB_ERR_INVALID_ARG     # w < 2
     assert _fwd(L, rib.Shape(2, 192, 192, 6, 32, 96, 0)) == rib.RIB_ERR_INVALID_ARG     # r < 1
     assert _fwd(L, rib.Shape(-1, 192, 192, 6, 32, 96, 16)) == rib.RIB_ERR_INVALID_ARG   # B < 0
-    assert _fwd(L, rib.Shape(2, 192, 192, 6, 64, 96, 16)) == rib.RIB_ERR_UNSUPPORTED    # d_c
+    assert _fwd(L, rib.Shape(2, 192, 192, 6, 48, 96, 16)) == rib.RIB_ERR_UNSUPPORTED    # d_c not 32 or 64
+    assert L.rib_fwd_workspace_size(ctypes.byref(rib.Shape(2, 192, 192, 6, 64, 96, 16)), rib.RIB_BF16) > 0
     assert _fwd(L, rib.Shape(2, 192, 192, 6, 32, 96, 33)) == rib.RIB_ERR_UNSUPPORTED    # r > 32
     assert _fwd(L, rib.Shape(1, 512, 512, 1, 32, 512, 16)) == rib.RIB_ERR_UNSUPPORTED   # w > 256
     assert _fwd(L, good, dtype=7) == rib.RIB_ERR_INVALID_ARG

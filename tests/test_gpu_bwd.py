@@ -55,6 +55,10 @@ def _compare(wl, x, grads, rqp, rkp, units=None, tag="", pos=True):
     (2, 14, 14, 1, 32, 7, 1, "bf16"),
     (1, 24, 48, 2, 32, 24, 17, "bf16"),
     (1, 40, 40, 1, 32, 40, 32, "bf16"),
+    # d_c = 64 (the one-thread-per-key / per-query kernels)
+    (1, 10, 15, 2, 64, 5, 3, "bf16"),
+    (1, 16, 16, 2, 64, 16, 20, "bf16"),
+    (1, 24, 24, 1, 64, 12, 16, "f32"),
 ], ids=lambda s: "B{}_H{}_W{}_h{}_d{}_w{}_r{}_{}".format(*s))
 def test_bwd_small_and_ragged(shape):
     dev = device()

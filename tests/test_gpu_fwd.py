@@ -79,6 +79,10 @@ def test_fwd_large_workloads_sampled(name, k):
     (1, 10, 15, 2, 32, 5, 3, "f32"),
     (2, 24, 24, 2, 32, 12, 20, "f32"),
     (1, 32, 32, 1, 32, 32, 8, "f32"),
+    # d_c = 64 (the one-thread-per-query kernels)
+    (1, 10, 15, 2, 64, 5, 3, "bf16"),
+    (1, 24, 24, 2, 64, 12, 16, "bf16"),
+    (1, 20, 20, 1, 64, 10, 32, "f32"),
 ], ids=lambda s: "B{}_H{}_W{}_h{}_d{}_w{}_r{}_{}".format(*s))
 def test_fwd_ragged_and_edge_shapes(shape):
     dev = device()

@@ -62,7 +62,8 @@ rib_status_t check_shape(const rib_shape_t* s, rib_dtype_t dt, bool need_rank) {
   if (need_rank) {
     if (s->r < 1) return fail(RIB_ERR_INVALID_ARG, "rank r=%d must be >= 1", s->r);
     if (s->r > 32) return fail(RIB_ERR_UNSUPPORTED, "rank r=%d exceeds 32", s->r);
-    if (s->d_c != 32) return fail(RIB_ERR_UNSUPPORTED, "d_c=%d: only d_c = 32 is implemented", s->d_c);
+    if (s->d_c != 32 && s->d_c != 64)
+      return fail(RIB_ERR_UNSUPPORTED, "d_c=%d: d_c = 32 and 64 are implemented", s->d_c);
   }
   int64_t elems = (int64_t)s->B * s->H * s->W * s->heads * s->d_c;
   if (elems > ((int64_t)1 << 40)) return fail(RIB_ERR_UNSUPPORTED, "feature map too large");
@@ -99,14 +100,18 @@ struct FwdLayout {
   size_t bytes;
 };
 
+// The bf16 MFMA kernels cover d_c = 32; float32 runs and d_c = 64 take the simple kernels
+// (windowed rows in and out).
+bool mfma_path(const Geom& g, rib_dtype_t dt) { return dt == RIB_BF16 && g.d_c == 32; }
+
 FwdLayout fwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
   const int es = esize_of(dt);
   const size_t t = (size_t)g.units * g.n_rows * g.d_c * es;
   const size_t pos = (size_t)g.n_rows * padded_rank(g.r) * es;
   Carve c(ws);
   FwdLayout L;
-  // the bf16 kernel reads Q_c and writes O in the map layout directly
-  const bool rows_qo = dt != RIB_BF16;
+  // the bf16 MFMA kernel reads Q_c and writes O in the map layout directly
+  const bool rows_qo = !mfma_path(g, dt);
   L.qw = rows_qo ? c.take(t) : nullptr;
   L.kw = c.take(t);
   L.vw = c.take(t);
@@ -164,13 +169,14 @@ struct BwdLayout {
 };
 
 BwdLayout bwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
+  // bf: the MFMA kernels, which also need the kappa copies and write the map directly
   const int es = esize_of(dt);
   const int rp = padded_rank(g.r);
   const size_t t = (size_t)g.units * g.n_rows * g.d_c * es;
   const size_t pos = (size_t)g.n_rows * rp * es;
   const size_t rowf = (size_t)g.units * g.n_rows * sizeof(float);
   const size_t part = (size_t)g.units * g.n_rows * rp * sizeof(float);
-  const bool bf = dt == RIB_BF16;
+  const bool bf = mfma_path(g, dt);
   Carve c(ws);
   BwdLayout L;
   L.qw = c.take(t);
@@ -453,13 +459,12 @@ static rib_status_t attn_fwd_impl(const rib_shape_t* shape, rib_dtype_t dtype, f
     const int es = esize_of(dtype);
     const int rp = padded_rank(g.r);
     hipError_t e;
-    const bool bf = dtype == RIB_BF16;
+    const bool bf = mfma_path(g, dtype);
     TimedGroup t_part(RIB_KERNEL_PARTITION, st);
     if (!bf && (e = launch_partition(g, es, WinLayout::kRows, q_c, L.qw, st)) != hipSuccess)
       return hip_fail(e, "partition q");
     if ((e = launch_partition(g, es, WinLayout::kRows, k_c, L.kw, st)) != hipSuccess) return hip_fail(e, "partition k");
-    if ((e = launch_partition(g, es, dtype == RIB_BF16 ? WinLayout::kTransKappa : WinLayout::kRows, v, L.vw, st)) !=
-        hipSuccess)
+    if ((e = launch_partition(g, es, bf ? WinLayout::kTransKappa : WinLayout::kRows, v, L.vw, st)) != hipSuccess)
       return hip_fail(e, "partition v");
     if (L.qp) {
       if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, q_p, es, L.qp, st)) != hipSuccess)
@@ -478,10 +483,10 @@ static rib_status_t attn_fwd_impl(const rib_shape_t* shape, rib_dtype_t dtype, f
     a.kmax2 = L.kmax2;
     a.rp = rp;
     a.gate = gate;
-    if (dtype == RIB_BF16 && (e = launch_key_bound(a, st)) != hipSuccess) return hip_fail(e, "key bound");
+    if (bf && (e = launch_key_bound(a, st)) != hipSuccess) return hip_fail(e, "key bound");
     t_part.end();
     TimedGroup t_attn(RIB_KERNEL_ATTN_FWD, st);
-    e = dtype == RIB_BF16 ? launch_attn_fwd_bf16(a, st) : launch_attn_fwd_f32(a, st);
+    e = bf ? launch_attn_fwd_bf16(a, st) : launch_attn_fwd_simple(a, es, st);
     if (e != hipSuccess) return hip_fail(e, "attention forward");
     t_attn.end();
     if (!bf) {
@@ -641,7 +646,7 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
     hipStream_t st = (hipStream_t)stream;
     const int es = esize_of(dtype);
     const int rp = padded_rank(g.r);
-    const bool bf = dtype == RIB_BF16;
+    const bool bf = mfma_path(g, dtype);
     hipError_t e;
 #define RIB_LAUNCH(call, what)                        \
   do {                                                \
@@ -666,7 +671,7 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
     }
     t_part.end();
     TimedGroup t_prep(RIB_KERNEL_BWD_PREP, st);
-    RIB_LAUNCH(launch_bwd_prep(g, es, o, d_o, lse, L.dd, L.lse2, st), "bwd prep");
+    RIB_LAUNCH(launch_bwd_prep(g, es, o, d_o, lse, L.dd, L.lse2, bf, st), "bwd prep");
     t_prep.end();
     BwdArgs a;
     a.g = g;
@@ -682,10 +687,11 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
     a.dqp_part = L.dqp_part; a.dkp_part = L.dkp_part;
     {
       TimedGroup t_dkv(RIB_KERNEL_ATTN_BWD_DKV, st);
-      RIB_LAUNCH(bf ? launch_attn_bwd_dkv_bf16(a, st) : launch_attn_bwd_dkv_f32(a, st), "attention backward dK/dV");
+      RIB_LAUNCH(bf ? launch_attn_bwd_dkv_bf16(a, st) : launch_attn_bwd_dkv_simple(a, es, st),
+                 "attention backward dK/dV");
       t_dkv.end();
       TimedGroup t_dq(RIB_KERNEL_ATTN_BWD_DQ, st);
-      RIB_LAUNCH(bf ? launch_attn_bwd_dq_bf16(a, st) : launch_attn_bwd_dq_f32(a, st), "attention backward dQ");
+      RIB_LAUNCH(bf ? launch_attn_bwd_dq_bf16(a, st) : launch_attn_bwd_dq_simple(a, es, st), "attention backward dQ");
       t_dq.end();
     }
     TimedGroup t_red(RIB_KERNEL_POS_REDUCE, st);

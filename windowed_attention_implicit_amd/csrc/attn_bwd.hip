@@ -418,72 +418,82 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ prep
 // D_i = sum_c dO_ic O_ic and LSE2_i = LSE_i * log2(e) per window row. For the
-// bf16 kernels they are stored negated (-D, -LSE2: what those kernels add,
+// bf16 MFMA kernels they are stored negated (-D, -LSE2: what those kernels add,
 // and the accumulator inputs the dkv kernel takes from LDS as they are); the
-// float32 kernels read them unnegated.
+// simple kernels read them unnegated.
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, PixelMap pm, const T* __restrict__ o,
                                                        const T* __restrict__ d_o, const float* __restrict__ lse,
-                                                       float* __restrict__ dd, float* __restrict__ lse2) {
+                                                       float* __restrict__ dd, float* __restrict__ lse2, float sgn) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   const int64_t total = (int64_t)g.units * g.n_rows;
   if (i >= total) return;
   const int unit = (int)(i / g.n_rows);
   const int t = (int)(i - (int64_t)unit * g.n_rows);
-  constexpr float sgn = sizeof(T) == 2 ? -1.f : 1.f;
   if (t >= g.N) {
     dd[i] = 0.f;
     lse2[i] = sgn * INFINITY;   // P = 0 for padded rows
     return;
   }
   const int64_t ph = pm.pixel_head(unit, t);
-  const T* orow = o + ph * 32;
-  const T* grow = d_o + ph * 32;
+  const T* orow = o + ph * g.d_c;
+  const T* grow = d_o + ph * g.d_c;
   float acc = 0.f;
-#pragma unroll
-  for (int ch = 0; ch < 32; ++ch) acc = fmaf((float)orow[ch], (float)grow[ch], acc);
+  for (int ch = 0; ch < g.d_c; ++ch) acc = fmaf((float)orow[ch], (float)grow[ch], acc);
   dd[i] = sgn * acc;
   lse2[i] = sgn * (lse[ph] * 1.44269504088896340736f);
 }
 
-// ------------------------------------------------------------------ float32
-// dK, dV: one thread per key, query tiles of 64 in LDS.
-template <int RP>
-__global__ __launch_bounds__(256) void attn_bwd_dkv_f32_kernel(BwdArgs a) {
-  constexpr int D = 32, DH = D + RP;
+// ------------------------------------------------------------------ simple kernels
+// float32 arithmetic on T (float or bf16) rows with D content channels: float32
+// runs and content widths the MFMA kernels do not cover (d_c = 64).
+// dK, dV: SPLIT threads per key (1 at d_c = 32; 2 at d_c = 64, each owning half of the
+// channels, so the key's registers fit without spilling), query tiles of 64 in LDS.
+template <typename T, int D, int RP>
+__global__ __launch_bounds__(256) void attn_bwd_dkv_simple_kernel(BwdArgs a) {
+  constexpr int DH = D + RP;
+  constexpr int SPLIT = D > 32 ? 2 : 1;
+  constexpr int DS = D / SPLIT, RS = RP / SPLIT;   // this thread's content / positional channels
+  constexpr int KPB = 256 / SPLIT;                  // keys per block
   __shared__ float sQ[kTile][DH + 1];
   __shared__ float sDo[kTile][D + 1];
   __shared__ float sL[kTile], sD[kTile];
   const Geom& g = a.g;
   const int N = g.N, n_rows = g.n_rows;
-  const int nkb = (N + 255) / 256;
+  const int nkb = (N + KPB - 1) / KPB;
   const int unit = blockIdx.x / nkb;
-  const int key = (blockIdx.x - unit * nkb) * 256 + threadIdx.x;
+  const int key = (blockIdx.x - unit * nkb) * KPB + threadIdx.x / SPLIT;
+  const int part = threadIdx.x % SPLIT;
+  const int c0 = part * DS, p0 = part * RS;         // first content / positional channel of this thread
   const int64_t ub = (int64_t)unit * n_rows;
-  const float* qw = (const float*)a.qw + ub * D;
-  const float* dow = (const float*)a.dow + ub * D;
-  const float* qp = (const float*)a.qp;
+  const T* qw = (const T*)a.qw + ub * D;
+  const T* dow = (const T*)a.dow + ub * D;
+  const T* qp = (const T*)a.qp;
   const int kk = key < N ? key : 0;
-  float kh[DH], vv[D], gk[DH], gv[D];
+  float kc[DS], kpv[RS], vv[DS], gk[DS], gkp[RS], gv[DS];
 #pragma unroll
-  for (int i = 0; i < D; ++i) { kh[i] = ((const float*)a.kw)[(ub + kk) * D + i]; vv[i] = ((const float*)a.vw)[(ub + kk) * D + i]; }
+  for (int i = 0; i < DS; ++i) {
+    kc[i] = (float)((const T*)a.kw)[(ub + kk) * D + c0 + i];
+    vv[i] = (float)((const T*)a.vw)[(ub + kk) * D + c0 + i];
+    gk[i] = 0.f;
+    gv[i] = 0.f;
+  }
 #pragma unroll
-  for (int i = 0; i < RP; ++i) kh[D + i] = ((const float*)a.kp)[(int64_t)kk * RP + i];
-#pragma unroll
-  for (int i = 0; i < DH; ++i) gk[i] = 0.f;
-#pragma unroll
-  for (int i = 0; i < D; ++i) gv[i] = 0.f;
+  for (int i = 0; i < RS; ++i) {
+    kpv[i] = (float)((const T*)a.kp)[(int64_t)kk * RP + p0 + i];
+    gkp[i] = 0.f;
+  }
   const float c = a.c;
   const int nqt = (N + kTile - 1) / kTile;
   for (int t = 0; t < nqt; ++t) {
     const int q0 = t * kTile;
     for (int i = threadIdx.x; i < kTile * DH; i += 256) {
       int r = i / DH, ch = i - r * DH;
-      sQ[r][ch] = ch < D ? qw[(int64_t)(q0 + r) * D + ch] : qp[(int64_t)(q0 + r) * RP + ch - D];
+      sQ[r][ch] = (float)(ch < D ? qw[(int64_t)(q0 + r) * D + ch] : qp[(int64_t)(q0 + r) * RP + ch - D]);
     }
     for (int i = threadIdx.x; i < kTile * D; i += 256) {
       int r = i / D, ch = i - r * D;
-      sDo[r][ch] = dow[(int64_t)(q0 + r) * D + ch];
+      sDo[r][ch] = (float)dow[(int64_t)(q0 + r) * D + ch];
     }
     if (threadIdx.x < kTile) {
       sL[threadIdx.x] = a.lse2[ub + q0 + threadIdx.x];
@@ -493,32 +503,45 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_f32_kernel(BwdArgs a) {
     for (int r = 0; r < kTile; ++r) {
       float s = 0.f, dp = 0.f;
 #pragma unroll
-      for (int i = 0; i < DH; ++i) s = fmaf(sQ[r][i], kh[i], s);
+      for (int i = 0; i < DS; ++i) {
+        s = fmaf(sQ[r][c0 + i], kc[i], s);
+        dp = fmaf(sDo[r][c0 + i], vv[i], dp);
+      }
 #pragma unroll
-      for (int i = 0; i < D; ++i) dp = fmaf(sDo[r][i], vv[i], dp);
+      for (int i = 0; i < RS; ++i) s = fmaf(sQ[r][D + p0 + i], kpv[i], s);
+      if constexpr (SPLIT == 2) {   // the key's two threads are adjacent lanes
+        s += __shfl_xor(s, 1);
+        dp += __shfl_xor(dp, 1);
+      }
       const float p = exp2f(fmaf(s, c, -sL[r]));
       const float ds = p * (dp - sD[r]);
 #pragma unroll
-      for (int i = 0; i < D; ++i) gv[i] = fmaf(p, sDo[r][i], gv[i]);
+      for (int i = 0; i < DS; ++i) {
+        gv[i] = fmaf(p, sDo[r][c0 + i], gv[i]);
+        gk[i] = fmaf(ds, sQ[r][c0 + i], gk[i]);
+      }
 #pragma unroll
-      for (int i = 0; i < DH; ++i) gk[i] = fmaf(ds, sQ[r][i], gk[i]);
+      for (int i = 0; i < RS; ++i) gkp[i] = fmaf(ds, sQ[r][D + p0 + i], gkp[i]);
     }
     __syncthreads();
   }
   if (key < N) {
-    float* dkw = (float*)a.dkw + (ub + key) * D;
-    float* dvw = (float*)a.dvw + (ub + key) * D;
+    T* dkw = (T*)a.dkw + (ub + key) * D + c0;
+    T* dvw = (T*)a.dvw + (ub + key) * D + c0;
 #pragma unroll
-    for (int i = 0; i < D; ++i) { dkw[i] = gk[i] * a.scale; dvw[i] = gv[i]; }
+    for (int i = 0; i < DS; ++i) {
+      dkw[i] = (T)(gk[i] * a.scale);
+      dvw[i] = (T)gv[i];
+    }
 #pragma unroll
-    for (int i = 0; i < RP; ++i) a.dkp_part[(ub + key) * RP + i] = gk[D + i] * a.scale;
+    for (int i = 0; i < RS; ++i) a.dkp_part[(ub + key) * RP + p0 + i] = gkp[i] * a.scale;
   }
 }
 
 // dQ: one thread per query, key tiles of 64 in LDS.
-template <int RP>
-__global__ __launch_bounds__(256) void attn_bwd_dq_f32_kernel(BwdArgs a) {
-  constexpr int D = 32, DH = D + RP;
+template <typename T, int D, int RP>
+__global__ __launch_bounds__(256) void attn_bwd_dq_simple_kernel(BwdArgs a) {
+  constexpr int DH = D + RP;
   __shared__ float sK[kTile][DH + 1];
   __shared__ float sV[kTile][D + 1];
   const Geom& g = a.g;
@@ -527,15 +550,18 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32_kernel(BwdArgs a) {
   const int unit = blockIdx.x / nqb;
   const int q = (blockIdx.x - unit * nqb) * 256 + threadIdx.x;
   const int64_t ub = (int64_t)unit * n_rows;
-  const float* kw = (const float*)a.kw + ub * D;
-  const float* vw = (const float*)a.vw + ub * D;
-  const float* kp = (const float*)a.kp;
+  const T* kw = (const T*)a.kw + ub * D;
+  const T* vw = (const T*)a.vw + ub * D;
+  const T* kp = (const T*)a.kp;
   const int qq = q < N ? q : 0;
   float qh[DH], gd[D], gq[DH];
 #pragma unroll
-  for (int i = 0; i < D; ++i) { qh[i] = ((const float*)a.qw)[(ub + qq) * D + i]; gd[i] = ((const float*)a.dow)[(ub + qq) * D + i]; }
+  for (int i = 0; i < D; ++i) {
+    qh[i] = (float)((const T*)a.qw)[(ub + qq) * D + i];
+    gd[i] = (float)((const T*)a.dow)[(ub + qq) * D + i];
+  }
 #pragma unroll
-  for (int i = 0; i < RP; ++i) qh[D + i] = ((const float*)a.qp)[(int64_t)qq * RP + i];
+  for (int i = 0; i < RP; ++i) qh[D + i] = (float)((const T*)a.qp)[(int64_t)qq * RP + i];
 #pragma unroll
   for (int i = 0; i < DH; ++i) gq[i] = 0.f;
   const float l2 = a.lse2[ub + qq], dq_d = a.dd[ub + qq];
@@ -545,11 +571,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32_kernel(BwdArgs a) {
     const int k0 = t * kTile;
     for (int i = threadIdx.x; i < kTile * DH; i += 256) {
       int r = i / DH, ch = i - r * DH;
-      sK[r][ch] = ch < D ? kw[(int64_t)(k0 + r) * D + ch] : kp[(int64_t)(k0 + r) * RP + ch - D];
+      sK[r][ch] = (float)(ch < D ? kw[(int64_t)(k0 + r) * D + ch] : kp[(int64_t)(k0 + r) * RP + ch - D]);
     }
     for (int i = threadIdx.x; i < kTile * D; i += 256) {
       int r = i / D, ch = i - r * D;
-      sV[r][ch] = vw[(int64_t)(k0 + r) * D + ch];
+      sV[r][ch] = (float)vw[(int64_t)(k0 + r) * D + ch];
     }
     __syncthreads();
     const int nk = min(kTile, N - k0);
@@ -567,9 +593,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_f32_kernel(BwdArgs a) {
     __syncthreads();
   }
   if (q < N) {
-    float* dqw = (float*)a.dqw + (ub + q) * D;
+    T* dqw = (T*)a.dqw + (ub + q) * D;
 #pragma unroll
-    for (int i = 0; i < D; ++i) dqw[i] = gq[i] * a.scale;
+    for (int i = 0; i < D; ++i) dqw[i] = (T)(gq[i] * a.scale);
 #pragma unroll
     for (int i = 0; i < RP; ++i) a.dqp_part[(ub + q) * RP + i] = gq[D + i] * a.scale;
   }
@@ -613,16 +639,17 @@ __global__ __launch_bounds__(256) void reduce_pos_grads_kernel(int units, int N,
 }  // namespace
 
 hipError_t launch_bwd_prep(const Geom& g, int esize, const void* o, const void* d_o, const float* lse, float* dd,
-                           float* lse2, hipStream_t stream) {
+                           float* lse2, bool negate, hipStream_t stream) {
   const int64_t total = (int64_t)g.units * g.n_rows;
   if (total == 0) return hipSuccess;
   dim3 grid((unsigned)((total + 255) / 256));
+  const float sgn = negate ? -1.f : 1.f;
   if (esize == 2)
     hipLaunchKernelGGL(bwd_prep_kernel<bf16>, grid, dim3(256), 0, stream, g, make_pixel_map(g), (const bf16*)o,
-                       (const bf16*)d_o, lse, dd, lse2);
+                       (const bf16*)d_o, lse, dd, lse2, sgn);
   else
     hipLaunchKernelGGL(bwd_prep_kernel<float>, grid, dim3(256), 0, stream, g, make_pixel_map(g), (const float*)o,
-                       (const float*)d_o, lse, dd, lse2);
+                       (const float*)d_o, lse, dd, lse2, sgn);
   return hipGetLastError();
 }
 
@@ -642,21 +669,35 @@ hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd_dkv_f32(const BwdArgs& a, hipStream_t stream) {
-  const int64_t blocks = (int64_t)a.g.units * ((a.g.N + 255) / 256);
+#define RIB_BWD_SIMPLE(K, T, D, RP) \
+  hipLaunchKernelGGL((K<T, D, RP>), dim3((unsigned)blocks), dim3(256), 0, stream, a)
+#define RIB_BWD_SIMPLE_ALL(K)                                                                              \
+  do {                                                                                                     \
+    if (esize == 4) {                                                                                      \
+      if (a.g.d_c == 32) { if (a.rp == 16) RIB_BWD_SIMPLE(K, float, 32, 16); else RIB_BWD_SIMPLE(K, float, 32, 32); } \
+      else { if (a.rp == 16) RIB_BWD_SIMPLE(K, float, 64, 16); else RIB_BWD_SIMPLE(K, float, 64, 32); }                \
+    } else {                                                                                               \
+      if (a.g.d_c == 32) { if (a.rp == 16) RIB_BWD_SIMPLE(K, bf16, 32, 16); else RIB_BWD_SIMPLE(K, bf16, 32, 32); }    \
+      else { if (a.rp == 16) RIB_BWD_SIMPLE(K, bf16, 64, 16); else RIB_BWD_SIMPLE(K, bf16, 64, 32); }                  \
+    }                                                                                                      \
+  } while (0)
+
+hipError_t launch_attn_bwd_dkv_simple(const BwdArgs& a, int esize, hipStream_t stream) {
+  const int kpb = a.g.d_c > 32 ? 128 : 256;   // keys per block (two threads per key at d_c = 64)
+  const int64_t blocks = (int64_t)a.g.units * ((a.g.N + kpb - 1) / kpb);
   if (blocks == 0) return hipSuccess;
-  if (a.rp == 16) hipLaunchKernelGGL(attn_bwd_dkv_f32_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(attn_bwd_dkv_f32_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  RIB_BWD_SIMPLE_ALL(attn_bwd_dkv_simple_kernel);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_bwd_dq_f32(const BwdArgs& a, hipStream_t stream) {
+hipError_t launch_attn_bwd_dq_simple(const BwdArgs& a, int esize, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.g.units * ((a.g.N + 255) / 256);
   if (blocks == 0) return hipSuccess;
-  if (a.rp == 16) hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  else hipLaunchKernelGGL(attn_bwd_dq_f32_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  RIB_BWD_SIMPLE_ALL(attn_bwd_dq_simple_kernel);
   return hipGetLastError();
 }
+#undef RIB_BWD_SIMPLE_ALL
+#undef RIB_BWD_SIMPLE
 
 hipError_t launch_reduce_pos_grads(int units, int N, int n_rows, int r, int rp, const float* part, float* out,
                                    hipStream_t stream) {

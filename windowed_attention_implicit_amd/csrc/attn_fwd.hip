@@ -690,11 +690,12 @@ __global__ __launch_bounds__(256) void rpb_prep_kernel(const float* __restrict__
 }
 
 // ---------------------------------------------------------------------------
-// float32 kernel: one thread per query, K/V tiles of 64 keys in LDS, exact
-// online softmax per tile. Used for float32 runs (correctness-sized work).
-template <int RP>
-__global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
-  constexpr int D = 32;
+// Simple kernel: one thread per query, K/V tiles of 64 keys in LDS, exact online
+// softmax per tile, float32 arithmetic on T (float or bf16) rows with D content
+// channels. It serves float32 runs and content widths the MFMA kernel does not
+// cover (d_c = 64): correctness-sized work.
+template <typename T, int D, int RP>
+__global__ __launch_bounds__(256) void attn_fwd_simple_kernel(FwdArgs a) {
   constexpr int DH = D + RP;
   __shared__ float sK[kKeyTile][DH + 1];
   __shared__ float sV[kKeyTile][D + 1];
@@ -703,17 +704,17 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
   const int nqb = (N + 255) / 256;
   const int unit = blockIdx.x / nqb;
   const int q = (blockIdx.x - unit * nqb) * 256 + threadIdx.x;
-  const float* qw = (const float*)a.qw + (int64_t)unit * n_rows * D;
-  const float* kw = (const float*)a.kw + (int64_t)unit * n_rows * D;
-  const float* vw = (const float*)a.vw + (int64_t)unit * n_rows * D;
-  const float* qp = (const float*)a.qp;
-  const float* kp = (const float*)a.kp;
+  const T* qw = (const T*)a.qw + (int64_t)unit * n_rows * D;
+  const T* kw = (const T*)a.kw + (int64_t)unit * n_rows * D;
+  const T* vw = (const T*)a.vw + (int64_t)unit * n_rows * D;
+  const T* qp = (const T*)a.qp;
+  const T* kp = (const T*)a.kp;
   float qh[DH];
   const int qq = q < N ? q : 0;
 #pragma unroll
-  for (int i = 0; i < D; ++i) qh[i] = qw[(int64_t)qq * D + i];
+  for (int i = 0; i < D; ++i) qh[i] = (float)qw[(int64_t)qq * D + i];
 #pragma unroll
-  for (int i = 0; i < RP; ++i) qh[D + i] = qp[(int64_t)qq * RP + i];
+  for (int i = 0; i < RP; ++i) qh[D + i] = (float)qp[(int64_t)qq * RP + i];
   float o[D];
 #pragma unroll
   for (int i = 0; i < D; ++i) o[i] = 0.f;
@@ -724,11 +725,11 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
     const int k0 = t * kKeyTile;
     for (int i = threadIdx.x; i < kKeyTile * DH; i += 256) {
       int kk = i / DH, ch = i - kk * DH;
-      sK[kk][ch] = ch < D ? kw[(int64_t)(k0 + kk) * D + ch] : kp[(int64_t)(k0 + kk) * RP + ch - D];
+      sK[kk][ch] = ch < D ? (float)kw[(int64_t)(k0 + kk) * D + ch] : (float)kp[(int64_t)(k0 + kk) * RP + ch - D];
     }
     for (int i = threadIdx.x; i < kKeyTile * D; i += 256) {
       int kk = i / D, ch = i - kk * D;
-      sV[kk][ch] = vw[(int64_t)(k0 + kk) * D + ch];
+      sV[kk][ch] = (float)vw[(int64_t)(k0 + kk) * D + ch];
     }
     __syncthreads();
     const int nk = min(kKeyTile, N - k0);
@@ -758,12 +759,12 @@ __global__ __launch_bounds__(256) void attn_fwd_f32_kernel(FwdArgs a) {
     __syncthreads();
   }
   if (q < N) {
-    float* ow = (float*)a.ow + (int64_t)unit * n_rows * D + (int64_t)q * D;
+    T* ow = (T*)a.ow + (int64_t)unit * n_rows * D + (int64_t)q * D;
     const float inv = 1.f / l;
     const PixelMap pm = make_pixel_map(g);
-    const float* gt = a.gate ? (const float*)a.gate + pm.pixel_head(unit, q) * D : nullptr;
+    const T* gt = a.gate ? (const T*)a.gate + pm.pixel_head(unit, q) * D : nullptr;
 #pragma unroll
-    for (int i = 0; i < D; ++i) ow[i] = gt ? o[i] * inv * gt[i] : o[i] * inv;
+    for (int i = 0; i < D; ++i) ow[i] = (T)(gt ? o[i] * inv * (float)gt[i] : o[i] * inv);
     if (a.lse) a.lse[pm.pixel_head(unit, q)] = (m + log2f(l)) * 0.69314718055994530942f;
   }
 }
@@ -825,14 +826,21 @@ hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream) {
+hipError_t launch_attn_fwd_simple(const FwdArgs& a, int esize, hipStream_t stream) {
   const int nqb = (a.g.N + 255) / 256;
   const int64_t blocks = (int64_t)a.g.units * nqb;
   if (blocks == 0) return hipSuccess;
-  if (a.rp == 16)
-    hipLaunchKernelGGL(attn_fwd_f32_kernel<16>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL(attn_fwd_f32_kernel<32>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  const dim3 grid((unsigned)blocks), block(256);
+#define RIB_FWD_SIMPLE(T, D, RP) hipLaunchKernelGGL((attn_fwd_simple_kernel<T, D, RP>), grid, block, 0, stream, a)
+  const int d = a.g.d_c;
+  if (esize == 4) {
+    if (d == 32) { if (a.rp == 16) RIB_FWD_SIMPLE(float, 32, 16); else RIB_FWD_SIMPLE(float, 32, 32); }
+    else { if (a.rp == 16) RIB_FWD_SIMPLE(float, 64, 16); else RIB_FWD_SIMPLE(float, 64, 32); }
+  } else {
+    if (d == 32) { if (a.rp == 16) RIB_FWD_SIMPLE(bf16, 32, 16); else RIB_FWD_SIMPLE(bf16, 32, 32); }
+    else { if (a.rp == 16) RIB_FWD_SIMPLE(bf16, 64, 16); else RIB_FWD_SIMPLE(bf16, 64, 32); }
+  }
+#undef RIB_FWD_SIMPLE
   return hipGetLastError();
 }
 

@@ -50,13 +50,13 @@ hipError_t launch_pack_pos_dual(int N, int n_rows, int r, int rp, const void* in
 struct FwdArgs {
   Geom g;
   float c;              // scale * log2(e)
-  const void* qw;       // [units][n_rows][32] (f32 path)
+  const void* qw;       // [units][n_rows][d_c] (simple path)
   const void* q_map;    // bf16 path: Q_c in the [B, H, W, heads, 32] map
-  const void* kw;       // [units][n_rows][32]
-  const void* vw;       // bf16: [units][32][n_rows] kappa layout; f32: [units][n_rows][32]
+  const void* kw;       // [units][n_rows][d_c]
+  const void* vw;       // MFMA path: [units][32][n_rows] kappa layout; simple path: [units][n_rows][d_c]
   const void* qp;       // [n_rows][rp]
   const void* kp;       // [n_rows][rp]
-  void* ow;             // [units][n_rows][32] (f32 path)
+  void* ow;             // [units][n_rows][d_c] (simple path)
   void* o_map;          // bf16 path: O in the [B, H, W, heads, 32] map
   float* lse;           // [B,H,W,heads] or nullptr
   float* kmax2;         // [units][key_bound_parts(N)] partial maxima of |[k_c | k_p]|^2 (bf16 path)
@@ -73,7 +73,9 @@ struct FwdArgs {
 hipError_t launch_key_bound(const FwdArgs& a, hipStream_t stream);
 int key_bound_parts(int N);
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
-hipError_t launch_attn_fwd_f32(const FwdArgs& a, hipStream_t stream);
+// One thread per query on windowed rows (qw, kw, vw, ow) of esize-byte elements with
+// g.d_c in {32, 64} channels: float32 runs, and bf16 runs with d_c = 64.
+hipError_t launch_attn_fwd_simple(const FwdArgs& a, int esize, hipStream_t stream);
 // RPB comparison kernel: table [heads][(2w-1)^2] float32 -> fp16 log2-unit rows,
 // row maxima and per-key offsets; then the attention (K/V windowed as for bf16).
 int rpb_table_stride(int w);
@@ -101,10 +103,10 @@ struct BwdArgs {
   float scale;
   int rp;
   // windowed inputs
-  const void* qw;       // [units][n_rows][32] rows
-  const void* kw;       // [units][n_rows][32] rows
-  const void* vw;       // [units][n_rows][32] rows
-  const void* dow;      // [units][n_rows][32] rows
+  const void* qw;       // [units][n_rows][d_c] rows
+  const void* kw;       // [units][n_rows][d_c] rows
+  const void* vw;       // [units][n_rows][d_c] rows
+  const void* dow;      // [units][n_rows][d_c] rows
   const void* qt;       // [units][32][n_rows] kappa (bf16 only)
   const void* kt;       // [units][32][n_rows] kappa (bf16 only)
   const void* dot;      // [units][32][n_rows] kappa (bf16 only)
@@ -114,10 +116,10 @@ struct BwdArgs {
   const void* kpt;      // [rp][n_rows] kappa (bf16 only)
   const float* lse2;    // [units][n_rows]  log2-domain LSE
   const float* dd;      // [units][n_rows]  D_i = sum_c dO_ic O_ic
-  // outputs: windowed (float32 path) or in the [B, H, W, heads, 32] map (bf16 path)
-  void* dqw;            // [units][n_rows][32]
-  void* dkw;            // [units][n_rows][32]
-  void* dvw;            // [units][n_rows][32]
+  // outputs: windowed (simple path) or in the [B, H, W, heads, 32] map (bf16 MFMA path)
+  void* dqw;            // [units][n_rows][d_c] (simple path)
+  void* dkw;            // [units][n_rows][d_c] (simple path)
+  void* dvw;            // [units][n_rows][d_c] (simple path)
   void* dq_map;
   void* dk_map;
   void* dv_map;
@@ -125,12 +127,14 @@ struct BwdArgs {
   float* dkp_part;      // [units][n_rows][rp]
 };
 // D and log2-domain LSE in windowed order, from O, dO and LSE in map layout.
+// negate: store -D and -LSE2 (what the bf16 MFMA kernels read); the simple kernels read them as they are
 hipError_t launch_bwd_prep(const Geom& g, int esize, const void* o, const void* d_o, const float* lse,
-                           float* dd, float* lse2, hipStream_t stream);
+                           float* dd, float* lse2, bool negate, hipStream_t stream);
 hipError_t launch_attn_bwd_dkv_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_attn_bwd_dkv_f32(const BwdArgs& a, hipStream_t stream);
-hipError_t launch_attn_bwd_dq_f32(const BwdArgs& a, hipStream_t stream);
+// One thread per key (dkv) / query (dq) on windowed rows of esize-byte elements, d_c in {32, 64}.
+hipError_t launch_attn_bwd_dkv_simple(const BwdArgs& a, int esize, hipStream_t stream);
+hipError_t launch_attn_bwd_dq_simple(const BwdArgs& a, int esize, hipStream_t stream);
 // Fixed-order sum over units of [units][n_rows][rp] partials -> [N][r] float32.
 hipError_t launch_reduce_pos_grads(int units, int N, int n_rows, int r, int rp, const float* part, float* out,
                                    hipStream_t stream);
