@@ -287,6 +287,13 @@ rib_status_t rib_rpb_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype
  * number of timed launches, and forgets them. Disabled by default; while
  * disabled no events are created. The recorded events are process-wide
  * host state guarded by a mutex.
+ *
+ * Each event pair sits between two launches on the stream and costs a few
+ * microseconds of idle GPU there, so a caller that needs one group's launch
+ * time while timing a whole step selects that group alone:
+ * rib_kernel_timing_select(mask) times group k when bit k of mask is set
+ * (0 turns timing off; bits past the last group are RIB_ERR_INVALID_ARG).
+ * rib_kernel_timing_enable(e) selects every group (e != 0) or none.
  */
 typedef enum {
   RIB_KERNEL_POSGEN = 0,       /* the posgen kernel */
@@ -304,6 +311,7 @@ typedef enum {
 } rib_kernel_t;
 
 rib_status_t rib_kernel_timing_enable(int32_t enable);
+rib_status_t rib_kernel_timing_select(uint32_t mask);
 rib_status_t rib_kernel_timing_read(rib_kernel_t kernel, double* total_ms, int64_t* launches);
 
 /* Static text naming a status code. */

@@ -225,3 +225,17 @@ def test_workspace_is_linear_not_quadratic(L):
         N = 96 * 96
         assert big < 2 * 6 * N * N                          # far below one N x N matrix per unit
     assert L.rib_fwd_workspace_size(ctypes.byref(rib.Shape(1, 10, 10, 1, 32, 3, 16)), rib.RIB_BF16) == 0
+
+
+def test_timing_select(L):
+    """Group masks: any subset of the groups is accepted, a bit past the last group is rejected and
+    leaves the previous selection; no events are recorded without a call."""
+    n = len(rib.KERNEL_GROUPS)
+    assert L.rib_kernel_timing_select(1 << rib.KERNEL_GROUPS["attn_fwd"]) == rib.RIB_OK
+    assert L.rib_kernel_timing_select((1 << n) - 1) == rib.RIB_OK
+    assert L.rib_kernel_timing_select(1 << n) == rib.RIB_ERR_INVALID_ARG
+    assert b"past the last" in L.rib_last_error()
+    assert L.rib_kernel_timing_select(0) == rib.RIB_OK
+    assert L.rib_kernel_timing_enable(1) == rib.RIB_OK and L.rib_kernel_timing_enable(0) == rib.RIB_OK
+    rib.kernel_timing_select("attn_fwd", "posgen")
+    rib.kernel_timing_select()

@@ -30,7 +30,7 @@ __all__ = [
     "fwd_workspace_size", "bwd_workspace_size", "FwdPlan", "BwdPlan", "Shape",
     "rpb_window_attn_fwd", "rpb_fwd_workspace_size", "RpbFwdPlan",
     "cla_gate", "window_attn_fwd_gated",
-    "KERNEL_GROUPS", "kernel_timing_enable", "kernel_timing_read",
+    "KERNEL_GROUPS", "kernel_timing_enable", "kernel_timing_select", "kernel_timing_read",
 ]
 
 RIB_OK, RIB_ERR_INVALID_ARG, RIB_ERR_UNSUPPORTED, RIB_ERR_WORKSPACE, RIB_ERR_HIP = range(5)
@@ -75,6 +75,7 @@ _SIGS = {
     "rib_window_attn_fwd_gated": (_i32, [ctypes.POINTER(Shape), _i32, _f32] + [_vp] * 8 + [_vp, _sz, _vp]),
     "rib_rpb_window_attn_fwd": (_i32, [ctypes.POINTER(Shape), _i32, _f32] + [_vp] * 6 + [_vp, _sz, _vp]),
     "rib_kernel_timing_enable": (_i32, [_i32]),
+    "rib_kernel_timing_select": (_i32, [ctypes.c_uint32]),
     "rib_kernel_timing_read": (_i32, [_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]),
     "rib_status_string": (ctypes.c_char_p, [_i32]),
     "rib_last_error": (ctypes.c_char_p, []),
@@ -374,6 +375,14 @@ KERNEL_GROUPS = {"posgen": 0, "partition": 1, "attn_fwd": 2, "unpartition": 3, "
 def kernel_timing_enable(enable: bool = True):
     """Start (or stop) bracketing each kernel group of later calls with HIP events on their stream."""
     _check(lib().rib_kernel_timing_enable(1 if enable else 0))
+
+
+def kernel_timing_select(*groups: str):
+    """Time only the named kernel groups of later calls (none: timing off)."""
+    mask = 0
+    for g in groups:
+        mask |= 1 << KERNEL_GROUPS[g]
+    _check(lib().rib_kernel_timing_select(mask))
 
 
 def kernel_timing_read(group: str):

@@ -205,7 +205,7 @@ BwdLayout bwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
 // ---- kernel timing (measurement aid, off by default)
 struct TimingState {
   std::mutex mu;
-  bool enabled = false;
+  uint32_t mask = 0;   // bit k: group k is timed
   std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[RIB_KERNEL_COUNT];
 };
 
@@ -222,7 +222,7 @@ class TimedGroup {
     TimingState& t = timing();
     {
       std::lock_guard<std::mutex> g(t.mu);
-      if (!t.enabled) return;
+      if (!((t.mask >> (int)k_) & 1u)) return;
     }
     if (hipEventCreate(&a_) != hipSuccess) return;
     if (hipEventCreate(&b_) != hipSuccess) {
@@ -291,9 +291,15 @@ const char* rib_status_string(rib_status_t status) {
 const char* rib_last_error(void) { return g_last_error.c_str(); }
 
 rib_status_t rib_kernel_timing_enable(int32_t enable) {
+  return rib_kernel_timing_select(enable ? (1u << RIB_KERNEL_COUNT) - 1u : 0u);
+}
+
+rib_status_t rib_kernel_timing_select(uint32_t mask) {
+  if (mask >> RIB_KERNEL_COUNT)
+    return fail(RIB_ERR_INVALID_ARG, "timing mask 0x%x names groups past the last (%d)", mask, RIB_KERNEL_COUNT - 1);
   TimingState& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
-  t.enabled = enable != 0;
+  t.mask = mask;
   return ok();
 }
 

@@ -421,27 +421,52 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 // bf16 MFMA kernels they are stored negated (-D, -LSE2: what those kernels add,
 // and the accumulator inputs the dkv kernel takes from LDS as they are); the
 // simple kernels read them unnegated.
-template <typename T>
+// Up to four lanes share a row, each reading 16-byte chunks (a group of lanes covers
+// 64 contiguous bytes per load), and the partial dot products meet by lane shuffles.
+template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, PixelMap pm, const T* __restrict__ o,
                                                        const T* __restrict__ d_o, const float* __restrict__ lse,
                                                        float* __restrict__ dd, float* __restrict__ lse2, float sgn) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  constexpr int kEl = 16 / (int)sizeof(T);     // elements per 16-byte chunk
+  constexpr int kCpr = D / kEl;                // chunks per row
+  constexpr int kL = kCpr < 4 ? kCpr : 4;      // lanes per row
+  constexpr int kCpl = kCpr / kL;              // chunks per lane
+  const int64_t i = ((int64_t)blockIdx.x * blockDim.x + threadIdx.x) / kL;
+  const int sub = threadIdx.x % kL;
   const int64_t total = (int64_t)g.units * g.n_rows;
-  if (i >= total) return;
+  if (i >= total) return;   // the kL lanes of a row leave together
   const int unit = (int)(i / g.n_rows);
   const int t = (int)(i - (int64_t)unit * g.n_rows);
   if (t >= g.N) {
-    dd[i] = 0.f;
-    lse2[i] = sgn * INFINITY;   // P = 0 for padded rows
+    if (sub == 0) {
+      dd[i] = 0.f;
+      lse2[i] = sgn * INFINITY;   // P = 0 for padded rows
+    }
     return;
   }
   const int64_t ph = pm.pixel_head(unit, t);
-  const T* orow = o + ph * g.d_c;
-  const T* grow = d_o + ph * g.d_c;
+  const u32x4* orow = (const u32x4*)(o + ph * D);
+  const u32x4* grow = (const u32x4*)(d_o + ph * D);
   float acc = 0.f;
-  for (int ch = 0; ch < g.d_c; ++ch) acc = fmaf((float)orow[ch], (float)grow[ch], acc);
-  dd[i] = sgn * acc;
-  lse2[i] = sgn * (lse[ph] * 1.44269504088896340736f);
+#pragma unroll
+  for (int j = 0; j < kCpl; ++j) {
+    const u32x4 ov = orow[sub + kL * j], gv = grow[sub + kL * j];
+    if constexpr (sizeof(T) == 2) {
+      const bf16x8 oe = __builtin_bit_cast(bf16x8, ov), ge = __builtin_bit_cast(bf16x8, gv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc = fmaf((float)oe[e], (float)ge[e], acc);
+    } else {
+      const f32x4 oe = __builtin_bit_cast(f32x4, ov), ge = __builtin_bit_cast(f32x4, gv);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc = fmaf(oe[e], ge[e], acc);
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < kL; m <<= 1) acc += __shfl_xor(acc, m);
+  if (sub == 0) {
+    dd[i] = sgn * acc;
+    lse2[i] = sgn * (lse[ph] * 1.44269504088896340736f);
+  }
 }
 
 // ------------------------------------------------------------------ simple kernels
@@ -642,14 +667,19 @@ hipError_t launch_bwd_prep(const Geom& g, int esize, const void* o, const void* 
                            float* lse2, bool negate, hipStream_t stream) {
   const int64_t total = (int64_t)g.units * g.n_rows;
   if (total == 0) return hipSuccess;
-  dim3 grid((unsigned)((total + 255) / 256));
   const float sgn = negate ? -1.f : 1.f;
-  if (esize == 2)
-    hipLaunchKernelGGL(bwd_prep_kernel<bf16>, grid, dim3(256), 0, stream, g, make_pixel_map(g), (const bf16*)o,
-                       (const bf16*)d_o, lse, dd, lse2, sgn);
-  else
-    hipLaunchKernelGGL(bwd_prep_kernel<float>, grid, dim3(256), 0, stream, g, make_pixel_map(g), (const float*)o,
-                       (const float*)d_o, lse, dd, lse2, sgn);
+  const PixelMap pm = make_pixel_map(g);
+  // lanes per row: min(4, 16-byte chunks per row), as in the kernel
+  const int lanes = std::min(4, g.d_c * esize / 16);
+  const dim3 grid((unsigned)((total * lanes + 255) / 256)), block(256);
+#define RIB_PREP(T, D) \
+  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), grid, block, 0, stream, g, pm, (const T*)o, (const T*)d_o, lse, dd, lse2, sgn)
+  if (esize == 2) {
+    if (g.d_c == 32) RIB_PREP(bf16, 32); else RIB_PREP(bf16, 64);
+  } else {
+    if (g.d_c == 32) RIB_PREP(float, 32); else RIB_PREP(float, 64);
+  }
+#undef RIB_PREP
   return hipGetLastError();
 }
 
