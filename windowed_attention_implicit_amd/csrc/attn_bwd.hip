@@ -68,10 +68,13 @@ struct DqTile {
              {16 * KP, 8, kTile / 8 + 1}}};
   }
 };
-// LDS tile rings. dkv (one workgroup per CU by registers) fetches tile t + 3
-// while processing tile t; dq fits two workgroups per CU, which a 3-deep ring
-// (tile t + 2 in flight) keeps within the 160 KB of LDS.
-constexpr int kBufsDkv = 4;
+// LDS tile rings. dkv at r <= 16 fits two workgroups per CU by registers (two
+// waves per SIMD), which a 2-deep ring (tile t + 1 in flight) keeps within the
+// 160 KB of LDS; at r <= 32 it has one workgroup per CU and fetches tile t + 3
+// while processing tile t. dq fits two workgroups per CU with a 3-deep ring
+// (tile t + 2 in flight).
+template <int KP>
+constexpr int kBufsDkv = KP == 1 ? 2 : 4;
 constexpr int kBufsDq = 3;
 
 // Workgroup barrier without the release fence of __syncthreads, which would
@@ -103,15 +106,43 @@ __device__ __forceinline__ bf16x8 token_frag(const bf16* content, const bf16* po
   return __builtin_bit_cast(bf16x8, v);
 }
 
+// Positional gradients at r = 16 on v_mfma_f32_16x16x32_bf16. A 32-key (dkv) or
+// 32-query (dq) column block's dS leaves the score layout as sb[2]: lane l holds, for
+// column l % 32, the 16 contraction indices 16 s + 8 (j / 4) + 4 h + j % 4 (h = l / 32,
+// j < 8) of the sub-tile. Swapping the odd 16-lane rows of sb[1] with the even rows of
+// sb[0] (v_permlane16_swap) leaves two B operands of 16 columns each: b[0] columns 0-15,
+// b[1] columns 16-31, and in both, k-block l / 16 = 0, 1, 2, 3 holds (s, h) = (1, 0),
+// (0, 0), (1, 1), (0, 1). In the channel-major kappa copy those indices are the 16-byte
+// chunk 2 s + h of the sub-tile, so the A fragment of lane l is chunk pos16_chunk(l) of
+// channel l % 16.
+__device__ __forceinline__ int pos16_chunk(int lane) {
+  const int kb = lane >> 4;
+  return 2 * (1 - (kb & 1)) + (kb >> 1);
+}
+
+__device__ __forceinline__ void pos16_b(const bf16x8 (&sb)[2], bf16x8 (&b)[2]) {
+  const u32x4 x = __builtin_bit_cast(u32x4, sb[1]), y = __builtin_bit_cast(u32x4, sb[0]);
+  u32x4 bx, by;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const auto r = __builtin_amdgcn_permlane16_swap(x[d], y[d], false, false);
+    bx[d] = r[0];
+    by[d] = r[1];
+  }
+  b[0] = __builtin_bit_cast(bf16x8, bx);
+  b[1] = __builtin_bit_cast(bf16x8, by);
+}
+
 // ------------------------------------------------------------------ dK, dV
 template <int KP>
-__global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   typedef BwdCfg<KP> C;
   typedef DkvTile<KP> LP;
   constexpr auto L = LP::get();
   constexpr int oQc = L.offset(0), oQp = L.offset(1), oDo = L.offset(2), oQt = L.offset(3), oQpt = L.offset(4),
                 oDot = L.offset(5), oL = L.offset(6), oD = L.offset(7);
-  __shared__ u32x4 sT[kBufsDkv][L.chunks()];
+  constexpr int kBufs = kBufsDkv<KP>, kAhead = kBufs - 1;   // tiles in flight ahead of the current one
+  __shared__ u32x4 sT[kBufs][L.chunks()];
 
   const Geom& g = a.g;
   const int N = g.N, n_rows = g.n_rows;
@@ -152,11 +183,16 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
                      : zero_frag();
   }
 
+  // acc_dkp: KP = 2, dK_p^T on 32x32 tiles; KP = 1, its 16 channels on two 16x16 tiles per
+  // column block (keys 0-15 / 16-31 of the block), 8 registers instead of 16
   f32x16 acc_dv[2], acc_dk[2], acc_dkp[2];
+  f32x4 acc_dkp16[2][2];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) { acc_dv[nb][i] = 0.f; acc_dk[nb][i] = 0.f; acc_dkp[nb][i] = 0.f; }
+    acc_dkp16[nb][0] = acc_dkp16[nb][1] = f32x4(0.f);
+  }
 
   // query tiles reach LDS by DMA (buffer_load ... lds), three tiles ahead
   const int row64 = n_rows * 64, nb2 = n_rows * 2, pos_bytes = n_rows * rp * 2;
@@ -170,15 +206,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
 
   const float c = a.c;
   const int nqt = (N + kTile - 1) / kTile;
-  tile_dma_issue<LP>(dma, wave, 0, sT[0]);
-  tile_dma_issue<LP>(dma, wave, min(1, nqt - 1), sT[1]);
-  tile_dma_issue<LP>(dma, wave, min(2, nqt - 1), sT[2]);
-  tile_dma_wait<LP, 2>(wave);
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) tile_dma_issue<LP>(dma, wave, min(i, nqt - 1), sT[i]);
+  tile_dma_wait<LP, kAhead - 1>(wave);
   __syncthreads();
   for (int t = 0; t < nqt; ++t) {
-    // tile t + 3 (the last tile again past the end) into the buffer tile t - 1 used
-    tile_dma_issue<LP>(dma, wave, min(t + 3, nqt - 1), sT[(t + 3) % kBufsDkv]);
-    const u32x4* T = sT[t % kBufsDkv];
+    // tile t + kAhead (the last tile again past the end) into the buffer tile t - 1 used
+    tile_dma_issue<LP>(dma, wave, min(t + kAhead, nqt - 1), sT[(t + kAhead) % kBufs]);
+    const u32x4* T = sT[t % kBufs];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int row = sub * 32 + l32;
@@ -205,8 +240,11 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
         const int ch = 4 * sub + 2 * s + half;
         dta[s] = lds_frag(&T[oDot + l32 * C::kTRow + ch]);
         qta[s] = lds_frag(&T[oQt + l32 * C::kTRow + ch]);
-        qpta[s] = l32 < C::kPosRows ? lds_frag(&T[oQpt + l32 * C::kTRow + ch]) : zero_frag();
+        if constexpr (KP == 2) qpta[s] = lds_frag(&T[oQpt + l32 * C::kTRow + ch]);
       }
+      // KP = 1: A of the 16x16x32 dK_p MFMA, channel lane % 16, the sub-tile's queries of
+      // k-block lane / 16 in the order pos16_b() leaves dS in
+      if constexpr (KP == 1) qpta[0] = lds_frag(&T[oQpt + (lane & 15) * C::kTRow + 4 * sub + pos16_chunk(lane)]);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         // sc = S' - LSE2 (log2 domain), dp = dP - D
@@ -229,11 +267,19 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
         for (int s = 0; s < 2; ++s) {
           acc_dv[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dta[s], pb[s], acc_dv[nb], 0, 0, 0);
           acc_dk[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qta[s], sb[s], acc_dk[nb], 0, 0, 0);
-          acc_dkp[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qpta[s], sb[s], acc_dkp[nb], 0, 0, 0);
+          if constexpr (KP == 2)
+            acc_dkp[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qpta[s], sb[s], acc_dkp[nb], 0, 0, 0);
+        }
+        if constexpr (KP == 1) {
+          bf16x8 b16[2];
+          pos16_b(sb, b16);
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            acc_dkp16[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qpta[0], b16[m], acc_dkp16[nb][m], 0, 0, 0);
         }
       }
     }
-    tile_dma_wait<LP, 2>(wave);   // tile t + 1 landed (this wave's part); t + 2, t + 3 may be in flight
+    tile_dma_wait<LP, kAhead - 1>(wave);   // tile t + 1 landed (this wave's part); later ones may be in flight
     barrier_dma();
   }
 
@@ -262,13 +308,23 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
       const int64_t row = map_base + (int64_t)(key / g.w) * row_elems + (int64_t)(key % g.w) * pix_elems;
       *(uint2*)(dvm + row + ch) = *(const uint2*)v4;
       *(uint2*)(dkm + row + ch) = *(const uint2*)k4;
-      if (ch < rp) {
+      if (KP == 2) {
         f32x4 p4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) p4[i] = acc_dkp[nb][4 * gq + i] * scale;
         *(f32x4*)(dkp + (int64_t)key * rp + ch) = p4;
       }
     }
+  }
+  if constexpr (KP == 1) {
+    // 16x16 tiles: lane holds channels 4 (lane / 16) + i of key 16 m + lane % 16 of the block
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int key = k0 + nb * 32 + 16 * m + (lane & 15);
+        if (key < N) *(f32x4*)(dkp + (int64_t)key * rp + 4 * (lane >> 4)) = acc_dkp16[nb][m] * scale;
+      }
   }
 }
 
@@ -320,11 +376,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     ndq[nb] = ok ? a.dd[ub + q] : 0.f;
   }
 
+  // acc_dqp: as acc_dkp in dkv (16x16 tiles at KP = 1)
   f32x16 acc_dq[2], acc_dqp[2];
+  f32x4 acc_dqp16[2][2];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb)
+  for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) { acc_dq[nb][i] = 0.f; acc_dqp[nb][i] = 0.f; }
+    acc_dqp16[nb][0] = acc_dqp16[nb][1] = f32x4(0.f);
+  }
 
   // key tiles reach LDS by DMA (buffer_load ... lds), two tiles ahead
   const int row64 = n_rows * 64, nb2 = n_rows * 2, pos_bytes = n_rows * rp * 2;
@@ -358,8 +418,9 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
         va[s] = lds_frag(&T[oV + row * C::kCRow + 2 * s + half]);
         const int ch = 4 * sub + 2 * s + half;
         kta[s] = lds_frag(&T[oKt + l32 * C::kTRow + ch]);
-        kpta[s] = l32 < C::kPosRows ? lds_frag(&T[oKpt + l32 * C::kTRow + ch]) : zero_frag();
+        if constexpr (KP == 2) kpta[s] = lds_frag(&T[oKpt + l32 * C::kTRow + ch]);
       }
+      if constexpr (KP == 1) kpta[0] = lds_frag(&T[oKpt + (lane & 15) * C::kTRow + 4 * sub + pos16_chunk(lane)]);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         // one query per lane: -LSE2 and -D are lane constants, added by one vector add each
@@ -380,7 +441,15 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           acc_dq[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kta[s], sb[s], acc_dq[nb], 0, 0, 0);
-          acc_dqp[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kpta[s], sb[s], acc_dqp[nb], 0, 0, 0);
+          if constexpr (KP == 2)
+            acc_dqp[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kpta[s], sb[s], acc_dqp[nb], 0, 0, 0);
+        }
+        if constexpr (KP == 1) {
+          bf16x8 b16[2];
+          pos16_b(sb, b16);
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+            acc_dqp16[nb][m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kpta[0], b16[m], acc_dqp16[nb][m], 0, 0, 0);
         }
       }
     }
@@ -406,13 +475,23 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
       const int ch = 8 * gq + 4 * half;
       *(uint2*)(dqm + map_base + (int64_t)(q / g.w) * row_elems + (int64_t)(q % g.w) * pix_elems + ch) =
           *(const uint2*)q4;
-      if (ch < rp) {
+      if (KP == 2) {
         f32x4 p4;
 #pragma unroll
         for (int i = 0; i < 4; ++i) p4[i] = acc_dqp[nb][4 * gq + i] * scale;
         *(f32x4*)(dqp + (int64_t)q * rp + ch) = p4;
       }
     }
+  }
+  if constexpr (KP == 1) {
+    // 16x16 tiles: lane holds channels 4 (lane / 16) + i of query 16 m + lane % 16 of the block
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const int q = q0 + nb * 32 + 16 * m + (lane & 15);
+        if (q < N) *(f32x4*)(dqp + (int64_t)q * rp + 4 * (lane >> 4)) = acc_dqp16[nb][m] * scale;
+      }
   }
 }
 
