@@ -377,12 +377,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   }
 
   // acc_dqp: as acc_dkp in dkv (16x16 tiles at KP = 1)
-  f32x16 acc_dq[2], acc_dqp[2];
+  f32x16 acc_dq[2], acc_dqp[2], cl[2];
   f32x4 acc_dqp16[2][2];
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { acc_dq[nb][i] = 0.f; acc_dqp[nb][i] = 0.f; }
+    for (int i = 0; i < 16; ++i) { acc_dq[nb][i] = 0.f; acc_dqp[nb][i] = 0.f; cl[nb][i] = nlq[nb]; }
     acc_dqp16[nb][0] = acc_dqp16[nb][1] = f32x4(0.f);
   }
 
@@ -423,9 +423,10 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
       if constexpr (KP == 1) kpta[0] = lds_frag(&T[oKpt + (lane & 15) * C::kTRow + 4 * sub + pos16_chunk(lane)]);
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        // one query per lane: -LSE2 and -D are lane constants, added by one vector add each
-        // (as accumulator inputs they would take 64 more registers than the kernel has)
-        f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[nb][0], f32x16(0.f), 0, 0, 0);
+        // one query per lane: -LSE2 enters as the score MFMA's accumulator input (a lane
+        // constant, 32 registers for both column blocks); -D is added by one vector add (as
+        // an accumulator input it would take 32 registers more than two waves per SIMD allow)
+        f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[nb][0], cl[nb], 0, 0, 0);
 #pragma unroll
         for (int s = 1; s < C::kSteps; ++s) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[nb][s], sc, 0, 0, 0);
         f32x16 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], df[nb][0], f32x16(0.f), 0, 0, 0);
@@ -436,7 +437,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int v = 8 * s + j;
-            sb[s][j] = f32_to_bf16(__builtin_amdgcn_exp2f(sc[v] + nlq[nb]) * (dp[v] + ndq[nb]));
+            sb[s][j] = f32_to_bf16(__builtin_amdgcn_exp2f(sc[v]) * (dp[v] + ndq[nb]));
           }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
