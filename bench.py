@@ -407,10 +407,10 @@ def main():
     tflops = flops / ms / 1e9
     attn_tflops = flops / attn_ms / 1e9
     tensor_bytes = wl.B * wl.H * wl.W * wl.heads * wl.d_c * 2
-    # the gathers of K and V (read + write each) and the key-norm bound, which reads the windowed K_c once
-    # more; Q_c is read and O written in the map layout by the attention kernel itself, and Q_p, K_p are
-    # read in place unless r needs padding to 16 or 32 (then they are packed: read + write each)
-    part_bytes = 5 * tensor_bytes + (0 if wl.r in (16, 32) else 4 * wl.N * wl.r * 2)
+    # one pass gathers K and V (read + write each) and takes the key-norm maxima from the K_c it moves;
+    # Q_c is read and O written in the map layout by the attention kernel itself, and Q_p, K_p are read
+    # in place unless r needs padding to 16 or 32 (then they are packed: read + write each)
+    part_bytes = 4 * tensor_bytes + (0 if wl.r in (16, 32) else 4 * wl.N * wl.r * 2)
     pg_bytes = 4 * (wl.hidden * 4 * wl.n_freq + 2 * wl.r * wl.hidden) + 2 * wl.N * wl.r * 2
     rec = counter_record()
     traffic = rec and rec.get("hbm_bytes_per_launch")
@@ -453,7 +453,7 @@ def main():
                           "frac_hbm": round(part_bytes / part_ms / 1e6 / PEAK_HBM_GBS, 3),
                           "cold_ms": round(cold["partition"], 5),
                           "cold_GB/s": round(part_bytes / cold["partition"] / 1e6, 1),
-                          "note": "GB/s over one read + one write of K_c and V and the key-norm read of K_c; "
+                          "note": "GB/s over one read + one write of K_c and V (the key-norm maxima come from the same pass); "
                                   "cold_* with the 256 MB MALL flushed before each call"},
             "attn_fwd": {"ms": round(attn_ms, 5), "TFLOP/s": round(attn_tflops, 1)},
             "unpartition": ({"ms": None, "note": "none: O rows are written in the map layout by the attention "

@@ -224,8 +224,10 @@ class TimedGroup {
       std::lock_guard<std::mutex> g(t.mu);
       if (!((t.mask >> (int)k_) & 1u)) return;
     }
-    if (hipEventCreate(&a_) != hipSuccess) return;
-    if (hipEventCreate(&b_) != hipSuccess) {
+    // timing-only events: no system-scope fence (an L2 write-back and invalidate at every
+    // record, which would idle the GPU between the launches being timed)
+    if (hipEventCreateWithFlags(&a_, hipEventDisableSystemFence) != hipSuccess) return;
+    if (hipEventCreateWithFlags(&b_, hipEventDisableSystemFence) != hipSuccess) {
       (void)hipEventDestroy(a_);
       return;
     }
@@ -467,29 +469,33 @@ static rib_status_t attn_fwd_impl(const rib_shape_t* shape, rib_dtype_t dtype, f
     hipError_t e;
     const bool bf = mfma_path(g, dtype);
     TimedGroup t_part(RIB_KERNEL_PARTITION, st);
-    if (!bf && (e = launch_partition(g, es, WinLayout::kRows, q_c, L.qw, st)) != hipSuccess)
-      return hip_fail(e, "partition q");
-    if ((e = launch_partition(g, es, WinLayout::kRows, k_c, L.kw, st)) != hipSuccess) return hip_fail(e, "partition k");
-    if ((e = launch_partition(g, es, bf ? WinLayout::kTransKappa : WinLayout::kRows, v, L.vw, st)) != hipSuccess)
-      return hip_fail(e, "partition v");
-    if (L.qp) {
+    if (L.qp) {   // positional rows padded to rp (the fused gather below reads K_p)
       if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, q_p, es, L.qp, st)) != hipSuccess)
         return hip_fail(e, "pack q_p");
       if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, k_p, es, L.kp, st)) != hipSuccess)
         return hip_fail(e, "pack k_p");
+    }
+    const void* kp_rows = L.kp ? L.kp : k_p;
+    if (bf) {
+      // K_c rows, V^T kappa and the key-norm partial maxima in one pass
+      if ((e = launch_gather_kv_bound(g, rp, k_c, v, kp_rows, L.kw, L.vw, L.kmax2, st)) != hipSuccess)
+        return hip_fail(e, "partition k, v");
+    } else {
+      if ((e = launch_partition(g, es, WinLayout::kRows, q_c, L.qw, st)) != hipSuccess) return hip_fail(e, "partition q");
+      if ((e = launch_partition(g, es, WinLayout::kRows, k_c, L.kw, st)) != hipSuccess) return hip_fail(e, "partition k");
+      if ((e = launch_partition(g, es, WinLayout::kRows, v, L.vw, st)) != hipSuccess) return hip_fail(e, "partition v");
     }
     FwdArgs a;
     a.g = g;
     a.c = resolve_scale(scale, shape) * kLog2e;
     a.qw = L.qw; a.kw = L.kw; a.vw = L.vw; a.ow = L.ow;
     a.qp = L.qp ? L.qp : q_p;
-    a.kp = L.kp ? L.kp : k_p;
+    a.kp = kp_rows;
     a.q_map = q_c; a.o_map = o;
     a.lse = lse;
     a.kmax2 = L.kmax2;
     a.rp = rp;
     a.gate = gate;
-    if (bf && (e = launch_key_bound(a, st)) != hipSuccess) return hip_fail(e, "key bound");
     t_part.end();
     TimedGroup t_attn(RIB_KERNEL_ATTN_FWD, st);
     e = bf ? launch_attn_fwd_bf16(a, st) : launch_attn_fwd_simple(a, es, st);
@@ -590,9 +596,9 @@ rib_status_t rib_rpb_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype
     hipStream_t st = (hipStream_t)stream;
     hipError_t e;
     TimedGroup t_part(RIB_KERNEL_PARTITION, st);
-    if ((e = launch_partition(g, 2, WinLayout::kRows, k_c, L.kw, st)) != hipSuccess) return hip_fail(e, "partition k");
-    if ((e = launch_partition(g, 2, WinLayout::kTransKappa, v, L.vw, st)) != hipSuccess)
-      return hip_fail(e, "partition v");
+    // K_c rows, V^T kappa and the key-norm partial maxima (no positional part) in one pass
+    if ((e = launch_gather_kv_bound(g, 0, k_c, v, nullptr, L.kw, L.vw, L.kmax2, st)) != hipSuccess)
+      return hip_fail(e, "partition k, v");
     if ((e = launch_rpb_prep(g, table, L.tab16, L.tmax, L.kidx, st)) != hipSuccess) return hip_fail(e, "rpb prep");
     FwdArgs a;
     a.g = g;
@@ -603,7 +609,6 @@ rib_status_t rib_rpb_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype
     a.kmax2 = L.kmax2;
     a.rp = 0;
     a.rpb_tab16 = L.tab16; a.rpb_max = L.tmax; a.rpb_kidx = L.kidx; a.rpb_stride = rpb_table_stride(g.w);
-    if ((e = launch_key_bound(a, st)) != hipSuccess) return hip_fail(e, "key bound");
     t_part.end();
     TimedGroup t_attn(RIB_KERNEL_RPB_ATTN_FWD, st);
     if ((e = launch_attn_fwd_rpb(a, st)) != hipSuccess) return hip_fail(e, "rpb attention forward");

@@ -49,7 +49,7 @@ constexpr int kQPerWave = 64;             // two 32-query MFMA column blocks
 constexpr int kKeyTile = 64;
 constexpr float kLazyTau = 8.0f;          // log2 units
 constexpr float kUnderflowGuard = 8.673617379884035e-19f;  // 2^-60
-constexpr int kKeyBoundTile = 256;        // keys per partial key-norm maximum
+constexpr int kKeyBoundTile = 64;         // keys per partial key-norm maximum (one per gather block)
 
 // s_waitcnt immediates (gfx9 encoding) waiting on the vector-memory counter
 // only: vmcnt in bits 3:0, expcnt (7) and lgkmcnt (15) left at their maxima.
@@ -619,43 +619,6 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
   }
 }
 
-// Partial key-norm maxima: block (unit, part) writes max over its kKeyBoundTile
-// keys of |[k_c | k_p]|^2 (float32) to kmax2[unit * parts + part].
-__global__ __launch_bounds__(kKeyBoundTile) void key_bound_kernel(int N, int n_rows, int rp, int parts,
-                                                                  const bf16* __restrict__ kw,
-                                                                  const bf16* __restrict__ kp,
-                                                                  float* __restrict__ kmax2) {
-  __shared__ float red[kKeyBoundTile / 64];
-  const int unit = blockIdx.x / parts;
-  const int part = blockIdx.x - unit * parts;
-  const int t = part * kKeyBoundTile + threadIdx.x;
-  float s = 0.f;
-  if (t < N) {
-    const bf16* kr = kw + ((int64_t)unit * n_rows + t) * 32;
-#pragma unroll
-    for (int c4 = 0; c4 < 4; ++c4) {
-      const bf16x8 v = __builtin_bit_cast(bf16x8, *(const u32x4*)(kr + c4 * 8));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s = fmaf((float)v[j], (float)v[j], s);
-    }
-    for (int c4 = 0; c4 < rp / 8; ++c4) {
-      const bf16x8 v = __builtin_bit_cast(bf16x8, *(const u32x4*)(kp + (int64_t)t * rp + c4 * 8));
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s = fmaf((float)v[j], (float)v[j], s);
-    }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) s = fmaxf(s, __shfl_xor(s, o));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float m = red[0];
-#pragma unroll
-    for (int w = 1; w < kKeyBoundTile / 64; ++w) m = fmaxf(m, red[w]);
-    kmax2[blockIdx.x] = m;
-  }
-}
-
 // RPB preparation. Block h < heads converts table row h to fp16 in log2 units
 // (zero-padded to `stride` entries) and writes its maximum; block `heads`
 // writes the per-key byte offsets -2 ((k / w)(2w - 1) + k % w) for k < N and
@@ -770,14 +733,6 @@ __global__ __launch_bounds__(256) void attn_fwd_simple_kernel(FwdArgs a) {
 }
 
 }  // namespace
-
-hipError_t launch_key_bound(const FwdArgs& a, hipStream_t stream) {
-  if (a.g.units == 0) return hipSuccess;
-  const int parts = (a.g.N + kKeyBoundTile - 1) / kKeyBoundTile;
-  hipLaunchKernelGGL(key_bound_kernel, dim3(a.g.units * parts), dim3(kKeyBoundTile), 0, stream, a.g.N, a.g.n_rows,
-                     a.rp, parts, (const bf16*)a.kw, (const bf16*)a.kp, a.kmax2);
-  return hipGetLastError();
-}
 
 int key_bound_parts(int N) { return (N + kKeyBoundTile - 1) / kKeyBoundTile; }
 

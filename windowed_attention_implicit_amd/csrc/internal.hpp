@@ -30,6 +30,10 @@ size_t posgen_bwd_workspace_bytes(int w, const rib_mlp_t& mlp);
 hipError_t launch_partition(const Geom& g, int esize, WinLayout layout, const void* x, void* xw,
                             hipStream_t stream);
 // bf16, d = 32: x -> both the kRows and the kTransKappa buffer in one pass.
+// bf16, d_c = 32: K_c -> rows, V -> kappa, and the per-64-key partial maxima of
+// |[k_c | k_p]|^2 (kp: [N][rp] rows, rp = 0 for none) in one pass.
+hipError_t launch_gather_kv_bound(const Geom& g, int rp, const void* k, const void* v, const void* kp, void* kw,
+                                  void* vt, float* kmax2, hipStream_t stream);
 hipError_t launch_partition_rows_kappa(const Geom& g, const void* x, void* xw_rows, void* xw_kappa,
                                        hipStream_t stream);
 // windowed kRows buffer -> x [B,H,W,heads,d].
@@ -69,8 +73,7 @@ struct FwdArgs {
   // optional CLA gate [B, H, W, heads, d_c] (same dtype as O): O' = O * G in the epilogue
   const void* gate = nullptr;
 };
-// Per-unit key-norm bound used by the bf16 forward (reads kw and kp, writes kmax2).
-hipError_t launch_key_bound(const FwdArgs& a, hipStream_t stream);
+// Partial key-norm maxima per unit of the bf16 forward: one per 64 keys.
 int key_bound_parts(int N);
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
 // One thread per query on windowed rows (qw, kw, vw, ow) of esize-byte elements with

@@ -107,6 +107,65 @@ __global__ __launch_bounds__(256) void gather_trans_kappa_kernel(PixelMap pm, in
   *(u32x4*)(xt + ((int64_t)u * 32 + d) * n_rows + g0 + pc * 8) = *(const u32x4*)vals;
 }
 
+// The bf16 forward's whole preparation in one pass. Block (unit, 64-token group):
+// K_c rows -> the token-major rows layout [units][n_rows][32] (rows >= N zero), V ->
+// the channel-major kappa layout (as gather_trans_kappa_kernel), and the group's
+// largest |[k_c | k_p]|^2 -> kmax2[unit * groups + group], the per-key-tile partial
+// maxima from which the attention kernel forms its softmax bound (K_p rows have rp
+// channels, rp = 0 for no positional part). The K_c norms come from the registers
+// that carry the rows, so K_c is read once.
+__global__ __launch_bounds__(256) void gather_kv_bound_kernel(PixelMap pm, int N, int n_rows, int rp,
+                                                              const bf16* __restrict__ k, const bf16* __restrict__ v,
+                                                              const bf16* __restrict__ kp, bf16* __restrict__ kw,
+                                                              bf16* __restrict__ vt, float* __restrict__ kmax2) {
+  __shared__ bf16 tile[64][32 + 2];
+  __shared__ float red[4];
+  const int groups = n_rows / 64;
+  const int u = blockIdx.x / groups;
+  const int gi = blockIdx.x - u * groups;
+  const int g0 = gi * 64;
+  const int tid = threadIdx.x;
+  {
+    const int tok = tid >> 2, c = tid & 3;
+    const int t = g0 + tok;
+    const int64_t ph = t < N ? pm.pixel_head(u, t) : 0;
+    u32x4 kv = u32x4(0u), vv = u32x4(0u);
+    if (t < N) {
+      kv = *(const u32x4*)(k + ph * 32 + c * 8);
+      vv = *(const u32x4*)(v + ph * 32 + c * 8);
+    }
+    *(u32x4*)(kw + ((int64_t)u * n_rows + t) * 32 + c * 8) = kv;
+    float ss = 0.f;
+    const bf16x8 ke = __builtin_bit_cast(bf16x8, kv);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) ss = fmaf((float)ke[j], (float)ke[j], ss);
+    if (t < N && c * 8 < rp) {   // rp <= 32: at most one positional chunk per lane
+      const bf16x8 pe = __builtin_bit_cast(bf16x8, *(const u32x4*)(kp + (int64_t)t * rp + c * 8));
+#pragma unroll
+      for (int j = 0; j < 8; ++j) ss = fmaf((float)pe[j], (float)pe[j], ss);
+    }
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);   // the token's |k_hat|^2 in its 4 lanes
+#pragma unroll
+    for (int o = 4; o < 64; o <<= 1) ss = fmaxf(ss, __shfl_xor(ss, o));
+    if ((tid & 63) == 0) red[tid >> 6] = ss;
+    const bf16* pv = (const bf16*)&vv;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) tile[tok][c * 8 + j] = pv[j];
+  }
+  __syncthreads();
+  if (tid == 0) kmax2[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const int d = tid >> 3, pc = tid & 7;
+  bf16 vals[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int p = pc * 8 + j;
+    const int tok = (p & ~15) | kappa16(p & 15);
+    vals[j] = tile[tok][d];
+  }
+  *(u32x4*)(vt + ((int64_t)u * 32 + d) * n_rows + g0 + pc * 8) = *(const u32x4*)vals;
+}
+
 template <typename InT, typename OutT>
 __global__ void pack_pos_kernel(int N, int n_rows, int r, int rp, const InT* __restrict__ in, OutT* __restrict__ out) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -156,6 +215,15 @@ hipError_t launch_partition(const Geom& g, int esize, WinLayout layout, const vo
     hipLaunchKernelGGL(gather_trans_kappa_kernel, dim3((unsigned)((int64_t)g.units * (g.n_rows / 64))), dim3(256), 0,
                        stream, make_pixel_map(g), g.N, g.n_rows, (const bf16*)x, (bf16*)xw, (bf16*)nullptr);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_kv_bound(const Geom& g, int rp, const void* k, const void* v, const void* kp, void* kw,
+                                  void* vt, float* kmax2, hipStream_t stream) {
+  if (g.units == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_kv_bound_kernel, dim3((unsigned)((int64_t)g.units * (g.n_rows / 64))), dim3(256), 0,
+                     stream, make_pixel_map(g), g.N, g.n_rows, rp, (const bf16*)k, (const bf16*)v, (const bf16*)kp,
+                     (bf16*)kw, (bf16*)vt, kmax2);
   return hipGetLastError();
 }
 
