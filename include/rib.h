@@ -219,8 +219,9 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
  *   dW1 = sum_t dz phi^T, db1 = sum_t dz.
  * Outputs are overwritten, not accumulated. Deterministic: up to 1024 blocks
  * each sum a fixed set of token tiles (up to 32 tokens) into their own slot of
- * the workspace, and a second kernel adds the slots in block order. Float32
- * throughout.
+ * the workspace, and a second kernel adds the slots in a fixed order (four
+ * contiguous ranges of blocks, each in block order, then the four range sums
+ * in order). Float32 throughout.
  *
  *   w, mlp      as for rib_posgen (same limits; b1 / b2 may be NULL for zeros);
  *               W1, b1, W2 and one token's tile, staged in LDS, must fit 64 KB
