@@ -481,9 +481,9 @@ static rib_status_t attn_fwd_impl(const rib_shape_t* shape, rib_dtype_t dtype, f
       if ((e = launch_gather_kv_bound(g, rp, k_c, v, kp_rows, L.kw, L.vw, L.kmax2, st)) != hipSuccess)
         return hip_fail(e, "partition k, v");
     } else {
-      if ((e = launch_partition(g, es, WinLayout::kRows, q_c, L.qw, st)) != hipSuccess) return hip_fail(e, "partition q");
-      if ((e = launch_partition(g, es, WinLayout::kRows, k_c, L.kw, st)) != hipSuccess) return hip_fail(e, "partition k");
-      if ((e = launch_partition(g, es, WinLayout::kRows, v, L.vw, st)) != hipSuccess) return hip_fail(e, "partition v");
+      if ((e = launch_partition(g, es, q_c, L.qw, st)) != hipSuccess) return hip_fail(e, "partition q");
+      if ((e = launch_partition(g, es, k_c, L.kw, st)) != hipSuccess) return hip_fail(e, "partition k");
+      if ((e = launch_partition(g, es, v, L.vw, st)) != hipSuccess) return hip_fail(e, "partition v");
     }
     FwdArgs a;
     a.g = g;
@@ -665,25 +665,32 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
   } while (0)
     TimedGroup t_part(RIB_KERNEL_PARTITION, st);
     if (bf) {
-      // Q_c, K_c and dO are needed in both windowed layouts: one pass over the map each
-      RIB_LAUNCH(launch_partition_rows_kappa(g, q_c, L.qw, L.qt, st), "partition q");
-      RIB_LAUNCH(launch_partition_rows_kappa(g, k_c, L.kw, L.kt, st), "partition k");
-      RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, v, L.vw, st), "partition v");
-      RIB_LAUNCH(launch_partition_rows_kappa(g, d_o, L.dow, L.dot, st), "partition do");
-      RIB_LAUNCH(launch_pack_pos_dual(g.N, g.n_rows, g.r, rp, q_p, L.qp, L.qpt, st), "pack q_p");
-      RIB_LAUNCH(launch_pack_pos_dual(g.N, g.n_rows, g.r, rp, k_p, L.kp, L.kpt, st), "pack k_p");
+      // one pass: Q_c, K_c, dO into both windowed layouts, V into rows, -D and -LSE2 per
+      // row, and the positional rows with their kappa transposes
+      BwdGather ga;
+      ga.pm = make_pixel_map(g);
+      ga.N = g.N; ga.n_rows = g.n_rows; ga.r = g.r; ga.rp = rp;
+      ga.q = (const bf16*)q_c; ga.k = (const bf16*)k_c; ga.v = (const bf16*)v;
+      ga.d_o = (const bf16*)d_o; ga.o = (const bf16*)o; ga.lse = lse;
+      ga.q_p = (const bf16*)q_p; ga.k_p = (const bf16*)k_p;
+      ga.qw = (bf16*)L.qw; ga.qt = (bf16*)L.qt; ga.kw = (bf16*)L.kw; ga.kt = (bf16*)L.kt;
+      ga.vw = (bf16*)L.vw; ga.dow = (bf16*)L.dow; ga.dot = (bf16*)L.dot;
+      ga.dd = L.dd; ga.lse2 = L.lse2;
+      ga.qp = (bf16*)L.qp; ga.qpt = (bf16*)L.qpt; ga.kp = (bf16*)L.kp; ga.kpt = (bf16*)L.kpt;
+      RIB_LAUNCH(launch_gather_bwd(ga, g.units, st), "backward gather");
+      t_part.end();
     } else {
-      RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, q_c, L.qw, st), "partition q");
-      RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, k_c, L.kw, st), "partition k");
-      RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, v, L.vw, st), "partition v");
-      RIB_LAUNCH(launch_partition(g, es, WinLayout::kRows, d_o, L.dow, st), "partition do");
+      RIB_LAUNCH(launch_partition(g, es, q_c, L.qw, st), "partition q");
+      RIB_LAUNCH(launch_partition(g, es, k_c, L.kw, st), "partition k");
+      RIB_LAUNCH(launch_partition(g, es, v, L.vw, st), "partition v");
+      RIB_LAUNCH(launch_partition(g, es, d_o, L.dow, st), "partition do");
       RIB_LAUNCH(launch_pack_pos(g.N, g.n_rows, g.r, rp, es, q_p, es, L.qp, st), "pack q_p");
       RIB_LAUNCH(launch_pack_pos(g.N, g.n_rows, g.r, rp, es, k_p, es, L.kp, st), "pack k_p");
+      t_part.end();
+      TimedGroup t_prep(RIB_KERNEL_BWD_PREP, st);
+      RIB_LAUNCH(launch_bwd_prep(g, es, o, d_o, lse, L.dd, L.lse2, st), "bwd prep");
+      t_prep.end();
     }
-    t_part.end();
-    TimedGroup t_prep(RIB_KERNEL_BWD_PREP, st);
-    RIB_LAUNCH(launch_bwd_prep(g, es, o, d_o, lse, L.dd, L.lse2, bf, st), "bwd prep");
-    t_prep.end();
     BwdArgs a;
     a.g = g;
     a.scale = resolve_scale(scale, shape);

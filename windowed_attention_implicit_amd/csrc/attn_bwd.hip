@@ -497,16 +497,14 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ prep
-// D_i = sum_c dO_ic O_ic and LSE2_i = LSE_i * log2(e) per window row. For the
-// bf16 MFMA kernels they are stored negated (-D, -LSE2: what those kernels add,
-// and the accumulator inputs the dkv kernel takes from LDS as they are); the
-// simple kernels read them unnegated.
+// D_i = sum_c dO_ic O_ic and LSE2_i = LSE_i * log2(e) per window row, for the simple
+// kernels (the bf16 MFMA path takes them negated from its one-pass gather).
 // Up to four lanes share a row, each reading 16-byte chunks (a group of lanes covers
 // 64 contiguous bytes per load), and the partial dot products meet by lane shuffles.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, PixelMap pm, const T* __restrict__ o,
                                                        const T* __restrict__ d_o, const float* __restrict__ lse,
-                                                       float* __restrict__ dd, float* __restrict__ lse2, float sgn) {
+                                                       float* __restrict__ dd, float* __restrict__ lse2) {
   constexpr int kEl = 16 / (int)sizeof(T);     // elements per 16-byte chunk
   constexpr int kCpr = D / kEl;                // chunks per row
   constexpr int kL = kCpr < 4 ? kCpr : 4;      // lanes per row
@@ -520,7 +518,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, PixelMap pm, cons
   if (t >= g.N) {
     if (sub == 0) {
       dd[i] = 0.f;
-      lse2[i] = sgn * INFINITY;   // P = 0 for padded rows
+      lse2[i] = INFINITY;   // P = 0 for padded rows
     }
     return;
   }
@@ -544,8 +542,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(Geom g, PixelMap pm, cons
 #pragma unroll
   for (int m = 1; m < kL; m <<= 1) acc += __shfl_xor(acc, m);
   if (sub == 0) {
-    dd[i] = sgn * acc;
-    lse2[i] = sgn * (lse[ph] * 1.44269504088896340736f);
+    dd[i] = acc;
+    lse2[i] = lse[ph] * 1.44269504088896340736f;
   }
 }
 
@@ -744,16 +742,15 @@ __global__ __launch_bounds__(256) void reduce_pos_grads_kernel(int units, int N,
 }  // namespace
 
 hipError_t launch_bwd_prep(const Geom& g, int esize, const void* o, const void* d_o, const float* lse, float* dd,
-                           float* lse2, bool negate, hipStream_t stream) {
+                           float* lse2, hipStream_t stream) {
   const int64_t total = (int64_t)g.units * g.n_rows;
   if (total == 0) return hipSuccess;
-  const float sgn = negate ? -1.f : 1.f;
   const PixelMap pm = make_pixel_map(g);
   // lanes per row: min(4, 16-byte chunks per row), as in the kernel
   const int lanes = std::min(4, g.d_c * esize / 16);
   const dim3 grid((unsigned)((total * lanes + 255) / 256)), block(256);
 #define RIB_PREP(T, D) \
-  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), grid, block, 0, stream, g, pm, (const T*)o, (const T*)d_o, lse, dd, lse2, sgn)
+  hipLaunchKernelGGL((bwd_prep_kernel<T, D>), grid, block, 0, stream, g, pm, (const T*)o, (const T*)d_o, lse, dd, lse2)
   if (esize == 2) {
     if (g.d_c == 32) RIB_PREP(bf16, 32); else RIB_PREP(bf16, 64);
   } else {

@@ -6,13 +6,11 @@
 
 namespace rib {
 
-// Window-layout codes of the gather/scatter kernels.
-enum class WinLayout {
-  kRows,       // [units][n_rows][d]     token-major rows, rows >= N zero
-  kTransKappa  // [units][d][n_rows]     channel-major; inside every group of 16
-               //                        tokens the positions are permuted by
-               //                        swapping bits 2 and 3 of the token index
-};
+// Windowed layouts of the gathers:
+//   rows   [units][n_rows][d]  token-major, rows >= N zero
+//   kappa  [units][d][n_rows]  channel-major; inside every group of 16 tokens the
+//                              positions are permuted by swapping bits 2 and 3 of
+//                              the token index (bf16 MFMA operands)
 
 hipError_t launch_posgen(int w, const rib_mlp_t& mlp, rib_dtype_t out_dtype, void* q_p, void* k_p,
                          hipStream_t stream);
@@ -26,17 +24,28 @@ hipError_t launch_posgen_bwd(int w, const rib_mlp_t& mlp, const float* dq_p, con
 size_t posgen_bwd_lds_bytes(const rib_mlp_t& mlp);
 size_t posgen_bwd_workspace_bytes(int w, const rib_mlp_t& mlp);
 
-// x [B,H,W,heads,d] -> windowed buffer in `layout` (rows >= N zero-filled).
-hipError_t launch_partition(const Geom& g, int esize, WinLayout layout, const void* x, void* xw,
-                            hipStream_t stream);
-// bf16, d = 32: x -> both the kRows and the kTransKappa buffer in one pass.
+// x [B,H,W,heads,d] -> windowed rows (rows >= N zero-filled).
+hipError_t launch_partition(const Geom& g, int esize, const void* x, void* xw, hipStream_t stream);
 // bf16, d_c = 32: K_c -> rows, V -> kappa, and the per-64-key partial maxima of
 // |[k_c | k_p]|^2 (kp: [N][rp] rows, rp = 0 for none) in one pass.
 hipError_t launch_gather_kv_bound(const Geom& g, int rp, const void* k, const void* v, const void* kp, void* kw,
                                   void* vt, float* kmax2, hipStream_t stream);
-hipError_t launch_partition_rows_kappa(const Geom& g, const void* x, void* xw_rows, void* xw_kappa,
-                                       hipStream_t stream);
-// windowed kRows buffer -> x [B,H,W,heads,d].
+// bf16, d_c = 32 backward preparation in one pass (gather_bwd_kernel): maps
+// [B, H, W, heads, 32] -> rows [units][n_rows][32] and kappa [units][32][n_rows];
+// lse [B, H, W, heads] -> -LSE2, and -D from dO and O, per row [units][n_rows];
+// Q_p, K_p [N][r] -> rows [n_rows][rp] and kappa [rp][n_rows].
+struct BwdGather {
+  PixelMap pm;
+  int N, n_rows, r, rp;
+  const bf16 *q, *k, *v, *d_o, *o;
+  const float* lse;
+  const bf16 *q_p, *k_p;
+  bf16 *qw, *qt, *kw, *kt, *vw, *dow, *dot;
+  float *dd, *lse2;
+  bf16 *qp, *qpt, *kp, *kpt;
+};
+hipError_t launch_gather_bwd(const BwdGather& a, int units, hipStream_t stream);
+// windowed rows -> x [B,H,W,heads,d].
 hipError_t launch_unpartition(const Geom& g, int esize, const void* xw, void* x, hipStream_t stream);
 // Public plain gather / scatter ([units][N][d], no padding).
 hipError_t launch_partition_plain(const Geom& g, int esize, const void* x, void* xw, hipStream_t stream);
@@ -46,10 +55,6 @@ hipError_t launch_unpartition_plain(const Geom& g, int esize, const void* xw, vo
 // precision (rows >= N and columns >= r zero). In and out may differ in type.
 hipError_t launch_pack_pos(int N, int n_rows, int r, int rp, int in_esize, const void* in, int out_esize,
                            void* out, hipStream_t stream);
-// bf16 [N, r] -> the padded [n_rows, rp] rows and their transposed, kappa-permuted copy
-// [rp, n_rows] in one pass.
-hipError_t launch_pack_pos_dual(int N, int n_rows, int r, int rp, const void* in, void* out, void* out_t,
-                                hipStream_t stream);
 
 struct FwdArgs {
   Geom g;
@@ -117,8 +122,8 @@ struct BwdArgs {
   const void* kp;       // [n_rows][rp]
   const void* qpt;      // [rp][n_rows] kappa (bf16 only)
   const void* kpt;      // [rp][n_rows] kappa (bf16 only)
-  const float* lse2;    // [units][n_rows]  log2-domain LSE
-  const float* dd;      // [units][n_rows]  D_i = sum_c dO_ic O_ic
+  const float* lse2;    // [units][n_rows]  log2-domain LSE (negated on the bf16 path)
+  const float* dd;      // [units][n_rows]  D_i = sum_c dO_ic O_ic (negated on the bf16 path)
   // outputs: windowed (simple path) or in the [B, H, W, heads, 32] map (bf16 MFMA path)
   void* dqw;            // [units][n_rows][d_c] (simple path)
   void* dkw;            // [units][n_rows][d_c] (simple path)
@@ -129,10 +134,10 @@ struct BwdArgs {
   float* dqp_part;      // [units][n_rows][rp]
   float* dkp_part;      // [units][n_rows][rp]
 };
-// D and log2-domain LSE in windowed order, from O, dO and LSE in map layout.
-// negate: store -D and -LSE2 (what the bf16 MFMA kernels read); the simple kernels read them as they are
+// D and log2-domain LSE in windowed order, from O, dO and LSE in map layout (the simple
+// kernels; the bf16 path gets -D and -LSE2 from launch_gather_bwd).
 hipError_t launch_bwd_prep(const Geom& g, int esize, const void* o, const void* d_o, const float* lse,
-                           float* dd, float* lse2, bool negate, hipStream_t stream);
+                           float* dd, float* lse2, hipStream_t stream);
 hipError_t launch_attn_bwd_dkv_bf16(const BwdArgs& a, hipStream_t stream);
 hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, hipStream_t stream);
 // One thread per key (dkv) / query (dq) on windowed rows of esize-byte elements, d_c in {32, 64}.

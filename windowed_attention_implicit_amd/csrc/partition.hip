@@ -72,41 +72,6 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(ChunkGeom g, int64_t 
 // Position inside a 16-token group after swapping bits 2 and 3 (an involution).
 __device__ __forceinline__ int kappa16(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
 
-// map -> channel-major kappa layout [units][32][n_rows], bf16, d = 32. One block
-// per (unit, 64-token group): 64 tokens x 64 bytes are staged in LDS, then
-// every thread writes 8 consecutive kappa positions of one channel. With `rows`
-// the same pass also writes the token-major rows layout [units][n_rows][32]
-// (rows >= N zero), so a tensor needed in both layouts is read once.
-__global__ __launch_bounds__(256) void gather_trans_kappa_kernel(PixelMap pm, int N, int n_rows,
-                                                                 const bf16* __restrict__ x, bf16* __restrict__ xt,
-                                                                 bf16* __restrict__ rows) {
-  __shared__ bf16 tile[64][32 + 2];
-  const int groups = n_rows / 64;
-  const int u = blockIdx.x / groups;
-  const int g0 = (blockIdx.x - u * groups) * 64;
-  const int tid = threadIdx.x;
-  {
-    const int tok = tid >> 2, c = tid & 3;
-    const int t = g0 + tok;
-    u32x4 v = u32x4(0u);
-    if (t < N) v = *(const u32x4*)(x + pm.pixel_head(u, t) * 32 + c * 8);
-    if (rows) *(u32x4*)(rows + ((int64_t)u * n_rows + t) * 32 + c * 8) = v;
-    const bf16* pv = (const bf16*)&v;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) tile[tok][c * 8 + j] = pv[j];
-  }
-  __syncthreads();
-  const int d = tid >> 3, pc = tid & 7;
-  bf16 vals[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int p = pc * 8 + j;
-    const int tok = (p & ~15) | kappa16(p & 15);
-    vals[j] = tile[tok][d];
-  }
-  *(u32x4*)(xt + ((int64_t)u * 32 + d) * n_rows + g0 + pc * 8) = *(const u32x4*)vals;
-}
-
 // The bf16 forward's whole preparation in one pass. Block (unit, 64-token group):
 // K_c rows -> the token-major rows layout [units][n_rows][32] (rows >= N zero), V ->
 // the channel-major kappa layout (as gather_trans_kappa_kernel), and the group's
@@ -166,6 +131,83 @@ __global__ __launch_bounds__(256) void gather_kv_bound_kernel(PixelMap pm, int N
   *(u32x4*)(vt + ((int64_t)u * 32 + d) * n_rows + g0 + pc * 8) = *(const u32x4*)vals;
 }
 
+// The bf16 backward's whole preparation in one pass. Block (unit, 64-token group):
+// Q_c, K_c and dO -> the rows layout and the channel-major kappa layout, V -> rows,
+// and per row the negated softmax statistics the MFMA kernels add: -D with
+// D = sum_c dO O, and -LSE2 = -LSE log2(e) (rows >= N: 0 and -inf, so P = 0). D comes
+// from the dO registers the gather already holds. Blocks of unit 0 also pack Q_p and
+// K_p for their 64 tokens (rows zero-padded to rp channels and their kappa transposes).
+__global__ __launch_bounds__(256) void gather_bwd_kernel(BwdGather a) {
+  __shared__ bf16 tile[3][64][32 + 2];
+  const int groups = a.n_rows / 64;
+  const int u = blockIdx.x / groups;
+  const int g0 = (blockIdx.x - u * groups) * 64;
+  const int tid = threadIdx.x;
+  const int N = a.N, n_rows = a.n_rows;
+  {
+    const int tok = tid >> 2, c = tid & 3;
+    const int t = g0 + tok;
+    const int64_t ph = t < N ? a.pm.pixel_head(u, t) : 0;
+    u32x4 x[4] = {u32x4(0u), u32x4(0u), u32x4(0u), u32x4(0u)}, ov = u32x4(0u);   // q, k, do, v; o
+    if (t < N) {
+      const int64_t off = ph * 32 + c * 8;
+      x[0] = *(const u32x4*)(a.q + off);
+      x[1] = *(const u32x4*)(a.k + off);
+      x[2] = *(const u32x4*)(a.d_o + off);
+      x[3] = *(const u32x4*)(a.v + off);
+      ov = *(const u32x4*)(a.o + off);
+    }
+    const int64_t row = ((int64_t)u * n_rows + t) * 32 + c * 8;
+    *(u32x4*)(a.qw + row) = x[0];
+    *(u32x4*)(a.kw + row) = x[1];
+    *(u32x4*)(a.dow + row) = x[2];
+    *(u32x4*)(a.vw + row) = x[3];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+      const bf16* pv = (const bf16*)&x[m];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) tile[m][tok][c * 8 + j] = pv[j];
+    }
+    const bf16x8 de = __builtin_bit_cast(bf16x8, x[2]), oe = __builtin_bit_cast(bf16x8, ov);
+    float dsum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dsum = fmaf((float)de[j], (float)oe[j], dsum);
+    dsum += __shfl_xor(dsum, 1);
+    dsum += __shfl_xor(dsum, 2);
+    if (c == 0) {
+      const int64_t i = (int64_t)u * n_rows + t;
+      a.dd[i] = t < N ? -dsum : 0.f;
+      a.lse2[i] = t < N ? -(a.lse[ph] * 1.44269504088896340736f) : -INFINITY;
+    }
+  }
+  if (u == 0) {   // positional tokens of this group: rows and kappa transposes
+    for (int i = tid; i < 64 * a.rp; i += 256) {
+      const int tl = i / a.rp, j = i - tl * a.rp, t = g0 + tl;
+      const int64_t kpos = (int64_t)j * n_rows + ((t & ~15) | kappa16(t & 15));
+      const bool ok = t < N && j < a.r;
+      const bf16 qv = ok ? a.q_p[(int64_t)t * a.r + j] : (bf16)0.f;
+      const bf16 kv = ok ? a.k_p[(int64_t)t * a.r + j] : (bf16)0.f;
+      a.qp[(int64_t)t * a.rp + j] = qv;
+      a.kp[(int64_t)t * a.rp + j] = kv;
+      a.qpt[kpos] = qv;
+      a.kpt[kpos] = kv;
+    }
+  }
+  __syncthreads();
+  const int d = tid >> 3, pc = tid & 7;
+  bf16* outs[3] = {a.qt, a.kt, a.dot};
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    bf16 vals[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int p = pc * 8 + j;
+      vals[j] = tile[m][(p & ~15) | kappa16(p & 15)][d];
+    }
+    *(u32x4*)(outs[m] + ((int64_t)u * 32 + d) * n_rows + g0 + pc * 8) = *(const u32x4*)vals;
+  }
+}
+
 template <typename InT, typename OutT>
 __global__ void pack_pos_kernel(int N, int n_rows, int r, int rp, const InT* __restrict__ in, OutT* __restrict__ out) {
   int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -173,19 +215,6 @@ __global__ void pack_pos_kernel(int N, int n_rows, int r, int rp, const InT* __r
   int t = i / rp, j = i - t * rp;
   float v = (t < N && j < r) ? (float)in[(int64_t)t * r + j] : 0.f;
   out[i] = (OutT)v;
-}
-
-// [N, r] positional tokens -> the zero-padded [n_rows, rp] rows and their kappa transpose
-// [rp, n_rows] in one pass (bf16): element (t, j) goes to rows[t][j] and to kappa
-// position kappa16(t) of channel j (kappa16 is its own inverse).
-__global__ void pack_pos_dual_kernel(int N, int n_rows, int r, int rp, const bf16* __restrict__ in,
-                                     bf16* __restrict__ out, bf16* __restrict__ outt) {
-  int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= n_rows * rp) return;
-  int t = i / rp, j = i - t * rp;
-  const bf16 v = (t < N && j < r) ? in[(int64_t)t * r + j] : (bf16)0.f;
-  out[i] = v;
-  outt[(int64_t)j * n_rows + ((t & ~15) | kappa16(t & 15))] = v;
 }
 
 ChunkGeom chunk_geom(const Geom& g, int esize, int n_rows) {
@@ -201,20 +230,14 @@ int64_t blocks_for(int64_t n, int threads) { return (n + threads - 1) / threads;
 
 }  // namespace
 
-hipError_t launch_partition(const Geom& g, int esize, WinLayout layout, const void* x, void* xw, hipStream_t stream) {
-  if (layout == WinLayout::kRows) {
-    ChunkGeom c = chunk_geom(g, esize, g.n_rows);
-    int64_t map_chunks = (int64_t)g.B * g.H * g.W * g.heads * c.cpr;
-    int64_t pad_chunks = (int64_t)g.units * (g.n_rows - g.N) * c.cpr;
-    int64_t n = map_chunks + pad_chunks;
-    if (n == 0) return hipSuccess;
-    hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks_for(n, 256)), dim3(256), 0, stream, c, map_chunks,
-                       pad_chunks, (const u32x4*)x, (u32x4*)xw);
-  } else {
-    if (g.units == 0) return hipSuccess;
-    hipLaunchKernelGGL(gather_trans_kappa_kernel, dim3((unsigned)((int64_t)g.units * (g.n_rows / 64))), dim3(256), 0,
-                       stream, make_pixel_map(g), g.N, g.n_rows, (const bf16*)x, (bf16*)xw, (bf16*)nullptr);
-  }
+hipError_t launch_partition(const Geom& g, int esize, const void* x, void* xw, hipStream_t stream) {
+  ChunkGeom c = chunk_geom(g, esize, g.n_rows);
+  int64_t map_chunks = (int64_t)g.B * g.H * g.W * g.heads * c.cpr;
+  int64_t pad_chunks = (int64_t)g.units * (g.n_rows - g.N) * c.cpr;
+  int64_t n = map_chunks + pad_chunks;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3((unsigned)blocks_for(n, 256)), dim3(256), 0, stream, c, map_chunks,
+                     pad_chunks, (const u32x4*)x, (u32x4*)xw);
   return hipGetLastError();
 }
 
@@ -227,11 +250,9 @@ hipError_t launch_gather_kv_bound(const Geom& g, int rp, const void* k, const vo
   return hipGetLastError();
 }
 
-hipError_t launch_partition_rows_kappa(const Geom& g, const void* x, void* xw_rows, void* xw_kappa,
-                                       hipStream_t stream) {
-  if (g.units == 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_trans_kappa_kernel, dim3((unsigned)((int64_t)g.units * (g.n_rows / 64))), dim3(256), 0,
-                     stream, make_pixel_map(g), g.N, g.n_rows, (const bf16*)x, (bf16*)xw_kappa, (bf16*)xw_rows);
+hipError_t launch_gather_bwd(const BwdGather& a, int units, hipStream_t stream) {
+  if (units == 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_bwd_kernel, dim3((unsigned)((int64_t)units * (a.n_rows / 64))), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -274,15 +295,6 @@ hipError_t launch_pack_pos(int N, int n_rows, int r, int rp, int in_esize, const
     hipLaunchKernelGGL((pack_pos_kernel<float, bf16>), grid, block, 0, stream, N, n_rows, r, rp, (const float*)in, (bf16*)out);
   else
     hipLaunchKernelGGL((pack_pos_kernel<bf16, float>), grid, block, 0, stream, N, n_rows, r, rp, (const bf16*)in, (float*)out);
-  return hipGetLastError();
-}
-
-hipError_t launch_pack_pos_dual(int N, int n_rows, int r, int rp, const void* in, void* out, void* out_t,
-                                hipStream_t stream) {
-  const int n = n_rows * rp;
-  if (n == 0) return hipSuccess;
-  hipLaunchKernelGGL(pack_pos_dual_kernel, dim3((n + 255) / 256), dim3(256), 0, stream, N, n_rows, r, rp,
-                     (const bf16*)in, (bf16*)out, (bf16*)out_t);
   return hipGetLastError();
 }
 
