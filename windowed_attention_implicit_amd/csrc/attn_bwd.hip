@@ -359,8 +359,17 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 
   // owned queries: B operands of S^T = K_hat Q_hat^T and dP^T = V dO^T
   const int q0 = qb * kPerBlock + wave * 64;
-  bf16x8 qf[2][C::kSteps], df[2][2];
+  // KP = 1: dP - D comes out of the dP MFMAs: a third K-step pairs channels 0 and 1 of a
+  // constant "ones" V fragment (vone) with -D split into two bf16 parts (dext, hi + lo,
+  // about 16 significant bits) on the dO side, which takes the per-score subtraction off
+  // the vector pipe for one MFMA of the matrix pipe's slack. Padded keys get dP - D = -D,
+  // harmless: their K_hat rows are zero. (KP = 2 has no registers to spare for it and adds
+  // -D on the vector pipe.)
+  constexpr bool kDext = KP == 1;
+  bf16x8 qf[2][C::kSteps], df[2][2], dext[2], vone;
   float nlq[2], ndq[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) vone[j] = (half == 0 && j < 2) ? (bf16)1.0f : (bf16)0.0f;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int q = q0 + nb * 32 + l32;
@@ -373,7 +382,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
       df[nb][s] = ok ? __builtin_bit_cast(bf16x8, *(const u32x4*)(dow + (int64_t)q * 32 + s * 16 + half * 8))
                      : zero_frag();
     nlq[nb] = ok ? a.lse2[ub + q] : -INFINITY;   // stored negated: -LSE2, -D
-    ndq[nb] = ok ? a.dd[ub + q] : 0.f;
+    const float nd = ok ? a.dd[ub + q] : 0.f;
+    ndq[nb] = nd;
+    const bf16 hi = f32_to_bf16(nd);
+    const bf16 lo = f32_to_bf16(nd - (float)hi);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) dext[nb][j] = half == 0 && j == 0 ? hi : (half == 0 && j == 1 ? lo : (bf16)0.0f);
   }
 
   // acc_dqp: as acc_dkp in dkv (16x16 tiles at KP = 1)
@@ -424,12 +438,13 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         // one query per lane: -LSE2 enters as the score MFMA's accumulator input (a lane
-        // constant, 32 registers for both column blocks); -D is added by one vector add (as
-        // an accumulator input it would take 32 registers more than two waves per SIMD allow)
+        // constant, 32 registers for both column blocks), -D through the third dP K-step
         f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[nb][0], cl[nb], 0, 0, 0);
 #pragma unroll
         for (int s = 1; s < C::kSteps; ++s) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[nb][s], sc, 0, 0, 0);
-        f32x16 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], df[nb][0], f32x16(0.f), 0, 0, 0);
+        f32x16 dp = kDext ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(vone, dext[nb], f32x16(0.f), 0, 0, 0)
+                          : f32x16(0.f);
+        dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], df[nb][0], dp, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1], df[nb][1], dp, 0, 0, 0);
         bf16x8 sb[2];
 #pragma unroll
@@ -437,7 +452,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const int v = 8 * s + j;
-            sb[s][j] = f32_to_bf16(__builtin_amdgcn_exp2f(sc[v]) * (dp[v] + ndq[nb]));
+            sb[s][j] = f32_to_bf16(__builtin_amdgcn_exp2f(sc[v]) * (kDext ? dp[v] : dp[v] + ndq[nb]));
           }
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
