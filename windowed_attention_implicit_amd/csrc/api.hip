@@ -632,8 +632,8 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
       // no unit contributes: the positional gradients are an empty sum (zeros)
       Geom g0 = make_geom(*shape);
       const int rp0 = padded_rank(g0.r);
-      hipError_t e = launch_reduce_pos_grads(0, g0.N, g0.n_rows, g0.r, rp0, nullptr, dq_p, (hipStream_t)stream);
-      if (e == hipSuccess) e = launch_reduce_pos_grads(0, g0.N, g0.n_rows, g0.r, rp0, nullptr, dk_p, (hipStream_t)stream);
+      hipError_t e =
+          launch_reduce_pos_grads(0, g0.N, g0.n_rows, g0.r, rp0, nullptr, dq_p, nullptr, dk_p, (hipStream_t)stream);
       if (e != hipSuccess) return hip_fail(e, "zero dq_p / dk_p");
       return ok();
     }
@@ -713,8 +713,8 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
       t_dq.end();
     }
     TimedGroup t_red(RIB_KERNEL_POS_REDUCE, st);
-    RIB_LAUNCH(launch_reduce_pos_grads(g.units, g.N, g.n_rows, g.r, rp, L.dqp_part, dq_p, st), "reduce dq_p");
-    RIB_LAUNCH(launch_reduce_pos_grads(g.units, g.N, g.n_rows, g.r, rp, L.dkp_part, dk_p, st), "reduce dk_p");
+    RIB_LAUNCH(launch_reduce_pos_grads(g.units, g.N, g.n_rows, g.r, rp, L.dqp_part, dq_p, L.dkp_part, dk_p, st),
+               "reduce dq_p, dk_p");
     t_red.end();
     if (!bf) {
       TimedGroup t_unp(RIB_KERNEL_UNPARTITION, st);

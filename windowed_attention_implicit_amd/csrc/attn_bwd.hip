@@ -723,8 +723,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_simple_kernel(BwdArgs a) {
 // out[t][j] = sum over units (in unit order, per slice) of part[u][t][j]; 8 unit
 // slices per column are combined in slice order: a fixed summation order.
 __global__ __launch_bounds__(256) void reduce_pos_grads_kernel(int units, int N, int n_rows, int r, int rp,
-                                                               const float* __restrict__ part, float* __restrict__ out) {
+                                                               const float* __restrict__ part_q,
+                                                               float* __restrict__ out_q,
+                                                               const float* __restrict__ part_k,
+                                                               float* __restrict__ out_k) {
   __shared__ float red[8][32];
+  // blockIdx.y: 0 reduces the dQ_p partials, 1 the dK_p partials
+  const float* part = blockIdx.y ? part_k : part_q;
+  float* out = blockIdx.y ? out_k : out_q;
   const int col = blockIdx.x * 32 + (threadIdx.x & 31);
   const int slice = threadIdx.x >> 5;
   const int ncols = N * rp;
@@ -821,11 +827,11 @@ hipError_t launch_attn_bwd_dq_simple(const BwdArgs& a, int esize, hipStream_t st
 #undef RIB_BWD_SIMPLE_ALL
 #undef RIB_BWD_SIMPLE
 
-hipError_t launch_reduce_pos_grads(int units, int N, int n_rows, int r, int rp, const float* part, float* out,
-                                   hipStream_t stream) {
+hipError_t launch_reduce_pos_grads(int units, int N, int n_rows, int r, int rp, const float* part_q, float* out_q,
+                                   const float* part_k, float* out_k, hipStream_t stream) {
   const int ncols = N * rp;
-  hipLaunchKernelGGL(reduce_pos_grads_kernel, dim3((ncols + 31) / 32), dim3(256), 0, stream, units, N, n_rows, r, rp,
-                     part, out);
+  hipLaunchKernelGGL(reduce_pos_grads_kernel, dim3((ncols + 31) / 32, 2), dim3(256), 0, stream, units, N, n_rows, r,
+                     rp, part_q, out_q, part_k, out_k);
   return hipGetLastError();
 }
 

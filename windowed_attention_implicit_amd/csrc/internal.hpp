@@ -143,8 +143,9 @@ hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, hipStream_t stream);
 // One thread per key (dkv) / query (dq) on windowed rows of esize-byte elements, d_c in {32, 64}.
 hipError_t launch_attn_bwd_dkv_simple(const BwdArgs& a, int esize, hipStream_t stream);
 hipError_t launch_attn_bwd_dq_simple(const BwdArgs& a, int esize, hipStream_t stream);
-// Fixed-order sum over units of [units][n_rows][rp] partials -> [N][r] float32.
-hipError_t launch_reduce_pos_grads(int units, int N, int n_rows, int r, int rp, const float* part, float* out,
-                                   hipStream_t stream);
+// Fixed-order sums over units of the [units][n_rows][rp] dQ_p and dK_p partials -> [N][r]
+// float32 each, in one launch (units = 0: zeros).
+hipError_t launch_reduce_pos_grads(int units, int N, int n_rows, int r, int rp, const float* part_q, float* out_q,
+                                   const float* part_k, float* out_k, hipStream_t stream);
 
 }  // namespace rib
