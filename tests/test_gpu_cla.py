@@ -96,6 +96,7 @@ def _gated_case(wl, dev, units=None, tag=""):
     (1, 24, 24, 3, 32, 12, 16, "bf16"),
     (2, 14, 28, 2, 32, 7, 5, "bf16"),
     (1, 10, 15, 2, 32, 5, 3, "f32"),
+    (1, 16, 16, 2, 64, 8, 16, "bf16"),   # d_c = 64: the one-thread-per-query kernel applies the gate
 ])
 def test_gated_forward_small(shape):
     dev = device()
