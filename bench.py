@@ -239,12 +239,12 @@ def stack_measure(steps: int, warmup: int, dev):
         time_steps(bp.run, steps, 2, reset)
         dkv, _ = kernel_avg_ms(rib, "attn_bwd_dkv")
         dq, _ = kernel_avg_ms(rib, "attn_bwd_dq")
-        prep, _ = kernel_avg_ms(rib, "bwd_prep")
+        gath, _ = kernel_avg_ms(rib, "partition")   # the one-pass backward gather (with -D, -LSE2)
         ff, bf = fwd_flops(wl.units, wl.N, wl.d_c, wl.r), bwd_flops(wl.units, wl.N, wl.d_c, wl.r)
         per.append({"w": wl.w, "fwd_ms": round(t_f, 4), "bwd_ms": round(t_b, 4),
                     "fwd_tflops": round(ff / t_f / 1e9, 1), "bwd_tflops": round(bf / t_b / 1e9, 1),
                     "attn_fwd_kernel_ms": fa and round(fa, 4), "bwd_dkv_kernel_ms": dkv and round(dkv, 4),
-                    "bwd_dq_kernel_ms": dq and round(dq, 4), "bwd_prep_kernel_ms": prep and round(prep, 4),
+                    "bwd_dq_kernel_ms": dq and round(dq, 4), "bwd_gather_kernel_ms": gath and round(gath, 4),
                     "bwd_kernels_tflops": (dkv and dq) and round(bf / (dkv + dq) / 1e9, 1),
                     "posgen_bwd_kernels_ms": pgb and round(pgb, 4)})
     rib.kernel_timing_enable(False)
