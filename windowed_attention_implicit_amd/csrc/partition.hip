@@ -72,6 +72,24 @@ __global__ __launch_bounds__(256) void scatter_rows_kernel(ChunkGeom g, int64_t 
 // Position inside a 16-token group after swapping bits 2 and 3 (an involution).
 __device__ __forceinline__ int kappa16(int p) { return (p & ~12) | ((p & 4) << 1) | ((p & 8) >> 1); }
 
+// Block -> (unit, 64-token group) of the one-pass gathers. One head's 32 bf16 channels are
+// half of a 128-byte line of the map, shared with the next head (the next unit). Workgroups
+// are dealt to the 8 XCDs round-robin, so in the unit-major order those two heads' blocks,
+// `groups` ids apart, share an XCD (and its L2) only when groups is a multiple of 8; for the
+// other window sizes (w = 16: 4 groups) the blocks run group-major, with consecutive logical
+// ids kept on one XCD, so the heads of one token group run side by side on one XCD.
+__device__ __forceinline__ void block_unit_group(int groups, int& u, int& gi) {
+  if (groups % 8 == 0) {
+    u = blockIdx.x / groups;
+    gi = blockIdx.x - u * groups;
+  } else {
+    const int units = gridDim.x / groups;
+    const int logical = xcd_remap(blockIdx.x, gridDim.x);
+    gi = logical / units;
+    u = logical - gi * units;
+  }
+}
+
 // The bf16 forward's whole preparation in one pass. Block (unit, 64-token group):
 // K_c rows -> the token-major rows layout [units][n_rows][32] (rows >= N zero), V ->
 // the channel-major kappa layout (as gather_trans_kappa_kernel), and the group's
@@ -86,8 +104,8 @@ __global__ __launch_bounds__(256) void gather_kv_bound_kernel(PixelMap pm, int N
   __shared__ bf16 tile[64][32 + 2];
   __shared__ float red[4];
   const int groups = n_rows / 64;
-  const int u = blockIdx.x / groups;
-  const int gi = blockIdx.x - u * groups;
+  int u, gi;
+  block_unit_group(groups, u, gi);
   const int g0 = gi * 64;
   const int tid = threadIdx.x;
   {
@@ -119,7 +137,7 @@ __global__ __launch_bounds__(256) void gather_kv_bound_kernel(PixelMap pm, int N
     for (int j = 0; j < 8; ++j) tile[tok][c * 8 + j] = pv[j];
   }
   __syncthreads();
-  if (tid == 0) kmax2[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (tid == 0) kmax2[u * groups + gi] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const int d = tid >> 3, pc = tid & 7;
   bf16 vals[8];
 #pragma unroll
@@ -140,8 +158,9 @@ __global__ __launch_bounds__(256) void gather_kv_bound_kernel(PixelMap pm, int N
 __global__ __launch_bounds__(256) void gather_bwd_kernel(BwdGather a) {
   __shared__ bf16 tile[3][64][32 + 2];
   const int groups = a.n_rows / 64;
-  const int u = blockIdx.x / groups;
-  const int g0 = (blockIdx.x - u * groups) * 64;
+  int u, gi;
+  block_unit_group(groups, u, gi);
+  const int g0 = gi * 64;
   const int tid = threadIdx.x;
   const int N = a.N, n_rows = a.n_rows;
   {
