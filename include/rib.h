@@ -51,7 +51,7 @@ extern "C" {
 typedef enum {
   RIB_OK = 0,
   RIB_ERR_INVALID_ARG = 1, /* bad shape, null or misaligned pointer, bad dtype */
-  RIB_ERR_UNSUPPORTED = 2, /* valid arguments this build does not implement */
+  RIB_ERR_UNSUPPORTED = 2, /* valid arguments the library does not implement */
   RIB_ERR_WORKSPACE = 3,   /* workspace missing or smaller than required */
   RIB_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
 } rib_status_t;
