@@ -140,3 +140,33 @@ def test_bwd_empty_batch_zero_positional_grads():
     torch.cuda.synchronize()
     assert dq.shape == e.shape
     assert not dqp.any() and not dkp.any()
+
+
+def test_bwd_max_window_invariants():
+    """w = 256 (N = 65536 tokens per unit, 2 heads): the oracle's N x N matrices do not fit, so the
+    gradients are held to identities of the method that hold at any size, per unit: every row of
+    dS sums to zero, so sum_j dK_hat_j = 0 (content and positional parts), and every row of P sums
+    to one, so sum_j dV_j = sum_i dO_i."""
+    dev = device()
+    w = 256
+    wl = rib_synth.custom_workload(1, 256, 256, 2, 32, w, 16, "bf16", backward=True, seed=257)
+    x = rib_synth.make_inputs(wl)
+    qpkp = rib_synth.make_positional(w * w, 16, "bf16", seed=5)
+    (dq, dk, dv, dqp, dkp), _, _ = _gpu_fwd_bwd(wl, x, dev, qpkp)
+    for t in (dq, dk, dv, dqp, dkp):
+        assert torch.isfinite(t.float()).all()
+    dk64, dv64 = to_f64(dk), to_f64(dv)
+    do64 = x["d_o"].f64()
+    for h in range(2):
+        sk = dk64[0, :, :, h, :].reshape(w * w, -1).sum(0)
+        mag = np.abs(dk64[0, :, :, h, :]).reshape(w * w, -1).sum(0)
+        print(f"head {h}: |sum dK_c| {np.abs(sk).max():.3e} vs sum |dK_c| {mag.max():.3e}", flush=True)
+        assert (np.abs(sk) <= 2e-3 * mag + 1e-3).all()
+        sv = dv64[0, :, :, h, :].reshape(w * w, -1).sum(0)
+        so = do64[0, :, :, h, :].reshape(w * w, -1).sum(0)
+        print(f"head {h}: max |sum dV - sum dO| {np.abs(sv - so).max():.3e}", flush=True)
+        assert np.allclose(sv, so, rtol=1e-2, atol=0.5)
+    # with one unit per head, dK_p is the sum of both heads' per-unit parts, each summing to zero
+    skp = to_f64(dkp).sum(0)
+    print(f"|sum dK_p| {np.abs(skp).max():.3e} vs sum |dK_p| {np.abs(to_f64(dkp)).sum(0).max():.3e}", flush=True)
+    assert (np.abs(skp) <= 2e-3 * np.abs(to_f64(dkp)).sum(0) + 1e-3).all()
