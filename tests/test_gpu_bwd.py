@@ -165,7 +165,9 @@ def test_bwd_max_window_invariants():
         sv = dv64[0, :, :, h, :].reshape(w * w, -1).sum(0)
         so = do64[0, :, :, h, :].reshape(w * w, -1).sum(0)
         print(f"head {h}: max |sum dV - sum dO| {np.abs(sv - so).max():.3e}", flush=True)
-        assert np.allclose(sv, so, rtol=1e-2, atol=0.5)
+        # both backward kernels form the forward's bf16 scores, so P is normalized by the forward's
+        # LSE up to fp32 and bf16 rounding (observed <= 8e-3 on sums of size ~256)
+        assert np.abs(sv - so).max() <= 0.05
     # with one unit per head, dK_p is the sum of both heads' per-unit parts, each summing to zero
     skp = to_f64(dkp).sum(0)
     print(f"|sum dK_p| {np.abs(skp).max():.3e} vs sum |dK_p| {np.abs(to_f64(dkp)).sum(0).max():.3e}", flush=True)

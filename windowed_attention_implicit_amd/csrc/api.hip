@@ -670,6 +670,7 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
       BwdGather ga;
       ga.pm = make_pixel_map(g);
       ga.N = g.N; ga.n_rows = g.n_rows; ga.r = g.r; ga.rp = rp;
+      ga.c = resolve_scale(scale, shape) * kLog2e;
       ga.q = (const bf16*)q_c; ga.k = (const bf16*)k_c; ga.v = (const bf16*)v;
       ga.d_o = (const bf16*)d_o; ga.o = (const bf16*)o; ga.lse = lse;
       ga.q_p = (const bf16*)q_p; ga.k_p = (const bf16*)k_p;

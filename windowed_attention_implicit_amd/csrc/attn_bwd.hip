@@ -17,8 +17,10 @@
 //  * dq: a workgroup owns 256 queries; it streams 64-key tiles of K_hat, V and
 //    K_hat^T (kappa) and accumulates dQ_hat^T += K_hat^T dS^T with one query
 //    per lane, like the forward.
-//  * The register-resident score operand (K in dkv, Q in dq) is pre-scaled by
-//    scale * log2(e). In dkv (one key per lane, queries along the accumulator
+//  * The Q_c, Q_p rows arrive pre-scaled by c = scale * log2(e) and rounded to
+//    bf16 exactly as the forward rounds them (the one-pass backward gather), so
+//    both kernels form the forward's scores and the score MFMA yields log2-domain
+//    logits directly. In dkv (one key per lane, queries along the accumulator
 //    rows) -LSE2 / -D enter as the accumulator inputs of the score / dP MFMAs,
 //    so P = exp2(acc) and dS = P * acc: per score one exp2, one multiply and
 //    the bf16 packs. In dq (one query per lane) they are lane constants and
@@ -87,14 +89,6 @@ __device__ __forceinline__ bf16x8 lds_frag(const u32x4* p) { return __builtin_bi
 
 __device__ __forceinline__ bf16x8 zero_frag() { return __builtin_bit_cast(bf16x8, u32x4(0u)); }
 
-// bf16(c * f) element-wise: the register-resident score operand is pre-scaled by
-// scale * log2(e) so the score MFMA yields log2-domain logits directly.
-__device__ __forceinline__ bf16x8 scale_frag(bf16x8 f, float c) {
-  bf16x8 r;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) r[j] = f32_to_bf16((float)f[j] * c);
-  return r;
-}
 
 // Loads the lane's 8 channels (16s + 8h ..) of row `row` of a [content 32 | pos rp] token.
 template <int KP>
@@ -176,7 +170,7 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
     const bool ok = key < N;
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s)
-      kf[nb][s] = ok ? scale_frag(token_frag<KP>(kw, kp, key, s, half), a.c) : zero_frag();
+      kf[nb][s] = ok ? token_frag<KP>(kw, kp, key, s, half) : zero_frag();
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       vf[nb][s] = ok ? __builtin_bit_cast(bf16x8, *(const u32x4*)(vw + (int64_t)key * 32 + s * 16 + half * 8))
@@ -376,7 +370,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     const bool ok = q < N;
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s)
-      qf[nb][s] = ok ? scale_frag(token_frag<KP>(qw, qp, q, s, half), a.c) : zero_frag();
+      qf[nb][s] = ok ? token_frag<KP>(qw, qp, q, s, half) : zero_frag();   // rows stored pre-scaled
 #pragma unroll
     for (int s = 0; s < 2; ++s)
       df[nb][s] = ok ? __builtin_bit_cast(bf16x8, *(const u32x4*)(dow + (int64_t)q * 32 + s * 16 + half * 8))

@@ -37,6 +37,7 @@ hipError_t launch_gather_kv_bound(const Geom& g, int rp, const void* k, const vo
 struct BwdGather {
   PixelMap pm;
   int N, n_rows, r, rp;
+  float c;   // scale * log2(e): the Q_c, Q_p rows are stored as bf16(c q)
   const bf16 *q, *k, *v, *d_o, *o;
   const float* lse;
   const bf16 *q_p, *k_p;

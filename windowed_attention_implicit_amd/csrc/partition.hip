@@ -150,7 +150,10 @@ __global__ __launch_bounds__(256) void gather_kv_bound_kernel(PixelMap pm, int N
 }
 
 // The bf16 backward's whole preparation in one pass. Block (unit, 64-token group):
-// Q_c, K_c and dO -> the rows layout and the channel-major kappa layout, V -> rows,
+// Q_c, K_c and dO -> the rows layout and the channel-major kappa layout, V -> rows (the Q_c
+// and Q_p rows, which only enter the score MFMAs, pre-scaled to bf16(c q) with c =
+// scale log2(e) exactly as the forward rounds them, so both backward kernels form the
+// forward's scores; the kappa copies, which enter dK_hat = dS^T Q_hat, stay unscaled),
 // and per row the negated softmax statistics the MFMA kernels add: -D with
 // D = sum_c dO O, and -LSE2 = -LSE log2(e) (rows >= N: 0 and -inf, so P = 0). D comes
 // from the dO registers the gather already holds. Blocks of unit 0 also pack Q_p and
@@ -177,7 +180,14 @@ __global__ __launch_bounds__(256) void gather_bwd_kernel(BwdGather a) {
       ov = *(const u32x4*)(a.o + off);
     }
     const int64_t row = ((int64_t)u * n_rows + t) * 32 + c * 8;
-    *(u32x4*)(a.qw + row) = x[0];
+    {
+      // Q_c rows pre-scaled into the log2 domain, rounded as the forward rounds them
+      const bf16x8 qe = __builtin_bit_cast(bf16x8, x[0]);
+      bf16x8 qs;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qs[j] = f32_to_bf16((float)qe[j] * a.c);
+      *(bf16x8*)(a.qw + row) = qs;
+    }
     *(u32x4*)(a.kw + row) = x[1];
     *(u32x4*)(a.dow + row) = x[2];
     *(u32x4*)(a.vw + row) = x[3];
@@ -206,7 +216,7 @@ __global__ __launch_bounds__(256) void gather_bwd_kernel(BwdGather a) {
       const bool ok = t < N && j < a.r;
       const bf16 qv = ok ? a.q_p[(int64_t)t * a.r + j] : (bf16)0.f;
       const bf16 kv = ok ? a.k_p[(int64_t)t * a.r + j] : (bf16)0.f;
-      a.qp[(int64_t)t * a.rp + j] = qv;
+      a.qp[(int64_t)t * a.rp + j] = f32_to_bf16((float)qv * a.c);   // pre-scaled, as Q_c
       a.kp[(int64_t)t * a.rp + j] = kv;
       a.qpt[kpos] = qv;
       a.kpt[kpos] = kv;
