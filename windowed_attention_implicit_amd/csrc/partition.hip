@@ -92,7 +92,8 @@ __device__ __forceinline__ void block_unit_group(int groups, int& u, int& gi) {
 
 // The bf16 forward's whole preparation in one pass. Block (unit, 64-token group):
 // K_c rows -> the token-major rows layout [units][n_rows][32] (rows >= N zero), V ->
-// the channel-major kappa layout (as gather_trans_kappa_kernel), and the group's
+// the channel-major kappa layout [units][32][n_rows] (64 tokens x 64 bytes staged in LDS,
+// then every thread writes 8 consecutive kappa positions of one channel), and the group's
 // largest |[k_c | k_p]|^2 -> kmax2[unit * groups + group], the per-key-tile partial
 // maxima from which the attention kernel forms its softmax bound (K_p rows have rp
 // channels, rp = 0 for no positional part). The K_c norms come from the registers
