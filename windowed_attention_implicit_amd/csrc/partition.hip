@@ -6,11 +6,15 @@
 // inside a window, heads innermost.
 //
 // A [B, H, W, heads, d] map stores, for every pixel, heads*d contiguous
-// channels; one window row of one head is w runs of d channels. The kernels
-// walk the map in its own memory order (16-byte chunks, fully coalesced on the
-// map side) and scatter / gather whole d-channel runs (64 bytes for bf16,
-// d = 32) on the windowed side. Padded rows (t >= N) of the internal buffers
-// are written as zeros by extra threads of the same launch.
+// channels; one window row of one head is w runs of d channels. The plain
+// gather / scatter kernels walk the map in its own memory order (16-byte
+// chunks, fully coalesced on the map side) and move whole d-channel runs
+// (64 bytes for bf16, d = 32) on the windowed side; padded rows (t >= N) of
+// the internal buffers are written as zeros by extra threads of the same
+// launch. The bf16 attention path instead prepares each direction in one pass
+// per (unit, 64-token group) block: gather_kv_bound_kernel (forward: K_c rows,
+// V kappa, key-norm maxima) and gather_bwd_kernel (backward: Q_c, K_c, dO rows
+// and kappa, V rows, -D and -LSE2, the positional packing).
 #include "internal.hpp"
 
 namespace rib {
