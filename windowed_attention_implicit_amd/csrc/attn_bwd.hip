@@ -23,9 +23,10 @@
 //    logits directly. In dkv (one key per lane, queries along the accumulator
 //    rows) -LSE2 / -D enter as the accumulator inputs of the score / dP MFMAs,
 //    so P = exp2(acc) and dS = P * acc: per score one exp2, one multiply and
-//    the bf16 packs. In dq (one query per lane) they are lane constants and
-//    are added with one vector add each: as accumulator inputs they would need
-//    64 registers the kernel does not have.
+//    the bf16 packs. In dq (one query per lane) -LSE2 is a lane constant held
+//    as the score MFMA's accumulator input, and at r <= 16 -D enters through a
+//    third dP K-step against a constant ones fragment; at r <= 32 there are no
+//    registers for that and -D is added on the vector pipe.
 //  * Both kernels are compiled with the VGPR form of the MFMAs (build flag):
 //    their state exceeds 256 arch VGPRs, and the AGPR form the compiler would
 //    otherwise pick costs a register copy per score.
@@ -198,7 +199,6 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
   TileDma<L.kParts, L.slots()> dma;
   tile_dma_init<LP>(dma, src, wave, lane);
 
-  const float c = a.c;
   const int nqt = (N + kTile - 1) / kTile;
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) tile_dma_issue<LP>(dma, wave, min(i, nqt - 1), sT[i]);
@@ -403,7 +403,6 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   TileDma<L.kParts, L.slots()> dma;
   tile_dma_init<LP>(dma, src, wave, lane);
 
-  const float c = a.c;
   const int nkt = (N + kTile - 1) / kTile;
   tile_dma_issue<LP>(dma, wave, 0, sT[0]);
   tile_dma_issue<LP>(dma, wave, min(1, nkt - 1), sT[1]);
