@@ -458,7 +458,10 @@ def main():
             "attn_fwd": {"ms": round(attn_ms, 5), "TFLOP/s": round(attn_tflops, 1)},
             "unpartition": ({"ms": None, "note": "none: O rows are written in the map layout by the attention "
                                                  "kernel"} if unp_ms is None else
-                            {"ms": round(unp_ms, 5), "GB/s": round(2 * tensor_bytes / unp_ms / 1e6, 1)}),
+                            {"ms": round(unp_ms, 5),
+                             "note": "the split-tail combine: the key-range pieces of each XCD's last partial round "
+                                     "of work items summed into O and LSE (the attention kernel writes the other "
+                                     "rows in the map layout itself)"}),
         },
         "host_ms_per_step": round(wall_ms, 4),
     }

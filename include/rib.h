@@ -115,7 +115,10 @@ rib_status_t rib_window_unpartition(const rib_shape_t* shape, rib_dtype_t dtype,
                                     const void* x_win, void* x, rib_stream_t stream);
 
 /* Bytes of device workspace rib_window_attn_fwd needs for this shape (0 when
- * the shape is invalid). Linear in the feature-map size: no N x N buffer. */
+ * the shape is invalid). Linear in the feature-map size: no N x N buffer. At
+ * w*w >= 2048 tokens the bf16 path also reserves room for the partial results
+ * of its split tail: at most 1024 pieces of 34 KiB (about 34 MiB), and 4 per
+ * eight work items of 256 queries when there are fewer. */
 size_t rib_fwd_workspace_size(const rib_shape_t* shape, rib_dtype_t dtype);
 
 /*
@@ -300,7 +303,8 @@ typedef enum {
   RIB_KERNEL_POSGEN = 0,       /* the posgen kernel */
   RIB_KERNEL_PARTITION = 1,    /* the gathers of one call (map -> window layouts, positional packing) */
   RIB_KERNEL_ATTN_FWD = 2,     /* the forward attention kernel alone */
-  RIB_KERNEL_UNPARTITION = 3,  /* the scatters of one call (window layout -> map) */
+  RIB_KERNEL_UNPARTITION = 3,  /* the scatters of one call (window layout -> map); for the
+                                  bf16 forward, the combine of its split tail */
   RIB_KERNEL_BWD_PREP = 4,     /* D = rowsum(dO * O) and log2-domain LSE */
   RIB_KERNEL_ATTN_BWD_DKV = 5, /* the backward dK / dV kernel alone */
   RIB_KERNEL_ATTN_BWD_DQ = 6,  /* the backward dQ kernel alone */

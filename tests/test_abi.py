@@ -216,11 +216,13 @@ def test_workspace_is_linear_not_quadratic(L):
     """No N x N buffer: the workspace grows with the map, not with the window area squared."""
     def ws(B, H, w, fn=L.rib_fwd_workspace_size):
         return fn(ctypes.byref(rib.Shape(B, H, H, 6, 32, w, 16)), rib.RIB_BF16)
-    for fn in (L.rib_fwd_workspace_size, L.rib_bwd_workspace_size):
+    # the bf16 forward's split-tail pieces (w*w >= 2048): a fixed cap of 1024 pieces of
+    # 256 queries x (32 + 2) floats, independent of the map and the window
+    for fn, split_cap in ((L.rib_fwd_workspace_size, 1024 * 256 * 34 * 4), (L.rib_bwd_workspace_size, 0)):
         small, big = ws(2, 192, 16, fn), ws(2, 192, 96, fn)
         # same map, 36x larger windows: only the per-window-size parts (positional tokens, their
         # transposes and per-unit partials, a few MB at w = 96) differ
-        assert abs(big - small) <= 0.03 * small + (4 << 20)
+        assert abs(big - small) <= 0.03 * small + (4 << 20) + split_cap
         assert ws(4, 192, 96, fn) <= 2 * ws(2, 192, 96, fn) + 4096
         N = 96 * 96
         assert big < 2 * 6 * N * N                          # far below one N x N matrix per unit

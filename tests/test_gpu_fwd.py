@@ -76,6 +76,9 @@ def test_fwd_large_workloads_sampled(name, k):
     (1, 24, 48, 2, 32, 24, 17, "bf16"),
     (1, 40, 40, 1, 32, 40, 32, "bf16"),
     (1, 2, 2, 1, 32, 2, 4, "bf16"),
+    # w*w >= 2048: the last partial round of workgroups is cut into key ranges and combined
+    (1, 50, 100, 2, 32, 50, 8, "bf16"),    # N = 2500: a 4-key last tile, r padded to 16
+    (1, 48, 48, 1, 32, 48, 32, "bf16"),    # N = 2304: whole tiles, two positional K-steps
     (1, 10, 15, 2, 32, 5, 3, "f32"),
     (2, 24, 24, 2, 32, 12, 20, "f32"),
     (1, 32, 32, 1, 32, 32, 8, "f32"),
@@ -184,6 +187,60 @@ def test_fwd_exact_pass_forced():
     x["k_c"] = rib_synth.Tensor("bf16", k.view(x["k_c"].data.dtype))
     o, lse, rqp, rkp = _run(wl, x, dev)
     _compare(wl, x, o, lse, rqp, rkp, tag="exact pass")
+
+
+def _combine_launches(fn):
+    """Runs fn() with the split-tail combine timed; returns how many combines it launched."""
+    rib.kernel_timing_select("unpartition")
+    rib.kernel_timing_read("unpartition")
+    try:
+        fn()
+        return rib.kernel_timing_read("unpartition")[1]
+    finally:
+        rib.kernel_timing_select()
+
+
+def test_fwd_split_tail_mixed_passes():
+    """w = 48 (N = 2304) on a 96 x 96 map, 2 heads: 72 work items, fewer than one round of
+    workgroup slots, so every item is cut into key ranges. Every query is 7.84375 in channel 1
+    and 0 elsewhere (scaled by scale * log2(e) it rounds to bf16 within 3.3e-4, so the large
+    scores below keep their accuracy). Key token 0 of each window carries 52 in channel 0,
+    which no query sees but which lifts the per-query bound |q'| max |k_hat| to ~85 log2 units;
+    key token 2000 carries 20 in channel 1 (score ~33). Ranges without token 2000 (scores
+    below ~8) underflow and take the exact pass with their own running max; the range with it
+    keeps the bound as its shift, so the combine adds pieces with different shifts."""
+    dev = device()
+    wl = rib_synth.custom_workload(1, 96, 96, 2, 32, 48, 16, "bf16", seed=48)
+    x = rib_synth.make_inputs(wl)
+    q = x["q_c"].data.view(np.int16).copy()
+    k = x["k_c"].data.view(np.int16).copy()
+    bf = lambda v: int(rib_synth.bf16_bits(np.array([v], np.float32))[0].view(np.int16))
+    q[...] = bf(0.0)
+    q[..., 1] = bf(7.84375)
+    k[:, ::48, ::48, :, 0] = bf(52.0)                 # token 0 of every 48 x 48 window
+    ty, tx = divmod(2000, 48)
+    k[:, ty::48, tx::48, :, 1] = bf(20.0)             # token 2000
+    x["q_c"] = rib_synth.Tensor("bf16", q.view(x["q_c"].data.dtype))
+    x["k_c"] = rib_synth.Tensor("bf16", k.view(x["k_c"].data.dtype))
+    out = {}
+    n = _combine_launches(lambda: out.update(zip(("o", "lse", "rqp", "rkp"), _run(wl, x, dev))))
+    print(f"split combines launched: {n}", flush=True)
+    assert n == 1
+    _compare(wl, x, out["o"], out["lse"], out["rqp"], out["rkp"], tag="split tail, mixed passes")
+
+
+def test_fwd_split_tail_at_full_size_launches():
+    """The 96 x 96 workload (batch 4, 6 heads: 3456 work items over 512 workgroup slots)
+    combines a split tail; w = 32 (16 key tiles) never splits."""
+    dev = device()
+    for (B, w, expect) in ((4, 96, 1), (2, 32, 0)):
+        wl = rib_synth.custom_workload(B, 192, 192, 6, 32, w, 16, "bf16", seed=w)
+        x = rib_synth.make_inputs(wl)
+        q, k, v = (to_gpu(x[n], dev) for n in ("q_c", "k_c", "v"))
+        qp, kp = (to_gpu(t, dev) for t in rib_synth.make_positional(w * w, 16, "bf16", seed=w))
+        n = _combine_launches(lambda: rib.window_attn_fwd(q, k, v, qp, kp, w))
+        print(f"w = {w}: split combines {n}", flush=True)
+        assert n == expect
 
 
 def test_fwd_max_window_sampled_rows():

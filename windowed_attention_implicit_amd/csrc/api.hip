@@ -97,6 +97,7 @@ struct Carve {
 struct FwdLayout {
   void *qw, *kw, *vw, *ow, *qp, *kp;
   float* kmax2;
+  float* part;   // split-tail pieces of the bf16 kernel (nullptr: none reserved)
   size_t bytes;
 };
 
@@ -121,6 +122,8 @@ FwdLayout fwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
   L.qp = pack ? c.take(pos) : nullptr;
   L.kp = pack ? c.take(pos) : nullptr;
   L.kmax2 = (float*)c.take((size_t)g.units * key_bound_parts(g.N) * sizeof(float));
+  const size_t pieces = rows_qo ? 0 : split_region_pieces(g.units, g.N);
+  L.part = pieces ? (float*)c.take(pieces * kSplitPieceFloats * sizeof(float)) : nullptr;
   L.bytes = c.off;
   return L;
 }
@@ -496,11 +499,19 @@ static rib_status_t attn_fwd_impl(const rib_shape_t* shape, rib_dtype_t dtype, f
     a.kmax2 = L.kmax2;
     a.rp = rp;
     a.gate = gate;
+    a.part = L.part;
+    if (bf && (e = plan_fwd_split(a)) != hipSuccess) return hip_fail(e, "split plan");
     t_part.end();
     TimedGroup t_attn(RIB_KERNEL_ATTN_FWD, st);
     e = bf ? launch_attn_fwd_bf16(a, st) : launch_attn_fwd_simple(a, es, st);
     if (e != hipSuccess) return hip_fail(e, "attention forward");
     t_attn.end();
+    if (bf && a.split_spx) {
+      // the pieces of the split tail: O and LSE of those items
+      TimedGroup t_comb(RIB_KERNEL_UNPARTITION, st);
+      if ((e = launch_fwd_split_combine(a, st)) != hipSuccess) return hip_fail(e, "split combine");
+      t_comb.end();
+    }
     if (!bf) {
       TimedGroup t_unp(RIB_KERNEL_UNPARTITION, st);
       if ((e = launch_unpartition(g, es, L.ow, o, st)) != hipSuccess) return hip_fail(e, "unpartition o");

@@ -39,6 +39,8 @@
 //    fixed per-lane source offsets, so tile staging costs neither VGPRs nor
 //    vector instructions. Workgroups of one unit are kept on one XCD (its L2
 //    holds the unit's K and V).
+#include <algorithm>
+
 #include "internal.hpp"
 
 namespace rib {
@@ -126,7 +128,31 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
   const int N = g.N, n_rows = g.n_rows;
   const int nqb = (N + C::kQPerBlock - 1) / C::kQPerBlock;
   const int total = g.units * nqb;
-  const int logical = xcd_remap(blockIdx.x, total);
+  const int nkt = (N + kKeyTile - 1) / kKeyTile;
+  // Work item and key-tile range. Items are numbered so that consecutive ones share an
+  // XCD (the hardware deals workgroups to the 8 XCDs in turn). With a split tail, the
+  // items of an XCD past its last whole round of slots are cut into split_s key ranges
+  // (pieces), dealt to that XCD after its whole items; trailing padding blocks exit.
+  int logical, t0 = 0, t1 = nkt, piece = -1;
+  if (RPB || a.split_spx == 0) {
+    logical = xcd_remap(blockIdx.x, total);
+  } else {
+    const int xcd = blockIdx.x % 8, i = blockIdx.x / 8;
+    const int q8 = total / 8, rem = total % 8;
+    const int n_x = q8 + (xcd < rem ? 1 : 0);
+    const int base = xcd < rem ? xcd * (q8 + 1) : rem * (q8 + 1) + (xcd - rem) * q8;
+    const int full = n_x / a.split_spx * a.split_spx;
+    if (i < full) {
+      logical = base + i;
+    } else {
+      const int j = i - full, k = j / a.split_s, r = j - k * a.split_s;
+      if (k >= n_x - full) return;   // padding block
+      logical = base + full + k;
+      t0 = r * nkt / a.split_s;
+      t1 = (r + 1) * nkt / a.split_s;
+      piece = (xcd * a.split_tail_max + k) * a.split_s + r;
+    }
+  }
   const int unit = logical / nqb;
   const int qb = logical - unit * nqb;
 
@@ -232,7 +258,6 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
   // chunks [64 i, 64 i + 64) of the buffer and is issued by wave i % 4; the
   // per-lane source offsets are fixed, only the key offset moves per tile.
   // Pad chunks fetch a duplicate of their row's first chunk.
-  const int nkt = (N + kKeyTile - 1) / kKeyTile;
   const __amdgpu_buffer_rsrc_t rs_kc = __builtin_amdgcn_make_buffer_rsrc((void*)kw, 0, n_rows * 64, kRsrcWord3);
   // K_p has N rows (rows past N read zero): either the packed copy or the caller's buffer
   const __amdgpu_buffer_rsrc_t rs_kp = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, N * rp * 2, kRsrcWord3);
@@ -461,12 +486,13 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
       __builtin_amdgcn_sched_barrier(0);
     };
 
-    // prologue: tiles 0 and 1 in LDS, tile 2 on its way, scores of subtile 0,
-    // K fragments of subtile 1. Tiles past the end repeat the last tile (read
-    // only by the unused scores of the subtile after the last).
-    dma_tile(0, 0);
-    dma_tile(min(1, nkt - 1), 1);
-    dma_tile(min(2, nkt - 1), 2);
+    // prologue: tiles t0 and t0 + 1 in LDS, t0 + 2 on its way, scores of the
+    // first subtile, K fragments of the second. Tiles past the range repeat its
+    // last tile (read only by the unused scores of the subtile after the last).
+    // Buffers are numbered from t0.
+    dma_tile(t0, 0);
+    dma_tile(min(t0 + 1, t1 - 1), 1);
+    dma_tile(min(t0 + 2, t1 - 1), 2);
     dma_wait_older();
     __syncthreads();
     f32x16 sc_a[2], sc_b[2];
@@ -488,10 +514,10 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
       gather_bias(0, 1, bh);
       bias_cinit(bh, mneg, 32, cinit);
     }
-    for (int t = 0; t < nkt; ++t) {
-      const int b0 = t % kBufs, b1 = (t + 1) % kBufs;
+    for (int t = t0; t < t1; ++t) {
+      const int b0 = (t - t0) % kBufs, b1 = (t - t0 + 1) % kBufs;
       const int k1 = (t + 1) * kKeyTile;
-      dma_tile(min(t + 3, nkt - 1), (t + 3) % kBufs);
+      dma_tile(min(t + 3, t1 - 1), (t - t0 + 3) % kBufs);
       half_step(sc_a, kf, b1, 0, k1, b0, 0, sc_b);        // softmax (t, 0); scores (t, 1); prefetch (t + 1, 0)
       half_step(sc_b, kf, b1, 1, k1 + 32, b0, 1, sc_a);   // softmax (t, 1); scores (t + 1, 0); prefetch (t + 1, 1)
       dma_wait_older();                          // tile t + 2 landed (this wave's part)
@@ -502,7 +528,7 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
       // query l32 of block nb: row l32 / 16 of lane l32 % 16; kept on half 0
       const float r0 = __shfl(lsum[nb][0], l32 & 15), r1 = __shfl(lsum[nb][1], l32 & 15);
       l_run[nb] = half == 0 ? (l32 < 16 ? r0 : r1) : 0.f;
-      if constexpr (!RPB)
+      if (!RPB && t1 == nkt)
         pad_sub[nb] = (float)(nkt * kKeyTile - N) * (float)f32_to_bf16(__builtin_amdgcn_exp2f(-mref[nb]));
     }
   }
@@ -529,12 +555,12 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
     // drain the fast pass's DMA (tiles past the end) before reusing buffers
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    dma_tile(0, 0);
+    dma_tile(t0, 0);
     __builtin_amdgcn_s_waitcnt(kVmcnt0);
     __syncthreads();
-    for (int t = 0; t < nkt; ++t) {
-      const int buf = t & 1;
-      if (t + 1 < nkt) dma_tile(t + 1, buf ^ 1);
+    for (int t = t0; t < t1; ++t) {
+      const int buf = (t - t0) & 1;
+      if (t + 1 < t1) dma_tile(t + 1, buf ^ 1);
       const bool tail = (t + 1) * kKeyTile > N;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
@@ -587,6 +613,26 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
       __builtin_amdgcn_s_waitcnt(kVmcnt0);
       __syncthreads();
     }
+  }
+
+  // ---- split piece: the unnormalized O, the row sums and the shifts go to the piece's slot
+  // (all 256 queries of the item, padded ones included); the combine kernel adds the pieces
+  if (!RPB && piece >= 0) {
+    float* po = a.part + (int64_t)piece * kSplitPieceFloats;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int ql = wave * kQPerWave + nb * 32 + l32;
+      const float l_tot = l_run[nb] + swap_halves(l_run[nb]);
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        f32x4 o4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = acc[nb][4 * gq + i];
+        *(f32x4*)(po + ql * 32 + 8 * gq + 4 * half) = o4;
+      }
+      if (half == 0) *(float2*)(po + 256 * 32 + 2 * ql) = make_float2(l_tot, m_run[nb]);
+    }
+    return;
   }
 
   // ---- epilogue: normalize, optionally gate (O' = O * G, G in the same map layout), write O
@@ -764,10 +810,209 @@ hipError_t launch_attn_fwd_rpb(const FwdArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+namespace {
+
+// Split-tail combine. Block (split item, 64 queries), thread (query, 8 channels): sums the
+// item's pieces in a fixed order, O = sum_r 2^(m_r - M) O_r / sum_r 2^(m_r - M) l_r with
+// M = max_r m_r (every piece of a fast pass has the same m, the query's bound), and writes
+// O (times the gate, when there is one) to the map and LSE = (M + log2 L) ln 2.
+__global__ __launch_bounds__(256) void fwd_split_combine_kernel(FwdArgs a) {
+  const Geom& g = a.g;
+  const int N = g.N;
+  const int nqb = (N + FwdCfg<1>::kQPerBlock - 1) / FwdCfg<1>::kQPerBlock;
+  const int total = g.units * nqb;
+  const int slot = blockIdx.x / 4, qpart = blockIdx.x % 4;
+  const int xcd = slot / a.split_tail_max, k = slot - xcd * a.split_tail_max;
+  const int q8 = total / 8, rem = total % 8;
+  const int n_x = q8 + (xcd < rem ? 1 : 0);
+  const int base = xcd < rem ? xcd * (q8 + 1) : rem * (q8 + 1) + (xcd - rem) * q8;
+  const int full = n_x / a.split_spx * a.split_spx;
+  if (k >= n_x - full) return;
+  const int item = base + full + k, unit = item / nqb, qb = item - unit * nqb;
+  const int ql = qpart * 64 + (int)threadIdx.x / 4, ch = 8 * ((int)threadIdx.x % 4);
+  const int q = qb * FwdCfg<1>::kQPerBlock + ql;
+  if (q >= N) return;
+  const float* p0 = a.part + (int64_t)slot * a.split_s * kSplitPieceFloats;
+  float M = -INFINITY;
+  for (int r = 0; r < a.split_s; ++r) M = fmaxf(M, p0[r * kSplitPieceFloats + 256 * 32 + 2 * ql + 1]);
+  float L = 0.f, o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  for (int r = 0; r < a.split_s; ++r) {
+    const float* pr = p0 + r * kSplitPieceFloats;
+    const float2 lm = *(const float2*)(pr + 256 * 32 + 2 * ql);
+    const float wgt = exp2f(lm.y - M);
+    L = fmaf(wgt, lm.x, L);
+    const f32x4 a0 = *(const f32x4*)(pr + ql * 32 + ch), a1 = *(const f32x4*)(pr + ql * 32 + ch + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[i] = fmaf(wgt, a0[i], o[i]);
+      o[4 + i] = fmaf(wgt, a1[i], o[4 + i]);
+    }
+  }
+  const float inv = 1.f / L;
+  const PixelMap pm = make_pixel_map(g);
+  const int64_t ph = pm.pixel_head(unit, q);
+  float gv[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) gv[i] = inv;
+  if (a.gate) {
+    const bf16x8 g8 = *(const bf16x8*)((const bf16*)a.gate + ph * 32 + ch);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) gv[i] = inv * (float)g8[i];
+  }
+  bf16x8 ob;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ob[i] = f32_to_bf16(o[i] * gv[i]);
+  *(bf16x8*)((bf16*)a.o_map + ph * 32 + ch) = ob;
+  if (a.lse && ch == 0) a.lse[ph] = (M + log2f(L)) * 0.69314718055994530942f;
+}
+
+// Compute units per XCD and workgroups per CU of the plain bf16 kernel (KP = 1, 2) on the
+// current device; cus = 0 when the compute units do not divide into 8 XCDs.
+struct XcdSlots {
+  int cus = 0, occ = 0;
+};
+XcdSlots split_slots(int kp, hipError_t* err) {
+  static XcdSlots cache[2][64];
+  static bool have[2][64];
+  int dev = 0;
+  if ((*err = hipGetDevice(&dev)) != hipSuccess) return {};
+  if (dev < 0 || dev >= 64) return {};
+  if (!have[kp - 1][dev]) {
+    int cus = 0, occ = 0;
+    if ((*err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return {};
+    *err = kp == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attn_fwd_bf16_kernel<1>, 256, 0)
+                   : hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, attn_fwd_bf16_kernel<2>, 256, 0);
+    if (*err != hipSuccess) return {};
+    cache[kp - 1][dev] = XcdSlots{cus % 8 == 0 ? cus / 8 : 0, occ};
+    have[kp - 1][dev] = true;
+  }
+  return cache[kp - 1][dev];
+}
+
+// Slot model of one XCD's tail, measured on MI355X with this kernel: n pieces of `len` (in
+// units of one whole item's time when `occ` workgroups share a CU) are dealt to the free
+// slots of `cus` CUs, always to the least busy CU first; a CU running fewer than `occ`
+// workgroups gives each of them kAloneSpeedup times the speed. Returns the time until the
+// last piece finishes.
+constexpr double kAloneSpeedup = 1.0 / 0.55;
+double tail_time(int n, double len, int cus, int occ) {
+  constexpr int kMaxSlots = 64 * 4;
+  if (n <= 0) return 0.0;
+  if (cus * occ > kMaxSlots || cus <= 0 || occ <= 0) return 1e30;
+  double rem[kMaxSlots];
+  for (int s = 0; s < cus * occ; ++s) rem[s] = -1.0;
+  auto busy = [&](int c) {
+    int k = 0;
+    for (int j = 0; j < occ; ++j) k += rem[c * occ + j] >= 0.0;
+    return k;
+  };
+  int next = 0;
+  auto deal = [&]() {
+    for (int k = 0; k < occ; ++k)
+      for (int c = 0; c < cus && next < n; ++c) {
+        if (busy(c) != k) continue;
+        for (int j = 0; j < occ; ++j)
+          if (rem[c * occ + j] < 0.0) {
+            rem[c * occ + j] = len;
+            ++next;
+            break;
+          }
+      }
+  };
+  deal();
+  double t = 0.0;
+  for (;;) {
+    double dt = 1e30;
+    for (int c = 0; c < cus; ++c) {
+      const double rate = busy(c) < occ ? kAloneSpeedup : 1.0;
+      for (int j = 0; j < occ; ++j)
+        if (rem[c * occ + j] >= 0.0) dt = std::min(dt, rem[c * occ + j] / rate);
+    }
+    if (dt >= 1e30) return t;
+    t += dt;
+    for (int c = 0; c < cus; ++c) {
+      const double rate = busy(c) < occ ? kAloneSpeedup : 1.0;
+      for (int j = 0; j < occ; ++j) {
+        double& r = rem[c * occ + j];
+        if (r < 0.0) continue;
+        r -= rate * dt;
+        if (r <= 1e-9) r = -1.0;
+      }
+    }
+    deal();
+  }
+}
+
+// Blocks of the split launch: per XCD its whole items plus split_s pieces per tail item,
+// every XCD padded to the largest count (the hardware deals blocks to XCDs in turn).
+int64_t split_blocks(const FwdArgs& a) {
+  const int nqb = (a.g.N + FwdCfg<1>::kQPerBlock - 1) / FwdCfg<1>::kQPerBlock;
+  const int total = a.g.units * nqb, q8 = total / 8, rem = total % 8;
+  int64_t most = 0;
+  for (int x = 0; x < 8; ++x) {
+    const int n_x = q8 + (x < rem ? 1 : 0), full = n_x / a.split_spx * a.split_spx;
+    most = std::max<int64_t>(most, full + (int64_t)(n_x - full) * a.split_s);
+  }
+  return 8 * most;
+}
+
+}  // namespace
+
+size_t split_region_pieces(int units, int N) {
+  const int nkt = (N + kKeyTile - 1) / kKeyTile;
+  if (nkt < kSplitMinTiles) return 0;
+  const int64_t total = (int64_t)units * ((N + FwdCfg<1>::kQPerBlock - 1) / FwdCfg<1>::kQPerBlock);
+  return (size_t)std::min<int64_t>(kMaxSplitPieces, 8 * ((total + 7) / 8) * 4);
+}
+
+hipError_t plan_fwd_split(FwdArgs& a) {
+  a.split_spx = 0;
+  a.split_s = 1;
+  a.split_tail_max = 0;
+  if (!a.part || (a.rp != 16 && a.rp != 32)) return hipSuccess;
+  const size_t region = split_region_pieces(a.g.units, a.g.N);
+  if (region == 0) return hipSuccess;
+  hipError_t e = hipSuccess;
+  const XcdSlots xs = split_slots(a.rp / 16, &e);
+  if (e != hipSuccess) return e;
+  const int spx = xs.cus * xs.occ;
+  if (spx <= 0) return hipSuccess;
+  const int nqb = (a.g.N + FwdCfg<1>::kQPerBlock - 1) / FwdCfg<1>::kQPerBlock;
+  const int total = a.g.units * nqb, q8 = total / 8, rem = total % 8;
+  int tail_max = 0;
+  for (int x = 0; x < 8; ++x) tail_max = std::max(tail_max, (q8 + (x < rem ? 1 : 0)) % spx);
+  if (tail_max == 0) return hipSuccess;
+  // Whole items, halves or quarters, whichever the slot model finishes first: a piece costs
+  // its share of the keys plus 3 % of an item (pipeline fill and drain, prologue), and the
+  // combine 4 % of an item; the split has to win by 1 % of an item.
+  constexpr double kPieceCost = 0.03, kCombineCost = 0.04, kMinGain = 0.01;
+  int S = 1;
+  double best = tail_time(tail_max, 1.0, xs.cus, xs.occ) - kMinGain;
+  for (int s2 : {2, 4}) {
+    if ((size_t)8 * tail_max * s2 > region) continue;
+    const double t = tail_time(tail_max * s2, 1.0 / s2 + kPieceCost, xs.cus, xs.occ) + kCombineCost;
+    if (t < best) best = t, S = s2;
+  }
+  if (S < 2) return hipSuccess;
+  a.split_spx = spx;
+  a.split_s = S;
+  a.split_tail_max = tail_max;
+  return hipSuccess;
+}
+
+hipError_t launch_fwd_split_combine(const FwdArgs& a, hipStream_t stream) {
+  if (a.split_spx == 0) return hipSuccess;
+  hipLaunchKernelGGL(fwd_split_combine_kernel, dim3((unsigned)(8 * a.split_tail_max * 4)), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   const int nqb = (a.g.N + FwdCfg<1>::kQPerBlock - 1) / FwdCfg<1>::kQPerBlock;
-  const int64_t blocks = (int64_t)a.g.units * nqb;
+  int64_t blocks = (int64_t)a.g.units * nqb;
   if (blocks == 0) return hipSuccess;
+  if (a.split_spx) blocks = split_blocks(a);
   if (a.gate) {
     if (a.rp == 16)
       hipLaunchKernelGGL((attn_fwd_bf16_kernel<1, false, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);

@@ -78,7 +78,27 @@ struct FwdArgs {
   int rpb_stride = 0;                   // rpb_table_stride(w)
   // optional CLA gate [B, H, W, heads, d_c] (same dtype as O): O' = O * G in the epilogue
   const void* gate = nullptr;
+  // Split tail (bf16 kernel, not the RPB one): each XCD's items past its last whole round
+  // of workgroup slots are cut into split_s key ranges whose unnormalized partials go to
+  // `part` and are summed by the combine kernel. split_spx = 0: no split.
+  int split_spx = 0;       // workgroup slots per XCD
+  int split_s = 1;         // key ranges per split item (2 or 4)
+  int split_tail_max = 0;  // largest number of split items of one XCD
+  float* part = nullptr;   // [8][split_tail_max][split_s] pieces of kSplitPieceFloats
 };
+// One split piece: the unnormalized O of 256 queries x 32 channels (float32), then per query
+// its row sum and the shift m it is taken against.
+constexpr int kSplitPieceFloats = 256 * 32 + 256 * 2;
+// Workspace reserved for split pieces (shape-only bound, planned within at launch) and the
+// smallest key-tile count (64 keys each) worth splitting.
+constexpr int kMaxSplitPieces = 1024;
+constexpr int kSplitMinTiles = 32;
+size_t split_region_pieces(int units, int N);
+// Sets the split fields of `a` (a.part must name split_region_pieces() pieces, or be null
+// for no split) from the device's workgroup slots; leaves them at "no split" when the
+// launch has no partial last round or the windows are too small.
+hipError_t plan_fwd_split(FwdArgs& a);
+hipError_t launch_fwd_split_combine(const FwdArgs& a, hipStream_t stream);
 // Partial key-norm maxima per unit of the bf16 forward: one per 64 keys.
 int key_bound_parts(int N);
 hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream);
