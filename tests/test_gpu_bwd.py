@@ -55,6 +55,9 @@ def _compare(wl, x, grads, rqp, rkp, units=None, tag="", pos=True):
     (2, 14, 14, 1, 32, 7, 1, "bf16"),
     (1, 24, 48, 2, 32, 24, 17, "bf16"),
     (1, 40, 40, 1, 32, 40, 32, "bf16"),
+    # windows of more than 2048 tokens
+    (1, 50, 100, 2, 32, 50, 8, "bf16"),     # N = 2500: a 4-row last tile, r padded to 16
+    (1, 48, 48, 3, 32, 48, 16, "bf16"),     # N = 2304: whole tiles
     # d_c = 64 (the one-thread-per-key / per-query kernels)
     (1, 10, 15, 2, 64, 5, 3, "bf16"),
     (1, 16, 16, 2, 64, 16, 20, "bf16"),
