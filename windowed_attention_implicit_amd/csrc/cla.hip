@@ -11,8 +11,10 @@
 //    is loaded into registers while the current one is computed (the LDS-only barriers leave
 //    those loads in flight). Each XCD walks its own contiguous band of tiles, so the rows a
 //    tile shares with the tiles above and below it are L2 hits on that XCD.
-//  * Depth-wise 3x3 on the vector unit in fp32: a thread owns two adjacent channels and eight
-//    consecutive pixels, with its 18 taps and 2 biases in registers for the whole launch.
+//  * Depth-wise 3x3 on the vector unit in fp32: a thread owns two adjacent channels and
+//    32 C / (2 threads) consecutive pixels (4 at C = 192); a 3 x 3 window of halo values slides
+//    along them. Taps and biases come from a tap-major LDS table read per tile, which leaves
+//    the registers for two workgroups per CU.
 //  * Point-wise 1x1 on the matrix unit: G^T[out][px] = W_pw[out][:] . D[px][:] as
 //    v_mfma_f32_16x16x32_bf16 over 16 outputs x 2 blocks of 16 pixels per wave (independent
 //    accumulators, so consecutive MFMAs do not wait on each other). Each wave keeps its 16 rows
