@@ -39,6 +39,10 @@
 //    fixed per-lane source offsets, so tile staging costs neither VGPRs nor
 //    vector instructions. Workgroups of one unit are kept on one XCD (its L2
 //    holds the unit's K and V).
+//  * Split tail: the items of an XCD past its last whole round of workgroup
+//    slots may be cut into 2 or 4 key ranges (chosen by a slot model of the
+//    XCD); each piece writes its unnormalized O, row sums and shifts, and
+//    fwd_split_combine_kernel adds them in a fixed order into O and LSE.
 #include <algorithm>
 
 #include "internal.hpp"
