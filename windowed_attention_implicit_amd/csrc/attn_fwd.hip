@@ -44,6 +44,7 @@
 //    XCD); each piece writes its unnormalized O, row sums and shifts, and
 //    fwd_split_combine_kernel adds them in a fixed order into O and LSE.
 #include <algorithm>
+#include <mutex>
 
 #include "internal.hpp"
 
@@ -278,7 +279,8 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
       off = r * 64 + (k < 4 ? k : 0) * 16;
     } else if (i < C::kKcDma + C::kKpDma) {
       const int c2 = c - C::kKpOff;
-      const int r = c2 / C::kKpRow, k = c2 % C::kKpRow;
+      constexpr int kKpRowNz = C::kKpRow ? C::kKpRow : 1;   // no positional part: branch never taken
+      const int r = c2 / kKpRowNz, k = c2 % kKpRowNz;
       off = r * rp * 2 + (k < 2 * KP ? k : 0) * 16;
     } else if (i < C::kKcDma + C::kKpDma + C::kVDma) {
       const int c3 = c - C::kVOff;
@@ -880,9 +882,11 @@ struct XcdSlots {
 XcdSlots split_slots(int kp, hipError_t* err) {
   static XcdSlots cache[2][64];
   static bool have[2][64];
+  static std::mutex mu;   // calls from several host threads fill the cache once
   int dev = 0;
   if ((*err = hipGetDevice(&dev)) != hipSuccess) return {};
   if (dev < 0 || dev >= 64) return {};
+  std::lock_guard<std::mutex> lk(mu);
   if (!have[kp - 1][dev]) {
     int cus = 0, occ = 0;
     if ((*err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return {};
