@@ -56,12 +56,16 @@ def check(name: str, got: np.ndarray, ref: np.ndarray, dtype: str, rel_l2: float
     return err.max(), err.mean(), rl2
 
 
-def sample_units(wl: rib_synth.Workload, k: int, seed: int = 0):
-    """k (batch, window-row, window-col, head) units spread over the map, first and last included."""
+def sample_units(wl: rib_synth.Workload, k: int, seed: int = 0, include=()):
+    """k (batch, window-row, window-col, head) units spread over the map: the first and the last,
+    k - 2 more drawn at random, plus the units whose flat indices are in `include` (heads
+    innermost, the order the library numbers its units)."""
     all_units = [(b, wy, wx, h) for b in range(wl.B) for wy in range(wl.H // wl.w)
                  for wx in range(wl.W // wl.w) for h in range(wl.heads)]
-    if k >= len(all_units):
+    n = len(all_units)
+    if k >= n:
         return all_units
     rng = np.random.default_rng(seed)
-    idx = set([0, len(all_units) - 1]) | set(rng.choice(len(all_units), size=k, replace=False).tolist())
-    return [all_units[i] for i in sorted(idx)][:max(k, 2)]
+    rest = rng.permutation(np.arange(1, n - 1))[:max(k - 2, 0)].tolist()
+    idx = {0, n - 1} | set(rest) | {int(i) for i in include}
+    return [all_units[i] for i in sorted(idx)]

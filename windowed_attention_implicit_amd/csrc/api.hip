@@ -121,7 +121,7 @@ FwdLayout fwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
   const bool pack = rows_qo || g.r != padded_rank(g.r);
   L.qp = pack ? c.take(pos) : nullptr;
   L.kp = pack ? c.take(pos) : nullptr;
-  L.kmax2 = (float*)c.take((size_t)g.units * key_bound_parts(g.N) * sizeof(float));
+  L.kmax2 = (float*)c.take(2 * (size_t)g.units * key_bound_parts(g.N) * sizeof(float));
   const size_t pieces = rows_qo ? 0 : split_region_pieces(g.units, g.N);
   L.part = pieces ? (float*)c.take(pieces * kSplitPieceFloats * sizeof(float)) : nullptr;
   L.bytes = c.off;
@@ -145,7 +145,7 @@ RpbLayout rpb_layout(const Geom& g, void* ws) {
   RpbLayout L;
   L.kw = c.take(t);
   L.vw = c.take(t);
-  L.kmax2 = (float*)c.take((size_t)g.units * key_bound_parts(g.N) * sizeof(float));
+  L.kmax2 = (float*)c.take(2 * (size_t)g.units * key_bound_parts(g.N) * sizeof(float));
   L.tab16 = (_Float16*)c.take((size_t)g.heads * rpb_table_stride(g.w) * 2);
   L.tmax = (float*)c.take((size_t)g.heads * sizeof(float));
   L.kidx = (int*)c.take((size_t)g.n_rows * sizeof(int));

@@ -57,6 +57,13 @@ constexpr int kKeyTile = 64;
 constexpr float kLazyTau = 8.0f;          // log2 units
 constexpr float kUnderflowGuard = 8.673617379884035e-19f;  // 2^-60
 constexpr int kKeyBoundTile = 64;         // keys per partial key-norm maximum (one per gather block)
+// Tiers of the bounded softmax with one positional K-step: when every score bound of a
+// workgroup's rows is at most kNoShiftMax (log2 units) and every |v| of the unit at most
+// kNoShiftVMax, P = exp2(S') needs no shift at all: P lies in [2^-64, 2^64], the row sums
+// and O accumulators stay below 2^14 * 2^64 * 2^40 < 2^128, and the score MFMA takes the
+// constant 0 as its accumulator input. Otherwise scores are shifted by the bound.
+constexpr float kNoShiftMax = 64.0f;
+constexpr float kNoShiftVMax = 1099511627776.0f;   // 2^40
 
 // s_waitcnt immediates (gfx9 encoding) waiting on the vector-memory counter
 // only: vmcnt in bits 3:0, expcnt (7) and lgkmcnt (15) left at their maxima.
@@ -75,6 +82,15 @@ __device__ __forceinline__ float swap_halves(float x) { return __shfl_xor(x, 32)
 // depend on; the waves write no LDS themselves. The memory clobber keeps the
 // compiler from moving LDS reads or DMA issue across it.
 __device__ __forceinline__ void barrier_dma() { asm volatile("s_barrier" ::: "memory"); }
+
+// Keeps x in VGPRs at this point of the instruction stream. Between two pins the compiler
+// cannot move the instruction that consumes or produces x: the fast pass uses pairs of pins
+// to fix the issue order of every MFMA, exp and pack (a wave issues in order, so the
+// order decides how well its matrix and vector work overlap). Emits no instruction.
+template <typename T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
 
 // KP: positional 16-channel steps, 1 (r <= 16) or 2 (r <= 32); 0 with RPB:
 // the relative-position-bias comparison variant (content-only scores plus a
@@ -118,8 +134,7 @@ struct BoolTag {
   static constexpr bool value = V;
 };
 
-// GATE: O' = O * G with G read in the map layout (its loads are issued before the key loop,
-// so their latency hides behind it)
+// GATE: O' = O * G with G read in the map layout by the output stage
 template <int KP, bool RPB = false, bool GATE = false>
 __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   typedef FwdCfg<KP, RPB> C;
@@ -182,10 +197,16 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
 
   // ---- per-unit key-norm bound: max over the partial maxima of the unit
   const int nkparts = (N + kKeyBoundTile - 1) / kKeyBoundTile;
-  float km = 0.f;
-  for (int i = lane; i < nkparts; i += 64) km = fmaxf(km, a.kmax2[(int64_t)unit * nkparts + i]);
+  float km = 0.f, vm = 0.f;
+  for (int i = lane; i < nkparts; i += 64) {
+    km = fmaxf(km, a.kmax2[(int64_t)unit * nkparts + i]);
+    vm = fmaxf(vm, a.kmax2[((int64_t)g.units + unit) * nkparts + i]);
+  }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) km = fmaxf(km, __shfl_xor(km, o));
+  for (int o = 32; o > 0; o >>= 1) {
+    km = fmaxf(km, __shfl_xor(km, o));
+    vm = fmaxf(vm, __shfl_xor(vm, o));
+  }
   const float kmax = sqrtf(km);
 
   // ---- RPB: the head's table, prepared in fp16 log2 units (entries padded to
@@ -230,17 +251,6 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
     }
     sq += swap_halves(sq);
     mref[nb] = sqrtf(sq) * kmax + bmax;
-  }
-  uint2 gpre[2][4];
-  if constexpr (GATE) {
-    const bf16* gmap = (const bf16*)a.gate;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int q = q0 + nb * 32 + l32;
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq)
-        gpre[nb][gq] = q < N ? *(const uint2*)(gmap + map_row(q) + 8 * gq + 4 * half) : make_uint2(0u, 0u);
-    }
   }
   // RPB: the bias of query q and key k is table[(w-1)(2w-1) + (w-1) + QI(q) - QI(k)] with
   // QI(t) = (t / w)(2w-1) + t % w. Per column block the lane keeps the LDS byte address of
@@ -388,7 +398,153 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
   // With RPB the accumulator init carries each score's bias too (rebuilt per
   // subtile) and padded keys start at -inf, so their P is zero.
   float pad_sub[2] = {0.f, 0.f};
-  {
+  if constexpr (KP == 1 && !RPB) {
+    // ===== fast pass, one positional K-step. Per 32-key subtile h (a half step) a wave
+    // forms 16 P words (2 exp2 + 1 pack each, 32 scores) and issues 14 MFMAs: the six score
+    // MFMAs (three K-steps x two 32-query column blocks), four PV MFMAs and four row-sum
+    // MFMAs. They are issued in a fixed order of 16 slots, one word and at most one MFMA per
+    // slot, so that the wave's in-order issue alternates matrix and vector work:
+    //   slot  1- 3: S(s, nb 1) of subtile h        words (0,0,*)   [block (nb, s)]
+    //   slot  4: R(1,1) of h-1    5: R(0,0)    6: P(0,0)    7: P(1,1) of h-1   words (0,1,*)
+    //   slot  9, 11, 13: S(s, nb 0) of subtile h+1   10: R(1,0)   12: P(1,0)   words (1,0,*)
+    //   slot 14: R(0,1)   15: P(0,1)                                           words (1,1,*)
+    // The score registers roll: nb 0 scores of h+1 overwrite those of h once their 8 words
+    // are formed (slot 9), nb 1 scores are formed at the start of their own half step. The
+    // last block's R and P wait for the next half step. K fragments of h+1 are read after
+    // slot 3, V^T fragment 1 of h after slot 7 and fragment 0 of h+1 after slot 15.
+    const bool shift = __syncthreads_or(!(fmaxf(mref[0], mref[1]) <= kNoShiftMax) || !(vm <= kNoShiftVMax));
+    auto fast_pass = [&](auto tier) {
+      constexpr bool SH = decltype(tier)::value;
+      const float msub[2] = {SH ? mref[0] : 0.f, SH ? mref[1] : 0.f};
+      f32x16 sc[2];
+      bf16x8 kf[C::kSteps], vf[2];
+      u32x4 wd[2][2];
+      f32x4 lsum[2];
+      bf16x8 rsel;   // row-sum selector (see below)
+      {
+        const bf16 one = (lane & 15) == ((lane >> 4) & 1) ? (bf16)1.0f : (bf16)0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) rsel[j] = one;
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        acc[nb] = f32x16(0.f);
+        lsum[nb] = f32x4(0.f);
+        wd[1][nb] = u32x4(0u);
+        m_run[nb] = msub[nb];
+      }
+      vf[1] = __builtin_bit_cast(bf16x8, u32x4(0u));
+      // Row sums on the matrix pipe: v_mfma_f32_16x16x32_bf16 with a 0/1 selector as A. Read
+      // as that MFMA's B operand, lane l of a P block holds query l % 16 + 16 * ((l / 16) % 2);
+      // the selector puts lane groups 0 and 2 into row 0 and groups 1 and 3 into row 1, so rows
+      // 0 and 1 of the 16x16 accumulator (lanes 0-15, elements 0 and 1) collect the sums of the
+      // block's queries 0-15 and 16-31 over the exact bf16 P values the PV MFMA consumes.
+      auto word_exp = [&](int nb, int s, int w, float& p0, float& p1) {
+        float x0 = sc[nb][8 * s + 2 * w], x1 = sc[nb][8 * s + 2 * w + 1];
+        if constexpr (SH) {
+          x0 -= msub[nb];
+          x1 -= msub[nb];
+        }
+        pin(x0);
+        pin(x1);
+        p0 = __builtin_amdgcn_exp2f(x0);
+        p1 = __builtin_amdgcn_exp2f(x1);
+        pin(p0);
+        pin(p1);
+      };
+      auto word_pack = [&](int nb, int s, int w, float p0, float p1) {
+        bf16x2 pr;
+        pr[0] = f32_to_bf16(p0);
+        pr[1] = f32_to_bf16(p1);
+        unsigned u = __builtin_bit_cast(unsigned, pr);
+        pin(u);
+        wd[nb][s][w] = u;
+      };
+      auto S = [&](int s, int nb) {
+        pin(kf[s]);
+        sc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[s], qf[nb][s], s == 0 ? f32x16(0.f) : sc[nb], 0, 0, 0);
+        pin(sc[nb]);
+      };
+      auto R = [&](int s, int nb) {
+        pin(lsum[nb]);
+        lsum[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(rsel, __builtin_bit_cast(bf16x8, wd[nb][s]), lsum[nb],
+                                                           0, 0, 0);
+        pin(lsum[nb]);
+      };
+      auto P = [&](int s, int nb) {
+        pin(acc[nb]);
+        acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[s], __builtin_bit_cast(bf16x8, wd[nb][s]), acc[nb], 0,
+                                                          0, 0);
+        pin(acc[nb]);
+      };
+      // one slot: the word's two exp2, then the MFMA (if any), then the pack (the MFMA also
+      // separates the second exp2 from the pack that reads it)
+      auto slot = [&](int nb, int s, int w, auto mfma) {
+        float p0, p1;
+        word_exp(nb, s, w, p0, p1);
+        mfma();
+        word_pack(nb, s, w, p0, p1);
+      };
+      auto none = [] {};
+      // half step h: (cbuf, csub) holds subtile h, (nbuf, nsub) subtile h + 1
+      auto hstep = [&](int cbuf, int csub, int nbuf, int nsub) {
+        slot(0, 0, 0, [&] { S(0, 1); });
+        slot(0, 0, 1, [&] { S(1, 1); });
+        slot(0, 0, 2, [&] { S(2, 1); });
+        load_kf(nbuf, nsub, kf);
+        slot(0, 0, 3, [&] { R(1, 1); });
+        slot(0, 1, 0, [&] { R(0, 0); });
+        slot(0, 1, 1, [&] { P(0, 0); });
+        slot(0, 1, 2, [&] { P(1, 1); });
+        vf[1] = vfrag(cbuf, csub, 1);
+        slot(0, 1, 3, none);
+        slot(1, 0, 0, [&] { S(0, 0); });
+        slot(1, 0, 1, [&] { R(1, 0); });
+        slot(1, 0, 2, [&] { S(1, 0); });
+        slot(1, 0, 3, [&] { P(1, 0); });
+        slot(1, 1, 0, [&] { S(2, 0); });
+        slot(1, 1, 1, [&] { R(0, 1); });
+        slot(1, 1, 2, [&] { P(0, 1); });
+        vf[0] = vfrag(nbuf, nsub, 0);
+        slot(1, 1, 3, none);
+      };
+
+      // prologue: tiles t0 and t0 + 1 in LDS, t0 + 2 on its way; nb 0 scores of the first
+      // subtile. Tiles past the range repeat its last tile (read only by the unused scores
+      // of the subtile after the last). Buffers are numbered from t0. The deferred block of
+      // the (nonexistent) previous subtile is zero.
+      dma_tile(t0, 0);
+      dma_tile(min(t0 + 1, t1 - 1), 1);
+      dma_tile(min(t0 + 2, t1 - 1), 2);
+      dma_wait_older();
+      __syncthreads();
+      load_kf(0, 0, kf);
+#pragma unroll
+      for (int s2 = 0; s2 < C::kSteps; ++s2) S(s2, 0);
+      vf[0] = vfrag(0, 0, 0);
+      for (int t = t0; t < t1; ++t) {
+        const int b0 = (t - t0) % kBufs, b1 = (t - t0 + 1) % kBufs;
+        dma_tile(min(t + 3, t1 - 1), (t - t0 + 3) % kBufs);
+        hstep(b0, 0, b0, 1);
+        hstep(b0, 1, b1, 0);
+        dma_wait_older();   // tile t + 2 landed (this wave's part)
+        barrier_dma();
+      }
+      R(1, 1);
+      P(1, 1);
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        // query l32 of block nb: row l32 / 16 of lane l32 % 16; kept on half 0
+        const float r0 = __shfl(lsum[nb][0], l32 & 15), r1 = __shfl(lsum[nb][1], l32 & 15);
+        l_run[nb] = half == 0 ? (l32 < 16 ? r0 : r1) : 0.f;
+        // keys past N have zero K rows: their P is exp2(0 - shift), rounded as the MFMA saw it
+        if (t1 == nkt)
+          pad_sub[nb] = (float)(nkt * kKeyTile - N) * (SH ? (float)f32_to_bf16(__builtin_amdgcn_exp2f(-mref[nb])) : 1.f);
+      }
+    };
+    if (shift) fast_pass(BoolTag<true>());
+    else fast_pass(BoolTag<false>());
+  } else {
     f32x16 cinit[2];
     const float mneg[2] = {-mref[0], -mref[1]};
     _Float16 bh[2][16];
@@ -657,7 +813,7 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
         float gv[4] = {inv, inv, inv, inv};
         if constexpr (GATE) {
           bf16 g4[4];
-          *(uint2*)g4 = gpre[nb][gq];
+          *(uint2*)g4 = *(const uint2*)((const bf16*)a.gate + at);
 #pragma unroll
           for (int i = 0; i < 4; ++i) gv[i] = inv * (float)g4[i];
         }
@@ -901,10 +1057,17 @@ XcdSlots split_slots(int kp, hipError_t* err) {
 
 // Slot model of one XCD's tail, measured on MI355X with this kernel: n pieces of `len` (in
 // units of one whole item's time when `occ` workgroups share a CU) are dealt to the free
-// slots of `cus` CUs, always to the least busy CU first; a CU running fewer than `occ`
-// workgroups gives each of them kAloneSpeedup times the speed. Returns the time until the
-// last piece finishes.
-constexpr double kAloneSpeedup = 1.0 / 0.55;
+// slots of `cus` CUs, always to the least busy CU first; a workgroup on a CU that runs k
+// workgroups runs at slot_rate(occ, k) times the speed of one of a full CU. Returns the
+// time until the last piece finishes.
+double slot_rate(int occ, int k) {
+  // measured: one positional K-step, 3 workgroups per CU (w = 64 items alone on their
+  // CUs, two per CU and four full rounds: 0.065, 0.103 and 0.127 ms per item round);
+  // two workgroups per CU (the r = 32 instance): alone 1.82x
+  if (occ == 3) return k == 1 ? 1.94 : (k == 2 ? 1.23 : 1.0);
+  if (occ == 2) return k == 1 ? 1.82 : 1.0;
+  return 1.0;
+}
 double tail_time(int n, double len, int cus, int occ) {
   constexpr int kMaxSlots = 64 * 4;
   if (n <= 0) return 0.0;
@@ -934,14 +1097,14 @@ double tail_time(int n, double len, int cus, int occ) {
   for (;;) {
     double dt = 1e30;
     for (int c = 0; c < cus; ++c) {
-      const double rate = busy(c) < occ ? kAloneSpeedup : 1.0;
+      const double rate = slot_rate(occ, busy(c));
       for (int j = 0; j < occ; ++j)
         if (rem[c * occ + j] >= 0.0) dt = std::min(dt, rem[c * occ + j] / rate);
     }
     if (dt >= 1e30) return t;
     t += dt;
     for (int c = 0; c < cus; ++c) {
-      const double rate = busy(c) < occ ? kAloneSpeedup : 1.0;
+      const double rate = slot_rate(occ, busy(c));
       for (int j = 0; j < occ; ++j) {
         double& r = rem[c * occ + j];
         if (r < 0.0) continue;

@@ -27,7 +27,8 @@ size_t posgen_bwd_workspace_bytes(int w, const rib_mlp_t& mlp);
 // x [B,H,W,heads,d] -> windowed rows (rows >= N zero-filled).
 hipError_t launch_partition(const Geom& g, int esize, const void* x, void* xw, hipStream_t stream);
 // bf16, d_c = 32: K_c -> rows, V -> kappa, and the per-64-key partial maxima of
-// |[k_c | k_p]|^2 (kp: [N][rp] rows, rp = 0 for none) in one pass.
+// |[k_c | k_p]|^2 (kp: [N][rp] rows, rp = 0 for none) and of |v| in one pass; kmax2 holds
+// 2 * units * key_bound_parts(N) floats (the |k_hat|^2 maxima, then the |v| maxima).
 hipError_t launch_gather_kv_bound(const Geom& g, int rp, const void* k, const void* v, const void* kp, void* kw,
                                   void* vt, float* kmax2, hipStream_t stream);
 // bf16, d_c = 32 backward preparation in one pass (gather_bwd_kernel): maps
@@ -69,7 +70,7 @@ struct FwdArgs {
   void* ow;             // [units][n_rows][d_c] (simple path)
   void* o_map;          // bf16 path: O in the [B, H, W, heads, 32] map
   float* lse;           // [B,H,W,heads] or nullptr
-  float* kmax2;         // [units][key_bound_parts(N)] partial maxima of |[k_c | k_p]|^2 (bf16 path)
+  float* kmax2;         // [2][units][key_bound_parts(N)] partial maxima of |[k_c | k_p]|^2, then of |v| (bf16 path)
   int rp;               // padded rank, 16 or 32 (0: the RPB comparison kernel)
   // RPB comparison kernel only (from launch_rpb_prep)
   const _Float16* rpb_tab16 = nullptr;  // [heads][rpb_stride] table * log2(e), fp16, zero-padded

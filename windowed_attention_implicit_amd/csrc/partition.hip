@@ -98,16 +98,17 @@ __device__ __forceinline__ void block_unit_group(int groups, int& u, int& gi) {
 // K_c rows -> the token-major rows layout [units][n_rows][32] (rows >= N zero), V ->
 // the channel-major kappa layout [units][32][n_rows] (64 tokens x 64 bytes staged in LDS,
 // then every thread writes 8 consecutive kappa positions of one channel), and the group's
-// largest |[k_c | k_p]|^2 -> kmax2[unit * groups + group], the per-key-tile partial
-// maxima from which the attention kernel forms its softmax bound (K_p rows have rp
-// channels, rp = 0 for no positional part). The K_c norms come from the registers
-// that carry the rows, so K_c is read once.
+// largest |[k_c | k_p]|^2 -> kmax2[unit * groups + group] and the group's largest |v| ->
+// kmax2[units * groups + unit * groups + group]: the per-key-tile partial maxima from which
+// the attention kernel forms its softmax bound and picks its exponent tier (K_p rows have
+// rp channels, rp = 0 for no positional part). The norms come from the registers that
+// carry the rows, so K_c and V are read once.
 __global__ __launch_bounds__(256) void gather_kv_bound_kernel(PixelMap pm, int N, int n_rows, int rp,
                                                               const bf16* __restrict__ k, const bf16* __restrict__ v,
                                                               const bf16* __restrict__ kp, bf16* __restrict__ kw,
                                                               bf16* __restrict__ vt, float* __restrict__ kmax2) {
   __shared__ bf16 tile[64][32 + 2];
-  __shared__ float red[4];
+  __shared__ float red[4], vred[4];
   const int groups = n_rows / 64;
   int u, gi;
   block_unit_group(groups, u, gi);
@@ -136,13 +137,24 @@ __global__ __launch_bounds__(256) void gather_kv_bound_kernel(PixelMap pm, int N
     ss += __shfl_xor(ss, 2);   // the token's |k_hat|^2 in its 4 lanes
 #pragma unroll
     for (int o = 4; o < 64; o <<= 1) ss = fmaxf(ss, __shfl_xor(ss, o));
-    if ((tid & 63) == 0) red[tid >> 6] = ss;
     const bf16* pv = (const bf16*)&vv;
+    float va = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) va = fmaxf(va, fabsf((float)pv[j]));
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) va = fmaxf(va, __shfl_xor(va, o));
+    if ((tid & 63) == 0) {
+      red[tid >> 6] = ss;
+      vred[tid >> 6] = va;
+    }
 #pragma unroll
     for (int j = 0; j < 8; ++j) tile[tok][c * 8 + j] = pv[j];
   }
   __syncthreads();
-  if (tid == 0) kmax2[u * groups + gi] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  if (tid == 0) {
+    kmax2[u * groups + gi] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    kmax2[(int64_t)gridDim.x + u * groups + gi] = fmaxf(fmaxf(vred[0], vred[1]), fmaxf(vred[2], vred[3]));
+  }
   const int d = tid >> 3, pc = tid & 7;
   bf16 vals[8];
 #pragma unroll
