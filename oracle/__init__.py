@@ -18,8 +18,6 @@ from .rib import (  # noqa: F401
     posgen,
     window_partition,
     window_unpartition,
-    unit_index,
-    unit_slices,
     concat_scores,
     attention_window_fwd,
     attention_window_bwd,

@@ -63,7 +63,7 @@ import numpy as np
 
 __all__ = [
     "window_coords", "fourier_features", "gelu", "mlp_param_count", "posgen",
-    "window_partition", "window_unpartition", "unit_index", "unit_slices",
+    "window_partition", "window_unpartition",
     "concat_scores", "attention_window_fwd", "attention_window_bwd",
     "rib_window_attn_fwd", "rib_window_attn_bwd", "default_scale",
     "gelu_grad", "posgen_bwd",
@@ -205,16 +205,6 @@ def posgen_bwd(w: int, n_freq: int, w1, b1, w2, b2, rank: int, dq_p, dk_p):
 def _check_divisible(H: int, W: int, w: int):
     if H % w or W % w:
         raise ValueError("H and W must be multiples of the window size")
-
-
-def unit_index(b: int, wy: int, wx: int, head: int, H: int, W: int, w: int, heads: int) -> int:
-    """Index of the (batch, window, head) unit: windows row-major per image, heads innermost."""
-    return ((b * (H // w) + wy) * (W // w) + wx) * heads + head
-
-
-def unit_slices(b: int, wy: int, wx: int, w: int):
-    """Index expressions selecting one window of a [B, H, W, ...] tensor."""
-    return (b, slice(wy * w, (wy + 1) * w), slice(wx * w, (wx + 1) * w))
 
 
 def window_partition(x: np.ndarray, w: int) -> np.ndarray:

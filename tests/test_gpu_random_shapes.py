@@ -2,11 +2,13 @@
 d_c 32 or 64, bf16 or float32, 1-2 images, 1-7 heads, positional tokens from posgen or random)
 against the float64 oracle, at the method's tolerance on every output.
 
-The library's own relative-L2 bar is applied to O and the content gradients only: the positional
-gradients can vanish exactly. At w = 2 the coordinates are +-1, every sin(2^k pi x) feature is 0
-and every cos feature is the same for all tokens, so all tokens share one positional token and
-dQ_p = scale K_p sum_j dS_ij = 0; the GPU then returns bf16 rounding noise (absolute error ~1e-4),
-whose relative size means nothing.
+The library's own relative-L2 bar is applied to every output except the positional gradients of
+windows of w <= 5, which can vanish or nearly vanish. At w = 2 the coordinates are +-1, every
+sin(2^k pi x) feature is 0 and every cos feature is the same for all tokens, so all tokens share one
+positional token and dQ_p = scale K_p sum_j dS_ij = 0; at w = 3 every sin feature is still 0, and
+at w <= 5 the few distinct coordinates leave K_p nearly constant over the window, so
+sum_j dS_ij K_p[j] nearly cancels (sum_j dS_ij = 0). The GPU then returns bf16 rounding noise
+(absolute error ~1e-4), whose relative size means nothing; the method's absolute bar still holds.
 """
 
 import numpy as np
@@ -69,4 +71,4 @@ def test_random_shape_fwd_bwd(case):
     assert lerr <= (1e-5 if dt == "f32" else 2e-2), f"LSE max-abs {lerr:.3e}"
     ref = oracle.rib_window_attn_bwd(x["q_c"].f64(), x["k_c"].f64(), x["v"].f64(), rqp, rkp, x["d_o"].f64(), w)
     for n, g, rr in zip(["dQ_c", "dK_c", "dV", "dQ_p", "dK_p"], grads, ref):
-        check(n, to_f64(g), rr, dt, rel_l2=None if n in ("dQ_p", "dK_p") else 1e-2)
+        check(n, to_f64(g), rr, dt, rel_l2=None if (n in ("dQ_p", "dK_p") and w <= 5) else 1e-2)

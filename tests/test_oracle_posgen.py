@@ -196,7 +196,26 @@ def test_bias_identical_for_every_window():
             np.testing.assert_allclose(2 * (xs - xs[0]) / (w - 1) - 1, c_ref, atol=1e-15)
 
 
-def test_param_count_independent_of_window():
-    counts = {w: oracle.mlp_param_count(16, 64, 16) for w in (16, 32, 64, 96)}
-    assert len(set(counts.values())) == 1
-    assert counts[96] == 64 * 64 + 64 + 32 * 64 + 32
+def test_param_count_is_what_posgen_uses_at_every_window():
+    """[EN §2.A "Advantages"]: the bias parameters do not grow with the window. Every entry of
+    W1, b1, W2, b2 is perturbed in turn and counted when it moves posgen's output; the count is
+    the same at every window size and equals mlp_param_count (a dropped bias, an unused feature
+    column or a rank mix-up would change it). w >= 4 keeps every sin feature nonzero (at w = 2
+    and 3 every coordinate is a multiple of pi/2 ... pi, where sin(2^k pi x) vanishes)."""
+    F, hid, r = 3, 5, 2
+    rng = np.random.default_rng(31)
+    params = {"w1": rng.normal(0, 0.5, (hid, 4 * F)), "b1": rng.normal(0, 0.5, hid),
+              "w2": rng.normal(0, 0.5, (2 * r, hid)), "b2": rng.normal(0, 0.5, 2 * r)}
+    counts = {}
+    for w in (4, 7, 16):
+        base = np.concatenate(oracle.posgen(w, F, params["w1"], params["b1"], params["w2"], params["b2"], r), axis=1)
+        used = 0
+        for name, arr in params.items():
+            for idx in np.ndindex(arr.shape):
+                pert = {k: v.copy() for k, v in params.items()}
+                pert[name][idx] += 1e-3
+                out = np.concatenate(oracle.posgen(w, F, pert["w1"], pert["b1"], pert["w2"], pert["b2"], r), axis=1)
+                used += int(np.abs(out - base).max() > 1e-9)
+        counts[w] = used
+    assert set(counts.values()) == {oracle.mlp_param_count(F, hid, r)}, counts
+    assert oracle.mlp_param_count(F, hid, r) == sum(a.size for a in params.values())
