@@ -16,8 +16,11 @@
  *
  * Conventions shared by every entry point
  *  - Pointers marked (device) are HIP device pointers, caller-allocated and
- *    caller-owned; the library never allocates or frees device memory and
- *    keeps no global mutable device state. Pointers to structs are host.
+ *    caller-owned; the library never allocates or frees device memory. Pointers
+ *    to structs are host. Host-side state: a per-device record of two fixed
+ *    facts (compute units, and workgroups per CU of the forward kernel) filled
+ *    once under a mutex, and the timing registry below; both are safe to use
+ *    from several host threads.
  *  - Tensors are dense, row-major, innermost dimension last, and 16-byte
  *    aligned. A feature map is [B, H, W, heads, d_c].
  *  - Windows are square, non-overlapping, unshifted and unpadded: H and W
@@ -188,7 +191,10 @@ rib_status_t rib_window_attn_fwd_gated(const rib_shape_t* shape, rib_dtype_t dty
 size_t rib_bwd_workspace_size(const rib_shape_t* shape, rib_dtype_t dtype);
 
 /*
- * rib_window_attn_bwd - gradients of the forward above given dO.
+ * rib_window_attn_bwd - gradients of the forward above given dO, for training
+ * [EN §4 "Efficiency": the RIB network trains 2.1x faster than the RPB one;
+ * ABS: RIB cuts training and inference time; DE §2.A.2: the MLP that makes
+ * Q_p, K_p is learned, so the positional tokens need gradients as well].
  *
  * Recomputes P from LSE (no N x N buffer) and returns the content-token
  * gradients dQ_c, dK_c, dV and the positional-token gradients dQ_p, dK_p,

@@ -148,6 +148,20 @@ def bwd_workspace_size(shape: Shape, dtype: torch.dtype) -> int:
     return int(lib().rib_bwd_workspace_size(ctypes.byref(shape), _dtype_code(dtype)))
 
 
+def _run_stream(stream, device, tensors):
+    """The stream handle of a plan's run(): the current stream, or the raw hipStream_t `stream`. For
+    a raw stream the plan's tensors are recorded on it, so the caching allocator does not hand
+    their memory to other work before the kernels queued there have finished with it (the plan
+    may be dropped first)."""
+    if stream is None:
+        return _stream(device)
+    ext = torch.cuda.ExternalStream(stream, device=device)
+    for t in tensors:
+        if t is not None:
+            t.record_stream(ext)
+    return ctypes.c_void_p(stream)
+
+
 def _workspace(nbytes: int, device) -> torch.Tensor:
     # torch's caching allocator returns 256-byte (or better) aligned blocks
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
@@ -239,8 +253,9 @@ class FwdPlan:
         self.ws = _workspace(self.ws_bytes, q_c.device)
 
     def run(self, stream=None):
+        """Enqueues the call on the current stream, or on `stream` (a raw hipStream_t handle)."""
         q_c, k_c, v, q_p, k_p = self.inputs
-        st = _stream(q_c.device) if stream is None else ctypes.c_void_p(stream)
+        st = _run_stream(stream, q_c.device, (*self.inputs, self.o, self.lse, self.ws))
         _check(lib().rib_window_attn_fwd(ctypes.byref(self.shape), self.dtype, self.scale, _ptr(q_c), _ptr(k_c),
                                          _ptr(v), _ptr(q_p), _ptr(k_p), _ptr(self.o), _ptr(self.lse),
                                          _ptr(self.ws), self.ws_bytes, st))
@@ -309,8 +324,9 @@ class BwdPlan:
         self.ws = _workspace(self.ws_bytes, q_c.device)
 
     def run(self, stream=None):
+        """Enqueues the call on the current stream, or on `stream` (a raw hipStream_t handle)."""
         q_c, k_c, v, q_p, k_p, o, lse, d_o = self.inputs
-        st = _stream(q_c.device) if stream is None else ctypes.c_void_p(stream)
+        st = _run_stream(stream, q_c.device, (*self.inputs, self.dq, self.dk, self.dv, self.dqp, self.dkp, self.ws))
         _check(lib().rib_window_attn_bwd(ctypes.byref(self.shape), self.dtype, self.scale, _ptr(q_c), _ptr(k_c),
                                          _ptr(v), _ptr(q_p), _ptr(k_p), _ptr(o), _ptr(lse), _ptr(d_o),
                                          _ptr(self.dq), _ptr(self.dk), _ptr(self.dv), _ptr(self.dqp),
@@ -354,8 +370,9 @@ class RpbFwdPlan:
         self.ws = _workspace(self.ws_bytes, q_c.device)
 
     def run(self, stream=None):
+        """Enqueues the call on the current stream, or on `stream` (a raw hipStream_t handle)."""
         q_c, k_c, v, table = self.inputs
-        st = _stream(q_c.device) if stream is None else ctypes.c_void_p(stream)
+        st = _run_stream(stream, q_c.device, (*self.inputs, self.o, self.lse, self.ws))
         _check(lib().rib_rpb_window_attn_fwd(ctypes.byref(self.shape), self.dtype, self.scale, _ptr(q_c), _ptr(k_c),
                                              _ptr(v), _ptr(table), _ptr(self.o), _ptr(self.lse), _ptr(self.ws),
                                              self.ws_bytes, st))

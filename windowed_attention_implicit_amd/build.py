@@ -28,6 +28,9 @@ COMMON_FLAGS = [
     # no packed fp32 instructions: compile plain float code to scalar VALU ops
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     f"-I{INCLUDE}", f"-I{CSRC}",
+    # per-kernel register / scratch report, checked below: no kernel of the library may spill
+    # registers to scratch memory
+    "-Rpass-analysis=kernel-resource-usage",
 ]
 # Per-file extra flags. The backward kernels keep more live state than 256
 # arch VGPRs; left to its heuristics the compiler then gives the score / dP
@@ -46,13 +49,32 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain (ROCm) is required to build librib.so")
 
 
+def _scratch_kernels(remarks: str) -> list:
+    """Kernels whose resource-usage remarks report scratch (per-lane stack memory): register
+    spills to memory. Spills into the accumulation registers (AGPRs) use no memory and pass."""
+    bad, name = [], None
+    for line in remarks.splitlines():
+        if "remark: Function Name:" in line:
+            name = line.split("Function Name:")[1].split("[-Rpass")[0].strip()
+        elif "ScratchSize [bytes/lane]:" in line:
+            n = int(line.split("ScratchSize [bytes/lane]:")[1].split("[-Rpass")[0].strip())
+            if n:
+                bad.append(f"{name} ({n} bytes per lane)")
+    return bad
+
+
 def _compile(hipcc: str, src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
     cmd = [hipcc, *COMMON_FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     proc = subprocess.run(cmd, capture_output=True, text=True)
-    msgs = "\n".join(l for l in (proc.stdout + proc.stderr).splitlines() if "packed-fp32-ops" not in l)
+    out = proc.stdout + proc.stderr
+    msgs = "\n".join(l for l in out.splitlines()
+                     if "packed-fp32-ops" not in l and "kernel-resource-usage" not in l)
     if proc.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{msgs}")
+    spills = _scratch_kernels(out)
+    if spills:
+        raise RuntimeError(f"{src}: kernels spill registers to scratch memory: " + "; ".join(spills))
     if verbose and msgs.strip():
         print(msgs, file=sys.stderr)
     return obj

@@ -444,22 +444,31 @@ size_t rib_bwd_workspace_size(const rib_shape_t* shape, rib_dtype_t dtype) {
   return bwd_layout(g, dtype, nullptr).bytes;
 }
 
+// Every argument of a forward call except the workspace (B == 0 skips the pointer checks).
+static rib_status_t check_fwd_args(const rib_shape_t* shape, rib_dtype_t dtype, float scale, const void* q_c,
+                                   const void* k_c, const void* v, const void* q_p, const void* k_p,
+                                   const void* gate, const void* o, const float* lse) {
+  RIB_TRY(check_shape(shape, dtype, true));
+  if (!(scale == scale) || isinf(scale)) return fail(RIB_ERR_INVALID_ARG, "scale is not finite");
+  if (shape->B == 0) return RIB_OK;
+  RIB_TRY(check_ptr(q_c, "q_c"));
+  RIB_TRY(check_ptr(k_c, "k_c"));
+  RIB_TRY(check_ptr(v, "v"));
+  RIB_TRY(check_ptr(q_p, "q_p"));
+  RIB_TRY(check_ptr(k_p, "k_p"));
+  RIB_TRY(check_ptr(o, "o"));
+  if (gate) RIB_TRY(check_ptr(gate, "gate"));
+  if (lse && ((uintptr_t)lse & 3u)) return fail(RIB_ERR_INVALID_ARG, "lse is not 4-byte aligned");
+  return RIB_OK;
+}
+
 static rib_status_t attn_fwd_impl(const rib_shape_t* shape, rib_dtype_t dtype, float scale, const void* q_c,
                                   const void* k_c, const void* v, const void* q_p, const void* k_p,
                                   const void* gate, void* o, float* lse, void* workspace, size_t workspace_bytes,
                                   rib_stream_t stream) {
   {
-    RIB_TRY(check_shape(shape, dtype, true));
-    if (!(scale == scale) || isinf(scale)) return fail(RIB_ERR_INVALID_ARG, "scale is not finite");
+    RIB_TRY(check_fwd_args(shape, dtype, scale, q_c, k_c, v, q_p, k_p, gate, o, lse));
     if (shape->B == 0) return ok();
-    RIB_TRY(check_ptr(q_c, "q_c"));
-    RIB_TRY(check_ptr(k_c, "k_c"));
-    RIB_TRY(check_ptr(v, "v"));
-    RIB_TRY(check_ptr(q_p, "q_p"));
-    RIB_TRY(check_ptr(k_p, "k_p"));
-    RIB_TRY(check_ptr(o, "o"));
-    if (gate) RIB_TRY(check_ptr(gate, "gate"));
-    if (lse && ((uintptr_t)lse & 3u)) return fail(RIB_ERR_INVALID_ARG, "lse is not 4-byte aligned");
     Geom g = make_geom(*shape);
     const size_t need = fwd_layout(g, dtype, nullptr).bytes;
     if (!workspace || workspace_bytes < need)
@@ -471,23 +480,7 @@ static rib_status_t attn_fwd_impl(const rib_shape_t* shape, rib_dtype_t dtype, f
     const int rp = padded_rank(g.r);
     hipError_t e;
     const bool bf = mfma_path(g, dtype);
-    TimedGroup t_part(RIB_KERNEL_PARTITION, st);
-    if (L.qp) {   // positional rows padded to rp (the fused gather below reads K_p)
-      if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, q_p, es, L.qp, st)) != hipSuccess)
-        return hip_fail(e, "pack q_p");
-      if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, k_p, es, L.kp, st)) != hipSuccess)
-        return hip_fail(e, "pack k_p");
-    }
     const void* kp_rows = L.kp ? L.kp : k_p;
-    if (bf) {
-      // K_c rows, V^T kappa and the key-norm partial maxima in one pass
-      if ((e = launch_gather_kv_bound(g, rp, k_c, v, kp_rows, L.kw, L.vw, L.kmax2, st)) != hipSuccess)
-        return hip_fail(e, "partition k, v");
-    } else {
-      if ((e = launch_partition(g, es, q_c, L.qw, st)) != hipSuccess) return hip_fail(e, "partition q");
-      if ((e = launch_partition(g, es, k_c, L.kw, st)) != hipSuccess) return hip_fail(e, "partition k");
-      if ((e = launch_partition(g, es, v, L.vw, st)) != hipSuccess) return hip_fail(e, "partition v");
-    }
     FwdArgs a;
     a.g = g;
     a.c = resolve_scale(scale, shape) * kLog2e;
@@ -500,7 +493,24 @@ static rib_status_t attn_fwd_impl(const rib_shape_t* shape, rib_dtype_t dtype, f
     a.rp = rp;
     a.gate = gate;
     a.part = L.part;
+    // the split plan queries the device (it can fail), so it is made before anything is launched
     if (bf && (e = plan_fwd_split(a)) != hipSuccess) return hip_fail(e, "split plan");
+    TimedGroup t_part(RIB_KERNEL_PARTITION, st);
+    if (L.qp) {   // positional rows padded to rp (the fused gather below reads K_p)
+      if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, q_p, es, L.qp, st)) != hipSuccess)
+        return hip_fail(e, "pack q_p");
+      if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, k_p, es, L.kp, st)) != hipSuccess)
+        return hip_fail(e, "pack k_p");
+    }
+    if (bf) {
+      // K_c rows, V^T kappa and the key-norm partial maxima in one pass
+      if ((e = launch_gather_kv_bound(g, rp, k_c, v, kp_rows, L.kw, L.vw, L.kmax2, st)) != hipSuccess)
+        return hip_fail(e, "partition k, v");
+    } else {
+      if ((e = launch_partition(g, es, q_c, L.qw, st)) != hipSuccess) return hip_fail(e, "partition q");
+      if ((e = launch_partition(g, es, k_c, L.kw, st)) != hipSuccess) return hip_fail(e, "partition k");
+      if ((e = launch_partition(g, es, v, L.vw, st)) != hipSuccess) return hip_fail(e, "partition v");
+    }
     t_part.end();
     TimedGroup t_attn(RIB_KERNEL_ATTN_FWD, st);
     e = bf ? launch_attn_fwd_bf16(a, st) : launch_attn_fwd_simple(a, es, st);
