@@ -18,9 +18,11 @@
  *  - Pointers marked (device) are HIP device pointers, caller-allocated and
  *    caller-owned; the library never allocates or frees device memory. Pointers
  *    to structs are host. Host-side state: a per-device record of two fixed
- *    facts (compute units, and workgroups per CU of the forward kernel) filled
- *    once under a mutex, and the timing registry below; both are safe to use
- *    from several host threads.
+ *    facts (compute units, and workgroups per CU of the forward kernel) and of
+ *    the address of the allocation-free forward's workspace array, each filled
+ *    once under a mutex, and the timing registry below; all are safe to use
+ *    from several host threads. Device-side state: that one array per GPU
+ *    (rib_window_attn_fwd_noalloc), used by no other entry point.
  *  - Tensors are dense, row-major, innermost dimension last, and 16-byte
  *    aligned. A feature map is [B, H, W, heads, d_c].
  *  - Windows are square, non-overlapping, unshifted and unpadded: H and W
@@ -146,6 +148,29 @@ rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
                                  void* o, float* lse,
                                  void* workspace, size_t workspace_bytes,
                                  rib_stream_t stream);
+
+/*
+ * rib_window_attn_fwd_noalloc - rib_window_attn_fwd for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): no workspace argument, and nothing is allocated.
+ *
+ * The workspace is an array of RIB_NOALLOC_WORKSPACE_BYTES in the library's own device
+ * memory, one per GPU, held from the library's first use on that GPU until the process
+ * ends; the first call on a GPU looks up its address there (a caller that captures graphs
+ * makes one call before capturing). Shapes whose rib_fwd_workspace_size() exceeds it return
+ * RIB_ERR_WORKSPACE: the 16x16 and 32x32 window layers of a [2, 192, 192, 6, 32] map fit
+ * (57 MB); the 96x96 workload of 16 windows x 6 heads (about 150 MB) does not. Every call
+ * on one GPU uses that GPU's array and overwrites it, so calls that overlap on one GPU
+ * (several streams, several host threads) race: the caller serialises them. No part of the
+ * array needs clearing: each call writes everything it reads. `stream` must belong to the
+ * current device (RIB_ERR_INVALID_ARG otherwise). Arguments, outputs and other errors as
+ * for rib_window_attn_fwd.
+ */
+#define RIB_NOALLOC_WORKSPACE_BYTES ((size_t)64 << 20)
+rib_status_t rib_window_attn_fwd_noalloc(const rib_shape_t* shape, rib_dtype_t dtype, float scale,
+                                         const void* q_c, const void* k_c, const void* v,
+                                         const void* q_p, const void* k_p,
+                                         void* o, float* lse, rib_stream_t stream);
 
 /*
  * rib_cla_gate - the gating map of convolutional local attention (CLA) [EN §2.B: a

@@ -91,6 +91,30 @@ def test_fwd_validation(L):
     assert _fwd(L, rib.Shape(0, 192, 192, 6, 32, 96, 16), ptrs=[None] * 6, ws=None, ws_bytes=0) == rib.RIB_OK
 
 
+def test_fwd_noalloc_validation(L):
+    """The allocation-free forward: argument errors as for the forward, shapes whose workspace
+    exceeds the library's per-GPU array rejected before any device call, empty batches valid."""
+    def call(shape, ptrs=None, dtype=rib.RIB_BF16):
+        p = ptrs or [FAKE] * 6
+        return L.rib_window_attn_fwd_noalloc(ctypes.byref(shape), dtype, 0.0, p[0], p[1], p[2], p[3], p[4], p[5],
+                                             None, None)
+    assert call(rib.Shape(2, 190, 192, 6, 32, 32, 16)) == rib.RIB_ERR_INVALID_ARG
+    assert call(rib.Shape(2, 192, 192, 6, 32, 32, 16), ptrs=[FAKE, None, FAKE, FAKE, FAKE, FAKE]) == \
+        rib.RIB_ERR_INVALID_ARG
+    assert call(rib.Shape(2, 192, 192, 6, 32, 32, 16), ptrs=[FAKE, FAKE, MISALIGNED, FAKE, FAKE, FAKE]) == \
+        rib.RIB_ERR_INVALID_ARG
+    # the 96x96 workload needs about 150 MB of workspace: more than the array holds
+    big = rib.Shape(4, 192, 192, 6, 32, 96, 16)
+    assert L.rib_fwd_workspace_size(ctypes.byref(big), rib.RIB_BF16) > rib.NOALLOC_WORKSPACE_BYTES
+    assert call(big) == rib.RIB_ERR_WORKSPACE
+    assert b"allocation-free" in L.rib_last_error()
+    # the small-window layers of a [2, 192, 192, 6, 32] map fit
+    for w in (16, 32):
+        s = rib.Shape(2, 192, 192, 6, 32, w, 16)
+        assert 0 < L.rib_fwd_workspace_size(ctypes.byref(s), rib.RIB_BF16) <= rib.NOALLOC_WORKSPACE_BYTES
+    assert call(rib.Shape(0, 192, 192, 6, 32, 32, 16)) == rib.RIB_OK
+
+
 def test_rpb_validation(L):
     good = rib.Shape(2, 192, 192, 6, 32, 96, 0)     # r is ignored by the RPB kernel
 

@@ -29,7 +29,7 @@ __all__ = [
     "posgen", "posgen_bwd", "window_partition", "window_unpartition", "window_attn_fwd", "window_attn_bwd",
     "fwd_workspace_size", "bwd_workspace_size", "FwdPlan", "BwdPlan", "Shape",
     "rpb_window_attn_fwd", "rpb_fwd_workspace_size", "RpbFwdPlan",
-    "cla_gate", "window_attn_fwd_gated",
+    "cla_gate", "window_attn_fwd_gated", "window_attn_fwd_noalloc", "NOALLOC_WORKSPACE_BYTES",
     "KERNEL_GROUPS", "kernel_timing_enable", "kernel_timing_select", "kernel_timing_read",
 ]
 
@@ -73,6 +73,7 @@ _SIGS = {
     "rib_rpb_fwd_workspace_size": (_sz, [ctypes.POINTER(Shape), _i32]),
     "rib_cla_gate": (_i32, [ctypes.POINTER(Shape), _i32] + [_vp] * 6 + [_vp]),
     "rib_window_attn_fwd_gated": (_i32, [ctypes.POINTER(Shape), _i32, _f32] + [_vp] * 8 + [_vp, _sz, _vp]),
+    "rib_window_attn_fwd_noalloc": (_i32, [ctypes.POINTER(Shape), _i32, _f32] + [_vp] * 7 + [_vp]),
     "rib_rpb_window_attn_fwd": (_i32, [ctypes.POINTER(Shape), _i32, _f32] + [_vp] * 6 + [_vp, _sz, _vp]),
     "rib_kernel_timing_enable": (_i32, [_i32]),
     "rib_kernel_timing_select": (_i32, [ctypes.c_uint32]),
@@ -279,6 +280,22 @@ def window_attn_fwd_gated(q_c, k_c, v, q_p, k_p, gate, w: int, scale: float | No
                                            _ptr(v), _ptr(q_p), _ptr(k_p), _ptr(gate), _ptr(plan.o), _ptr(plan.lse),
                                            _ptr(plan.ws), plan.ws_bytes, _stream(q_c.device)))
     return plan.o, plan.lse
+
+
+NOALLOC_WORKSPACE_BYTES = 64 << 20
+
+
+def window_attn_fwd_noalloc(q_c, k_c, v, q_p, k_p, w: int, o=None, lse=None, scale: float | None = None):
+    """The forward through the allocation-free entry point (its workspace is the library's own
+    per-GPU array of NOALLOC_WORKSPACE_BYTES). Writes into `o` / `lse` when given (`lse` may be
+    None), else allocates them here in Python; returns (O, LSE or None)."""
+    _require_gpu(q_c, k_c, v, q_p, k_p, o, lse)
+    shape = _shape_of(q_c, w, q_p.shape[1])
+    o = torch.empty_like(q_c) if o is None else o
+    _check(lib().rib_window_attn_fwd_noalloc(ctypes.byref(shape), _dtype_code(q_c.dtype),
+                                             0.0 if scale is None else float(scale), _ptr(q_c), _ptr(k_c), _ptr(v),
+                                             _ptr(q_p), _ptr(k_p), _ptr(o), _ptr(lse), _stream(q_c.device)))
+    return o, lse
 
 
 def cla_gate(x: torch.Tensor, w_dw: torch.Tensor, b_dw, w_pw: torch.Tensor, b_pw, heads: int,

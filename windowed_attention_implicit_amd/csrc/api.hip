@@ -269,6 +269,50 @@ class TimedGroup {
   bool on_ = false;
 };
 
+// ---- workspace of the allocation-free forward: a file-scope array in device memory, one per
+// GPU the library runs on, held until the process ends. In host code `scratch` names a host-side
+// stand-in, not the array: kernels get the address hipGetSymbolAddress returns on each device.
+static __device__ __align__(256) unsigned char scratch[RIB_NOALLOC_WORKSPACE_BYTES];
+
+struct ScratchTable {
+  std::mutex mu;
+  void* ptr[64] = {};
+};
+
+ScratchTable& scratch_table() {
+  static ScratchTable t;
+  return t;
+}
+
+// The array's address on the device `stream` belongs to, which must be the current device
+// (*wrong_device is set otherwise); looked up once per device.
+hipError_t scratch_address(hipStream_t stream, void** out, bool* wrong_device, int* devs) {
+  *wrong_device = false;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (stream) {
+    hipDevice_t sd = 0;
+    if ((e = hipStreamGetDevice(stream, &sd)) != hipSuccess) return e;
+    if ((int)sd != dev) {
+      *wrong_device = true;
+      devs[0] = (int)sd;
+      devs[1] = dev;
+      return hipSuccess;
+    }
+  }
+  if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+  ScratchTable& t = scratch_table();
+  std::lock_guard<std::mutex> lk(t.mu);
+  if (!t.ptr[dev]) {
+    void* p = nullptr;
+    if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch))) != hipSuccess) return e;
+    t.ptr[dev] = p;
+  }
+  *out = t.ptr[dev];
+  return hipSuccess;
+}
+
 float resolve_scale(float scale, const rib_shape_t* s) {
   return scale > 0.f ? scale : 1.0f / sqrtf((float)(s->d_c + s->r));
 }
@@ -552,6 +596,32 @@ rib_status_t rib_window_attn_fwd_gated(const rib_shape_t* shape, rib_dtype_t dty
                          stream);
   } catch (...) {
     return fail(RIB_ERR_HIP, "unexpected C++ exception in rib_window_attn_fwd_gated");
+  }
+}
+
+rib_status_t rib_window_attn_fwd_noalloc(const rib_shape_t* shape, rib_dtype_t dtype, float scale, const void* q_c,
+                                         const void* k_c, const void* v, const void* q_p, const void* k_p, void* o,
+                                         float* lse, rib_stream_t stream) {
+  try {
+    RIB_TRY(check_fwd_args(shape, dtype, scale, q_c, k_c, v, q_p, k_p, nullptr, o, lse));
+    const size_t need = fwd_layout(make_geom(*shape), dtype, nullptr).bytes;
+    if (need > RIB_NOALLOC_WORKSPACE_BYTES)
+      return fail(RIB_ERR_WORKSPACE,
+                  "this shape needs %zu bytes of workspace, more than the %zu the allocation-free forward holds "
+                  "per GPU; call rib_window_attn_fwd with a caller workspace",
+                  need, (size_t)RIB_NOALLOC_WORKSPACE_BYTES);
+    if (shape->B == 0) return ok();
+    void* ws = nullptr;
+    bool wrong = false;
+    int devs[2] = {0, 0};
+    hipError_t e = scratch_address((hipStream_t)stream, &ws, &wrong, devs);
+    if (e != hipSuccess) return hip_fail(e, "allocation-free forward: workspace address");
+    if (wrong)
+      return fail(RIB_ERR_INVALID_ARG, "stream belongs to device %d but device %d is current", devs[0], devs[1]);
+    return attn_fwd_impl(shape, dtype, scale, q_c, k_c, v, q_p, k_p, nullptr, o, lse, ws,
+                         RIB_NOALLOC_WORKSPACE_BYTES, stream);
+  } catch (...) {
+    return fail(RIB_ERR_HIP, "unexpected C++ exception in rib_window_attn_fwd_noalloc");
   }
 }
 
