@@ -67,14 +67,16 @@ class FwdStep:
         self.w1 = torch.from_numpy(x["w1"]).to(dev)
         self.w2 = torch.from_numpy(x["w2"]).to(dev)
         self.mlp = rib._Mlp(wl.n_freq, wl.hidden, wl.r, self.w1.data_ptr(), None, self.w2.data_ptr(), None)
-        self.qp = torch.empty((wl.N, wl.r), dtype=torch.bfloat16, device=dev)
+        dt = torch.float32 if wl.dtype == "f32" else torch.bfloat16
+        self.pos_code = rib.RIB_F32 if wl.dtype == "f32" else rib.RIB_BF16
+        self.qp = torch.empty((wl.N, wl.r), dtype=dt, device=dev)
         self.kp = torch.empty_like(self.qp)
         self.plan = rib.FwdPlan(self.q, self.k, self.v, self.qp, self.kp, wl.w)
 
     def run(self):
         L = self.rib.lib()
         st = self.rib._stream(self.q.device)
-        self.rib._check(L.rib_posgen(self.wl.w, ctypes.byref(self.mlp), self.rib.RIB_BF16,
+        self.rib._check(L.rib_posgen(self.wl.w, ctypes.byref(self.mlp), self.pos_code,
                                      ctypes.c_void_p(self.qp.data_ptr()), ctypes.c_void_p(self.kp.data_ptr()), st))
         self.plan.run()
 
@@ -257,6 +259,85 @@ def stack_measure(steps: int, warmup: int, dev):
             "layers": per}
 
 
+def group_ms(fn, steps: int, groups):
+    """Average per-call time of each kernel group of fn, from a loop of its own with every group timed."""
+    import windowed_attention_implicit_amd as rib
+    rib.kernel_timing_enable(True)
+    for g in rib.KERNEL_GROUPS:
+        rib.kernel_timing_read(g)
+    time_steps(fn, steps, 2, lambda: [rib.kernel_timing_read(g) for g in rib.KERNEL_GROUPS])
+    out = {}
+    for g in groups:
+        t, n = rib.kernel_timing_read(g)
+        out[g] = round(t / steps, 5) if n else None
+    rib.kernel_timing_enable(False)
+    return out
+
+
+def configs_measure(steps: int, dev):
+    """The other forward workloads the method is measured on (single 16x16 window in float32; 32x32
+    windows on a 256x256 map, 6 heads, r = 8; 64x64 windows on a 128x128 map x 8, r = 16): one
+    step = posgen + gathers + attention (+ split-tail combine), the same step as the headline."""
+    import rib_synth
+    import windowed_attention_implicit_amd as rib
+    out = {}
+    for name in ("w16_single_fp32", "w32_map256_bf16", "w64_map128x8_bf16"):
+        wl = rib_synth.WORKLOADS[name]
+        x = rib_synth.make_inputs(wl)
+        step = FwdStep(wl, x, dev)
+        rib.kernel_timing_enable(False)
+        ms, _ = time_steps(step.run, steps, 5)
+        groups = group_ms(step.run, steps, ("posgen", "partition", "attn_fwd", "unpartition"))
+        flops = fwd_flops(wl.units, wl.N, wl.d_c, wl.r)
+        ktot = sum(v for v in groups.values() if v)
+        out[name] = {
+            "workload": (f"{wl.windows} window(s) of {wl.w}x{wl.w} (N={wl.N}) on a {wl.H}x{wl.W} map x {wl.B}, "
+                         f"{wl.heads} heads, d_c={wl.d_c}, r={wl.r}, {wl.dtype}"),
+            "ms_per_step": round(ms, 5), "tflops": round(flops / ms / 1e9, 3),
+            "windows_per_s": round(wl.windows / (ms / 1e3), 1), "window_heads_per_s": round(wl.units / (ms / 1e3), 1),
+            "pct_of_bf16_peak": round(100 * flops / ms / 1e9 / PEAK_BF16_TFLOPS, 2) if wl.dtype == "bf16" else None,
+            "kernel_ms": groups,
+            "attn_kernel_tflops": groups["attn_fwd"] and round(flops / groups["attn_fwd"] / 1e9, 1),
+            "gather_share_of_kernel_time": groups["partition"] and round(groups["partition"] / ktot, 3),
+            "note": ("kernel groups: posgen; partition = the K/V gather (+ packing of Q_p, K_p when r is not 16 or "
+                     "32); attn_fwd = the attention kernel; unpartition = the split-tail combine (bf16) or the O "
+                     "scatter (float32); the gaps between launches are the rest of the step"),
+        }
+    return out
+
+
+def tiers_measure(wl, x, dev, steps: int):
+    """What the bounded softmax costs when it cannot go unshifted, on the headline shape: Q_c and K_c
+    scaled by 3 (score bounds above 64 log2 units: the shifted tier), and one key per window with 127
+    in channel 0 (bounds ~150 log2 units above most rows' largest score: row sums underflow the guard
+    and every workgroup reruns its rows with the exact online-softmax pass)."""
+    import torch
+    import windowed_attention_implicit_amd as rib
+    q, k, v = (to_gpu(x[n], dev) for n in ("q_c", "k_c", "v"))
+    w1, w2 = torch.from_numpy(x["w1"]).to(dev), torch.from_numpy(x["w2"]).to(dev)
+    qp, kp = rib.posgen(wl.w, w1, None, w2, None, wl.r, out_dtype=torch.bfloat16)
+    k_big = k.clone()
+    k_big[:, ::wl.w, ::wl.w, :, 0] = 127.0
+    cases = {"unshifted (N(0,1) inputs)": (q, k), "shifted (Q_c, K_c x 3)": ((q.float() * 3).to(torch.bfloat16),
+                                                                          (k.float() * 3).to(torch.bfloat16)),
+             "exact pass (one key per window with 127 in channel 0)": (q, k_big)}
+    plans = {name: rib.FwdPlan(qq, kk, v, qp, kp, wl.w) for name, (qq, kk) in cases.items()}
+    rib.kernel_timing_select("attn_fwd")
+    res = {}
+    for name, plan in plans.items():
+        for _ in range(2):
+            plan.run()
+        torch.cuda.synchronize()
+        rib.kernel_timing_read("attn_fwd")
+        for _ in range(steps):
+            plan.run()
+        t, n = rib.kernel_timing_read("attn_fwd")
+        res[name] = round(t / n, 5)
+    rib.kernel_timing_select()
+    base = res["unshifted (N(0,1) inputs)"]
+    return {"attn_kernel_ms": res, "slowdown": {k2: round(v2 / base, 3) for k2, v2 in res.items()}}
+
+
 def rpb_compare(wl, x, dev, steps: int, rib_attn_ms: float):
     """The relative-position-bias attention that RIB replaces, on the same Q_c, K_c, V: the RPB
     kernel (bias gathered per score from an fp16 (2w-1)^2 table in LDS) against the RIB attention
@@ -356,6 +437,11 @@ def main():
                     help="also time the window-size stack 16/32/64/96, forward + backward")
     ap.add_argument("--no-rpb", action="store_true",
                     help="skip the relative-position-bias comparison kernel")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other forward workloads (16x16 float32, 32x32, 64x64 windows)")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="time the headline step only (no CLA, tiers, other workloads, RPB, stack or CPU "
+                         "baseline): the command the profiler runs")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -474,8 +560,18 @@ def main():
         torch.cuda.synchronize()
         result["calibration_copy_bytes"] = 2 * n * 4
 
-    print("bench: CLA gate", file=sys.stderr, flush=True)
-    result["cla"] = cla_measure(wl, x, step, dev, max(10, args.steps // 2))
+    if args.only_headline:
+        args.no_configs = args.no_rpb = args.no_cpu_baseline = True
+        args.stack = False
+    else:
+        print("bench: CLA gate", file=sys.stderr, flush=True)
+        result["cla"] = cla_measure(wl, x, step, dev, max(10, args.steps // 2))
+        print("bench: softmax tiers", file=sys.stderr, flush=True)
+        result["softmax_tiers"] = tiers_measure(wl, x, dev, max(10, args.steps // 2))
+
+    if not args.no_configs:
+        print("bench: other workloads", file=sys.stderr, flush=True)
+        result["configs"] = configs_measure(max(10, args.steps // 2), dev)
 
     if not args.no_rpb:
         print("bench: RPB comparison kernel", file=sys.stderr, flush=True)

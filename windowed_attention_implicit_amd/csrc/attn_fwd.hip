@@ -57,11 +57,13 @@ constexpr int kKeyTile = 64;
 constexpr float kLazyTau = 8.0f;          // log2 units
 constexpr float kUnderflowGuard = 8.673617379884035e-19f;  // 2^-60
 constexpr int kKeyBoundTile = 64;         // keys per partial key-norm maximum (one per gather block)
-// Tiers of the bounded softmax with one positional K-step: when every score bound of a
-// workgroup's rows is at most kNoShiftMax (log2 units) and every |v| of the unit at most
-// kNoShiftVMax, P = exp2(S') needs no shift at all: P lies in [2^-64, 2^64], the row sums
-// and O accumulators stay below 2^14 * 2^64 * 2^40 < 2^128, and the score MFMA takes the
-// constant 0 as its accumulator input. Otherwise scores are shifted by the bound.
+// Tiers of the bounded softmax with one positional K-step. P = exp2(S' - s) may reach 2^64
+// when every |v| of the unit is at most kNoShiftVMax: the row sums and O accumulators then
+// stay below 2^14 * 2^64 * 2^40 < 2^128. So the shift of row i is s_i = max(0, m_i - 64)
+// with m_i its score bound; when every s_i of a workgroup is 0, P = exp2(S') needs no shift
+// at all and P lies in [2^-64, 2^64] (no underflow either). A row sum can fall below the
+// underflow guard only when the bound overshoots the row's largest score by more than
+// 124 log2 units. With a larger |v| the shift is the bound itself (P <= 1).
 constexpr float kNoShiftMax = 64.0f;
 constexpr float kNoShiftVMax = 1099511627776.0f;   // 2^40
 
@@ -412,10 +414,13 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
     // are formed (slot 9), nb 1 scores are formed at the start of their own half step. The
     // last block's R and P wait for the next half step. K fragments of h+1 are read after
     // slot 3, V^T fragment 1 of h after slot 7 and fragment 0 of h+1 after slot 15.
-    const bool shift = __syncthreads_or(!(fmaxf(mref[0], mref[1]) <= kNoShiftMax) || !(vm <= kNoShiftVMax));
+    const bool small_v = vm <= kNoShiftVMax;
+    const bool shift = __syncthreads_or(!(fmaxf(mref[0], mref[1]) <= kNoShiftMax) || !small_v);
     auto fast_pass = [&](auto tier) {
       constexpr bool SH = decltype(tier)::value;
-      const float msub[2] = {SH ? mref[0] : 0.f, SH ? mref[1] : 0.f};
+      float msub[2];
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) msub[nb] = !SH ? 0.f : (small_v ? fmaxf(mref[nb] - kNoShiftMax, 0.f) : mref[nb]);
       f32x16 sc[2];
       bf16x8 kf[C::kSteps], vf[2];
       u32x4 wd[2][2];
@@ -539,7 +544,7 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
         l_run[nb] = half == 0 ? (l32 < 16 ? r0 : r1) : 0.f;
         // keys past N have zero K rows: their P is exp2(0 - shift), rounded as the MFMA saw it
         if (t1 == nkt)
-          pad_sub[nb] = (float)(nkt * kKeyTile - N) * (SH ? (float)f32_to_bf16(__builtin_amdgcn_exp2f(-mref[nb])) : 1.f);
+          pad_sub[nb] = (float)(nkt * kKeyTile - N) * (SH ? (float)f32_to_bf16(__builtin_amdgcn_exp2f(-msub[nb])) : 1.f);
       }
     };
     if (shift) fast_pass(BoolTag<true>());
