@@ -120,10 +120,12 @@ rib_status_t rib_window_unpartition(const rib_shape_t* shape, rib_dtype_t dtype,
                                     const void* x_win, void* x, rib_stream_t stream);
 
 /* Bytes of device workspace rib_window_attn_fwd needs for this shape (0 when
- * the shape is invalid). Linear in the feature-map size: no N x N buffer. At
- * w*w >= 2048 tokens the bf16 path also reserves room for the partial results
- * of its split tail: at most 1024 pieces of 34 KiB (about 34 MiB), and 4 per
- * eight work items of 256 queries when there are fewer. */
+ * the shape is invalid, at least 256 otherwise). Linear in the feature-map size:
+ * no N x N buffer. bf16 windows whose side divides 64 (8, 16, 32, 64) with
+ * r <= 16 read K_c and V in their maps and gather nothing. At w*w >= 2048 tokens
+ * the bf16 path also reserves room for the partial results of its split tail:
+ * at most 1024 pieces of 34 KiB (about 34 MiB), and 4 per eight work items of
+ * 256 queries when there are fewer. */
 size_t rib_fwd_workspace_size(const rib_shape_t* shape, rib_dtype_t dtype);
 
 /*
@@ -158,8 +160,9 @@ rib_status_t rib_window_attn_fwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
  * memory, one per GPU, held from the library's first use on that GPU until the process
  * ends; the first call on a GPU looks up its address there (a caller that captures graphs
  * makes one call before capturing). Shapes whose rib_fwd_workspace_size() exceeds it return
- * RIB_ERR_WORKSPACE: the 16x16 and 32x32 window layers of a [2, 192, 192, 6, 32] map fit
- * (57 MB); the 96x96 workload of 16 windows x 6 heads (about 150 MB) does not. Every call
+ * RIB_ERR_WORKSPACE: the 16x16, 32x32 and 64x64 window layers of a [2, 192, 192, 6, 32] map
+ * fit (their K_c and V are read in place; at most the split tail's 35 MB), the 96x96 workload
+ * of 16 windows x 6 heads (about 150 MB) does not. Every call
  * on one GPU uses that GPU's array and overwrites it, so calls that overlap on one GPU
  * (several streams, several host threads) race: the caller serialises them. No part of the
  * array needs clearing: each call writes everything it reads. `stream` must belong to the

@@ -98,6 +98,7 @@ def _gated_case(wl, dev, units=None, tag=""):
     (1, 10, 15, 2, 32, 5, 3, "f32"),
     (1, 16, 16, 2, 64, 8, 16, "bf16"),   # d_c = 64: the one-thread-per-query kernel applies the gate
     (1, 48, 48, 2, 32, 48, 16, "bf16"),  # N = 2304: every item in key ranges, the combine applies the gate
+    (1, 32, 48, 2, 32, 16, 16, "bf16"),  # w divides 64: K_c and V read in their maps
 ])
 def test_gated_forward_small(shape):
     dev = device()

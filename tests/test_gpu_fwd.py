@@ -85,6 +85,11 @@ def test_fwd_large_workloads_sampled(name, k, tail):
     (1, 24, 48, 2, 32, 24, 17, "bf16"),
     (1, 40, 40, 1, 32, 40, 32, "bf16"),
     (1, 2, 2, 1, 32, 2, 4, "bf16"),
+    # windows whose side divides 64 with r <= 16: K_c and V read in their maps (no gather)
+    (1, 16, 24, 2, 32, 8, 5, "bf16"),
+    (2, 64, 48, 3, 32, 16, 16, "bf16"),
+    (1, 64, 96, 2, 32, 32, 9, "bf16"),
+    (1, 128, 64, 1, 32, 64, 16, "bf16"),
     # w*w >= 2048: the last partial round of workgroups is cut into key ranges and combined
     (1, 50, 100, 2, 32, 50, 8, "bf16"),    # N = 2500: a 4-key last tile, r padded to 16
     (1, 48, 48, 1, 32, 48, 32, "bf16"),    # N = 2304: whole tiles, two positional K-steps
@@ -253,6 +258,32 @@ def test_fwd_split_tail_at_full_size_launches():
         n = _combine_launches(lambda: rib.window_attn_fwd(q, k, v, qp, kp, w))
         print(f"w = {w}: split combines {n}", flush=True)
         assert n == expect
+
+
+@pytest.mark.parametrize("kind", ["overflow", "underflow"])
+def test_fwd_map_kv_exact_pass(kind):
+    """Windows whose side divides 64 run without a key-norm bound: the fast pass takes exp2 of the
+    unshifted scores and checks its row sums and accumulators afterwards. Overflow: token 0's key
+    and every query carry 60 in channel 0, so scores reach ~750 log2 units and exp2 overflows.
+    Underflow: every query carries -60 and every key +60 there, so every score is below -700 and
+    every P underflows. Either way the workgroups rerun with the exact pass."""
+    dev = device()
+    wl = rib_synth.custom_workload(1, 32, 48, 2, 32, 16, 16, "bf16", seed=30 if kind == "overflow" else 31)
+    x = rib_synth.make_inputs(wl)
+    bf = lambda v: rib_synth.bf16_bits(np.asarray(v, np.float32)).view(np.int16)
+    q = x["q_c"].data.view(np.int16).copy()
+    k = x["k_c"].data.view(np.int16).copy()
+    if kind == "overflow":
+        q[..., 0] = bf(60.0)
+        k[:, ::16, ::16, :, 0] = bf(60.0)
+    else:
+        q[..., 0] = bf(-60.0)
+        k[..., 0] = bf(60.0)
+    x["q_c"] = rib_synth.Tensor("bf16", q.view(x["q_c"].data.dtype))
+    x["k_c"] = rib_synth.Tensor("bf16", k.view(x["k_c"].data.dtype))
+    o, lse, rqp, rkp = _run(wl, x, dev)
+    # scores of hundreds of log2 units: the bf16 query operand's relative rounding shows in the LSE
+    _compare(wl, x, o, lse, rqp, rkp, tag=f"map K/V, {kind}", lse_rel=2 * 2.0 ** -9)
 
 
 def test_fwd_shifted_tier_large_scores():

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <utility>
@@ -105,6 +106,12 @@ struct FwdLayout {
 // (windowed rows in and out).
 bool mfma_path(const Geom& g, rib_dtype_t dt) { return dt == RIB_BF16 && g.d_c == 32; }
 
+// ... and among them, windows whose side divides 64 (a 64-key tile is whole window rows) with
+// one positional K-step: the attention kernel reads K_c and V in their maps, no gather runs.
+bool mapkv_path(const Geom& g, rib_dtype_t dt) {
+  return mfma_path(g, dt) && g.r <= 16 && g.w >= 8 && 64 % g.w == 0;
+}
+
 FwdLayout fwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
   const int es = esize_of(dt);
   const size_t t = (size_t)g.units * g.n_rows * g.d_c * es;
@@ -113,15 +120,16 @@ FwdLayout fwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
   FwdLayout L;
   // the bf16 MFMA kernel reads Q_c and writes O in the map layout directly
   const bool rows_qo = !mfma_path(g, dt);
+  const bool mapkv = mapkv_path(g, dt);
   L.qw = rows_qo ? c.take(t) : nullptr;
-  L.kw = c.take(t);
-  L.vw = c.take(t);
+  L.kw = mapkv ? nullptr : c.take(t);
+  L.vw = mapkv ? nullptr : c.take(t);
   L.ow = rows_qo ? c.take(t) : nullptr;
   // the bf16 kernel reads Q_p, K_p in place when no padding is needed (r = 16 or 32)
   const bool pack = rows_qo || g.r != padded_rank(g.r);
   L.qp = pack ? c.take(pos) : nullptr;
   L.kp = pack ? c.take(pos) : nullptr;
-  L.kmax2 = (float*)c.take(2 * (size_t)g.units * key_bound_parts(g.N) * sizeof(float));
+  L.kmax2 = mapkv ? nullptr : (float*)c.take(2 * (size_t)g.units * key_bound_parts(g.N) * sizeof(float));
   const size_t pieces = rows_qo ? 0 : split_region_pieces(g.units, g.N);
   L.part = pieces ? (float*)c.take(pieces * kSplitPieceFloats * sizeof(float)) : nullptr;
   L.bytes = c.off;
@@ -479,7 +487,8 @@ rib_status_t rib_window_unpartition(const rib_shape_t* shape, rib_dtype_t dtype,
 size_t rib_fwd_workspace_size(const rib_shape_t* shape, rib_dtype_t dtype) {
   if (check_shape(shape, dtype, true) != RIB_OK) return 0;
   Geom g = make_geom(*shape);
-  return fwd_layout(g, dtype, nullptr).bytes;
+  // at least 256 bytes: 0 means an invalid shape (the map-addressed windows need nothing)
+  return std::max<size_t>(fwd_layout(g, dtype, nullptr).bytes, 256);
 }
 
 size_t rib_bwd_workspace_size(const rib_shape_t* shape, rib_dtype_t dtype) {
@@ -514,7 +523,7 @@ static rib_status_t attn_fwd_impl(const rib_shape_t* shape, rib_dtype_t dtype, f
     RIB_TRY(check_fwd_args(shape, dtype, scale, q_c, k_c, v, q_p, k_p, gate, o, lse));
     if (shape->B == 0) return ok();
     Geom g = make_geom(*shape);
-    const size_t need = fwd_layout(g, dtype, nullptr).bytes;
+    const size_t need = std::max<size_t>(fwd_layout(g, dtype, nullptr).bytes, 256);
     if (!workspace || workspace_bytes < need)
       return fail(RIB_ERR_WORKSPACE, "workspace of %zu bytes is smaller than the %zu required", workspace_bytes, need);
     if ((uintptr_t)workspace & 255u) return fail(RIB_ERR_INVALID_ARG, "workspace is not 256-byte aligned");
@@ -524,6 +533,7 @@ static rib_status_t attn_fwd_impl(const rib_shape_t* shape, rib_dtype_t dtype, f
     const int rp = padded_rank(g.r);
     hipError_t e;
     const bool bf = mfma_path(g, dtype);
+    const bool mapkv = mapkv_path(g, dtype);
     const void* kp_rows = L.kp ? L.kp : k_p;
     FwdArgs a;
     a.g = g;
@@ -532,6 +542,8 @@ static rib_status_t attn_fwd_impl(const rib_shape_t* shape, rib_dtype_t dtype, f
     a.qp = L.qp ? L.qp : q_p;
     a.kp = kp_rows;
     a.q_map = q_c; a.o_map = o;
+    a.k_map = mapkv ? k_c : nullptr;
+    a.v_map = mapkv ? v : nullptr;
     a.lse = lse;
     a.kmax2 = L.kmax2;
     a.rp = rp;
@@ -546,7 +558,9 @@ static rib_status_t attn_fwd_impl(const rib_shape_t* shape, rib_dtype_t dtype, f
       if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, k_p, es, L.kp, st)) != hipSuccess)
         return hip_fail(e, "pack k_p");
     }
-    if (bf) {
+    if (mapkv) {
+      // nothing to gather: the attention kernel reads K_c and V in their maps
+    } else if (bf) {
       // K_c rows, V^T kappa and the key-norm partial maxima in one pass
       if ((e = launch_gather_kv_bound(g, rp, k_c, v, kp_rows, L.kw, L.vw, L.kmax2, st)) != hipSuccess)
         return hip_fail(e, "partition k, v");

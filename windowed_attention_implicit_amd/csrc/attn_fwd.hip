@@ -130,14 +130,21 @@ constexpr int kBufs = 4;                  // LDS tile ring depth
 constexpr int kRsrcWord3 = 0x00020000;
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
 
 template <bool V>
 struct BoolTag {
   static constexpr bool value = V;
 };
 
-// GATE: O' = O * G with G read in the map layout by the output stage
-template <int KP, bool RPB = false, bool GATE = false>
+// GATE: O' = O * G with G read in the map layout by the output stage.
+// MAPKV (one positional K-step, windows whose side divides 64: a 64-key tile is 64 / w whole
+// window rows): K_c and V tiles reach LDS by DMA straight from the [B, H, W, heads, 32] maps,
+// both token-major; the PV MFMA's channel-major V^T fragments come from transposing LDS reads
+// (ds_read_b64_tr_b16). No gather runs and no key-norm bound exists: the fast pass takes
+// P = exp2(S') unshifted and the exact pass reruns a workgroup whose row sums or accumulators
+// came out non-finite or below the underflow guard.
+template <int KP, bool RPB = false, bool GATE = false, bool MAPKV = false>
 __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_kernel(FwdArgs a) {
   typedef FwdCfg<KP, RPB> C;
   // Ring of kBufs tile buffers. While tile t is processed, tiles t and t + 1
@@ -191,8 +198,15 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
   const int64_t row_elems = (int64_t)g.W * g.heads * 32, pix_elems = (int64_t)g.heads * 32;
   auto map_row = [&](int t) { return map_base + (int64_t)(t / g.w) * row_elems + (int64_t)(t % g.w) * pix_elems; };
   const bf16* qmap = (const bf16*)a.q_map;
-  const bf16* kw = (const bf16*)a.kw + (int64_t)unit * n_rows * 32;
-  const bf16* vt = (const bf16*)a.vw + (int64_t)unit * 32 * n_rows;
+  static_assert(!MAPKV || (KP == 1 && !RPB), "map-addressed K / V: one positional K-step only");
+  // map-addressed tiles: key k of a tile sits at (k / w) window rows and (k % w) pixels from the
+  // tile's first key, and tile t starts t * (64 / w) window rows below the window's first row
+  const int row_bytes = g.W * g.heads * 64, pix_bytes = g.heads * 64;
+  const int tile_step = MAPKV ? (kKeyTile / g.w) * row_bytes : 0;
+  const bf16* kw = MAPKV ? (const bf16*)a.k_map + map_base : (const bf16*)a.kw + (int64_t)unit * n_rows * 32;
+  const bf16* vt = MAPKV ? (const bf16*)a.v_map + map_base : (const bf16*)a.vw + (int64_t)unit * 32 * n_rows;
+  // bytes from the window's first pixel-head row to the end of its last one
+  const int span_bytes = MAPKV ? (g.w - 1) * row_bytes + (g.w - 1) * pix_bytes + 64 : n_rows * 64;
   const bf16* qp = (const bf16*)a.qp;
   const bf16* kp = (const bf16*)a.kp;
   const float c = a.c;
@@ -200,7 +214,7 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
   // ---- per-unit key-norm bound: max over the partial maxima of the unit
   const int nkparts = (N + kKeyBoundTile - 1) / kKeyBoundTile;
   float km = 0.f, vm = 0.f;
-  for (int i = lane; i < nkparts; i += 64) {
+  for (int i = lane; !MAPKV && i < nkparts; i += 64) {
     km = fmaxf(km, a.kmax2[(int64_t)unit * nkparts + i]);
     vm = fmaxf(vm, a.kmax2[((int64_t)g.units + unit) * nkparts + i]);
   }
@@ -275,10 +289,10 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
   // chunks [64 i, 64 i + 64) of the buffer and is issued by wave i % 4; the
   // per-lane source offsets are fixed, only the key offset moves per tile.
   // Pad chunks fetch a duplicate of their row's first chunk.
-  const __amdgpu_buffer_rsrc_t rs_kc = __builtin_amdgcn_make_buffer_rsrc((void*)kw, 0, n_rows * 64, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_kc = __builtin_amdgcn_make_buffer_rsrc((void*)kw, 0, span_bytes, kRsrcWord3);
   // K_p has N rows (rows past N read zero): either the packed copy or the caller's buffer
   const __amdgpu_buffer_rsrc_t rs_kp = __builtin_amdgcn_make_buffer_rsrc((void*)kp, 0, N * rp * 2, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc((void*)vt, 0, n_rows * 64, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rs_v = __builtin_amdgcn_make_buffer_rsrc((void*)vt, 0, span_bytes, kRsrcWord3);
   const __amdgpu_buffer_rsrc_t rs_i = __builtin_amdgcn_make_buffer_rsrc((void*)a.rpb_kidx, 0, n_rows * 4, kRsrcWord3);
   int dma_off[4];
 #pragma unroll
@@ -288,7 +302,7 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
     int off = 0;
     if (i < C::kKcDma) {
       const int r = c / C::kKcRow, k = c % C::kKcRow;
-      off = r * 64 + (k < 4 ? k : 0) * 16;
+      off = (MAPKV ? (r / g.w) * row_bytes + (r % g.w) * pix_bytes : r * 64) + (k < 4 ? k : 0) * 16;
     } else if (i < C::kKcDma + C::kKpDma) {
       const int c2 = c - C::kKpOff;
       constexpr int kKpRowNz = C::kKpRow ? C::kKpRow : 1;   // no positional part: branch never taken
@@ -296,9 +310,14 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
       off = r * rp * 2 + (k < 2 * KP ? k : 0) * 16;
     } else if (i < C::kKcDma + C::kKpDma + C::kVDma) {
       const int c3 = c - C::kVOff;
-      int r = c3 / C::kVRow, k = c3 % C::kVRow;
-      if (r >= 32) r = 0, k = 0;
-      off = r * n_rows * 2 + (k < 8 ? k : 0) * 16;
+      if constexpr (MAPKV) {   // token-major V rows laid out as the K_c rows: [64 keys][5 chunks]
+        const int r = c3 / C::kKcRow, k = c3 % C::kKcRow;
+        off = (r / g.w) * row_bytes + (r % g.w) * pix_bytes + (k < 4 ? k : 0) * 16;
+      } else {
+        int r = c3 / C::kVRow, k = c3 % C::kVRow;
+        if (r >= 32) r = 0, k = 0;
+        off = r * n_rows * 2 + (k < 8 ? k : 0) * 16;
+      }
     } else {
       off = lane < 16 ? lane * 16 : (int)0x80000000;   // 64 key offsets; the rest of the block reads zeros
     }
@@ -313,11 +332,13 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
       if (i < C::kDma) {
         auto* dst = (__attribute__((address_space(3))) void*)&sT[buf][64 * i];
         if (i < C::kKcDma)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kc, dst, 16, dma_off[jj] + k0 * 64, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kc, dst, 16, dma_off[jj] + (MAPKV ? t * tile_step : k0 * 64), 0,
+                                                   0, 0);
         else if (i < C::kKcDma + C::kKpDma)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_kp, dst, 16, dma_off[jj] + k0 * rp * 2, 0, 0, 0);
         else if (i < C::kKcDma + C::kKpDma + C::kVDma)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, dst, 16, dma_off[jj] + k0 * 2, 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_v, dst, 16, dma_off[jj] + (MAPKV ? t * tile_step : k0 * 2), 0, 0,
+                                                   0);
         else
           __builtin_amdgcn_raw_ptr_buffer_load_lds(rs_i, dst, 16, dma_off[jj] + k0 * 4, 0, 0, 0);
       }
@@ -340,8 +361,31 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
       kf[s] = __builtin_bit_cast(bf16x8, sT[buf][ch]);
     }
   };
-  auto vfrag = [&](int buf, int sub, int s) {
-    return __builtin_bit_cast(bf16x8, sT[buf][C::kVOff + l32 * C::kVRow + 4 * sub + 2 * s + half]);
+  auto vfrag = [&](int buf, int sub, int s) -> bf16x8 {
+    if constexpr (MAPKV) {
+      // Transposing LDS read: in each 16-lane group, lane i gets element i & 3 of the 8 bytes
+      // read by lanes (i >> 2) + 4j, j = 0..3. Lane si of group G reads key 4 half + (si >> 2)
+      // (+ 8 for the second read) at channels 16 (G & 1) + 4 (si & 3) .. + 3, so lane l gets
+      // channel l % 32 of keys 4 half + 0..3 and 8 + 4 half + 0..3: the A operand in the key
+      // order of the P words (bits 2 and 3 of the key swapped).
+      const int si = lane & 15;
+      const int key = sub * 32 + s * 16 + 4 * half + (si >> 2);
+      const int ch = 16 * ((lane >> 4) & 1) + 4 * (si & 3);
+      auto* vb = (__attribute__((address_space(3))) char*)&sT[buf][C::kVOff];
+      const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4v*)(vb + key * (16 * C::kKcRow) + ch * 2));
+      const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+          (__attribute__((address_space(3))) bf16x4v*)(vb + (key + 8) * (16 * C::kKcRow) + ch * 2));
+      bf16x8 out;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        out[j] = lo[j];
+        out[4 + j] = hi[j];
+      }
+      return out;
+    } else {
+      return __builtin_bit_cast(bf16x8, sT[buf][C::kVOff + l32 * C::kVRow + 4 * sub + 2 * s + half]);
+    }
   };
   // RPB: the log2-domain bias of the lane's 16 accumulator rows (keys 8(v/4) + 4h + v%4 of
   // subtile sub) for both column blocks, gathered from the LDS table ...
@@ -547,7 +591,7 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
           pad_sub[nb] = (float)(nkt * kKeyTile - N) * (SH ? (float)f32_to_bf16(__builtin_amdgcn_exp2f(-msub[nb])) : 1.f);
       }
     };
-    if (shift) fast_pass(BoolTag<true>());
+    if (!MAPKV && shift) fast_pass(BoolTag<true>());
     else fast_pass(BoolTag<false>());
   } else {
     f32x16 cinit[2];
@@ -708,6 +752,12 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
     l_run[nb] -= half == 0 ? pad_sub[nb] : 0.f;
     const float l_tot = l_run[nb] + swap_halves(l_run[nb]);
     bad |= !(l_tot >= kUnderflowGuard) || !(l_tot < INFINITY);
+    if constexpr (MAPKV) {   // no bound: an overflow may have reached the accumulators
+      float asum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) asum += fabsf(acc[nb][i]);
+      bad |= !(asum < INFINITY);
+    }
   }
 
   // ===== exact pass (rare fallback): classic online softmax, double-buffered
@@ -1189,7 +1239,13 @@ hipError_t launch_attn_fwd_bf16(const FwdArgs& a, hipStream_t stream) {
   int64_t blocks = (int64_t)a.g.units * nqb;
   if (blocks == 0) return hipSuccess;
   if (a.split_spx) blocks = split_blocks(a);
-  if (a.gate) {
+  if (a.k_map) {
+    if (a.gate)
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<1, false, true, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((attn_fwd_bf16_kernel<1, false, false, true>), dim3((unsigned)blocks), dim3(256), 0, stream,
+                         a);
+  } else if (a.gate) {
     if (a.rp == 16)
       hipLaunchKernelGGL((attn_fwd_bf16_kernel<1, false, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
     else

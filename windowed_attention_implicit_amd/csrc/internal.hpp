@@ -63,6 +63,10 @@ struct FwdArgs {
   float c;              // scale * log2(e)
   const void* qw;       // [units][n_rows][d_c] (simple path)
   const void* q_map;    // bf16 path: Q_c in the [B, H, W, heads, 32] map
+  // bf16, one positional K-step, w dividing 64: K_c and V read in their maps by the attention
+  // kernel (kw, vw and kmax2 unused); nullptr otherwise
+  const void* k_map = nullptr;
+  const void* v_map = nullptr;
   const void* kw;       // [units][n_rows][d_c]
   const void* vw;       // MFMA path: [units][32][n_rows] kappa layout; simple path: [units][n_rows][d_c]
   const void* qp;       // [n_rows][rp]
