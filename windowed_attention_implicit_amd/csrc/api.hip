@@ -174,13 +174,13 @@ rib_status_t check_rpb(const rib_shape_t* s, rib_dtype_t dt) {
 }
 
 struct BwdLayout {
-  void *qw, *kw, *vw, *dow, *qt, *kt, *dot, *qp, *kp, *qpt, *kpt, *dqw, *dkw, *dvw;
+  void *qw, *kw, *vw, *dow, *qp, *kp, *dqw, *dkw, *dvw;
   float *lse2, *dd, *dqp_part, *dkp_part;
   size_t bytes;
 };
 
 BwdLayout bwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
-  // bf: the MFMA kernels, which also need the kappa copies and write the map directly
+  // bf: the MFMA kernels, which write the map directly
   const int es = esize_of(dt);
   const int rp = padded_rank(g.r);
   const size_t t = (size_t)g.units * g.n_rows * g.d_c * es;
@@ -194,13 +194,8 @@ BwdLayout bwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
   L.kw = c.take(t);
   L.vw = c.take(t);
   L.dow = c.take(t);
-  L.qt = bf ? c.take(t) : nullptr;
-  L.kt = bf ? c.take(t) : nullptr;
-  L.dot = bf ? c.take(t) : nullptr;
   L.qp = c.take(pos);
   L.kp = c.take(pos);
-  L.qpt = bf ? c.take(pos) : nullptr;
-  L.kpt = bf ? c.take(pos) : nullptr;
   // the bf16 kernels write dQ_c, dK_c, dV in the map layout directly
   L.dqw = bf ? nullptr : c.take(t);
   L.dkw = bf ? nullptr : c.take(t);
@@ -770,8 +765,8 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
   } while (0)
     TimedGroup t_part(RIB_KERNEL_PARTITION, st);
     if (bf) {
-      // one pass: Q_c, K_c, dO into both windowed layouts, V into rows, -D and -LSE2 per
-      // row, and the positional rows with their kappa transposes
+      // one pass: Q_c, K_c, dO and V into windowed rows, -D and -LSE2 per row, and the
+      // positional rows
       BwdGather ga;
       ga.pm = make_pixel_map(g);
       ga.N = g.N; ga.n_rows = g.n_rows; ga.r = g.r; ga.rp = rp;
@@ -779,10 +774,9 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
       ga.q = (const bf16*)q_c; ga.k = (const bf16*)k_c; ga.v = (const bf16*)v;
       ga.d_o = (const bf16*)d_o; ga.o = (const bf16*)o; ga.lse = lse;
       ga.q_p = (const bf16*)q_p; ga.k_p = (const bf16*)k_p;
-      ga.qw = (bf16*)L.qw; ga.qt = (bf16*)L.qt; ga.kw = (bf16*)L.kw; ga.kt = (bf16*)L.kt;
-      ga.vw = (bf16*)L.vw; ga.dow = (bf16*)L.dow; ga.dot = (bf16*)L.dot;
+      ga.qw = (bf16*)L.qw; ga.kw = (bf16*)L.kw; ga.vw = (bf16*)L.vw; ga.dow = (bf16*)L.dow;
       ga.dd = L.dd; ga.lse2 = L.lse2;
-      ga.qp = (bf16*)L.qp; ga.qpt = (bf16*)L.qpt; ga.kp = (bf16*)L.kp; ga.kpt = (bf16*)L.kpt;
+      ga.qp = (bf16*)L.qp; ga.kp = (bf16*)L.kp;
       RIB_LAUNCH(launch_gather_bwd(ga, g.units, st), "backward gather");
       t_part.end();
     } else {
@@ -803,8 +797,7 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
     a.c = a.scale * kLog2e;
     a.rp = rp;
     a.qw = L.qw; a.kw = L.kw; a.vw = L.vw; a.dow = L.dow;
-    a.qt = L.qt; a.kt = L.kt; a.dot = L.dot;
-    a.qp = L.qp; a.kp = L.kp; a.qpt = L.qpt; a.kpt = L.kpt;
+    a.qp = L.qp; a.kp = L.kp;
     a.lse2 = L.lse2; a.dd = L.dd;
     a.dqw = L.dqw; a.dkw = L.dkw; a.dvw = L.dvw;
     a.dq_map = dq_c; a.dk_map = dk_c; a.dv_map = dv;

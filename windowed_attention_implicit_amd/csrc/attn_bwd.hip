@@ -10,17 +10,20 @@
 //
 // bf16 design: two MFMA kernels, deterministic (no atomics):
 //  * dkv: a workgroup owns 256 keys (4 waves x 64); it streams 64-query tiles
-//    of Q_hat, dO (row-major) and their channel-major kappa-permuted copies
-//    through LDS. S = Q_hat K_hat^T and dP = dO V^T come out with one key per
-//    lane, so P and dS feed dV^T += dO^T P and dK_hat^T += Q_hat^T dS directly
-//    as MFMA B operands.
-//  * dq: a workgroup owns 256 queries; it streams 64-key tiles of K_hat, V and
-//    K_hat^T (kappa) and accumulates dQ_hat^T += K_hat^T dS^T with one query
-//    per lane, like the forward.
+//    of Q_hat and dO (token-major rows) and their -LSE2, -D through LDS.
+//    S = Q_hat K_hat^T and dP = dO V^T come out with one key per lane, so P
+//    and dS feed dV^T += dO^T P and dK_hat^T += Q_hat^T dS directly as MFMA B
+//    operands; the channel-major A operands dO^T, Q_hat^T come from the same
+//    rows by transposing LDS reads (tr_frag).
+//  * dq: a workgroup owns 256 queries; it streams 64-key tiles of K_hat and V
+//    rows and accumulates dQ_hat^T += K_hat^T dS^T with one query per lane,
+//    like the forward (K_hat^T by transposing reads).
 //  * The Q_c, Q_p rows arrive pre-scaled by c = scale * log2(e) and rounded to
 //    bf16 exactly as the forward rounds them (the one-pass backward gather), so
 //    both kernels form the forward's scores and the score MFMA yields log2-domain
-//    logits directly. In dkv (one key per lane, queries along the accumulator
+//    logits directly. dK_hat = scale dS^T Q_hat is formed from the same pre-scaled
+//    rows and multiplied by scale / c (one more bf16 rounding of Q_hat, not
+//    visible in bf16 outputs; sum_j dK_hat[j] = 0 holds for any Q rows). In dkv (one key per lane, queries along the accumulator
 //    rows) -LSE2 / -D enter as the accumulator inputs of the score / dP MFMAs,
 //    so P = exp2(acc) and dS = P * acc: per score one exp2, one multiply and
 //    the bf16 packs. In dq (one query per lane) -LSE2 is a lane constant held
@@ -39,6 +42,7 @@ namespace rib {
 namespace {
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 bf16x4v;
 
 constexpr int kTile = 64;          // streamed tile (queries in dkv, keys in dq)
 constexpr int kPerBlock = 256;     // owned keys (dkv) / queries (dq) per workgroup
@@ -48,37 +52,29 @@ struct BwdCfg {
   static constexpr int kSteps = 2 + KP;           // 16-channel steps of [content | pos]
   static constexpr int kCRow = 5;                 // chunks per content / dO / V row in LDS (4 + 1 pad)
   static constexpr int kPRow = 2 * KP + 1;        // chunks per positional row (2KP + 1 pad)
-  static constexpr int kTRow = kTile / 8 + 1;     // chunks per transposed row (8 + 1 pad)
   static constexpr int kPosRows = 16 * KP;
 };
 
 // LDS tile layouts (parts in DMA order). dkv streams query tiles: Q_hat
-// content and positional rows, dO rows, the channel-major kappa copies of
-// Q_hat (content, positional) and dO, and the tile's -LSE2 and -D.
+// content and positional rows, dO rows, and the tile's -LSE2 and -D.
 template <int KP>
 struct DkvTile {
-  static constexpr TileLayout<8> get() {
-    return {{{kTile, 4, 5}, {kTile, 2 * KP, 2 * KP + 1}, {kTile, 4, 5}, {32, 8, kTile / 8 + 1},
-             {16 * KP, 8, kTile / 8 + 1}, {32, 8, kTile / 8 + 1}, {1, 16, 16}, {1, 16, 16}}};
+  static constexpr TileLayout<5> get() {
+    return {{{kTile, 4, 5}, {kTile, 2 * KP, 2 * KP + 1}, {kTile, 4, 5}, {1, 16, 16}, {1, 16, 16}}};
   }
 };
-// dq streams key tiles: K_hat content and positional rows, V rows and the
-// channel-major kappa copies of K_hat (content, positional).
+// dq streams key tiles: K_hat content and positional rows and V rows.
 template <int KP>
 struct DqTile {
-  static constexpr TileLayout<5> get() {
-    return {{{kTile, 4, 5}, {kTile, 2 * KP, 2 * KP + 1}, {kTile, 4, 5}, {32, 8, kTile / 8 + 1},
-             {16 * KP, 8, kTile / 8 + 1}}};
-  }
+  static constexpr TileLayout<3> get() { return {{{kTile, 4, 5}, {kTile, 2 * KP, 2 * KP + 1}, {kTile, 4, 5}}}; }
 };
-// LDS tile rings. dkv at r <= 16 fits two workgroups per CU by registers (two
-// waves per SIMD), which a 2-deep ring (tile t + 1 in flight) keeps within the
-// 160 KB of LDS; at r <= 32 it has one workgroup per CU and fetches tile t + 3
-// while processing tile t. dq fits two workgroups per CU with a 3-deep ring
-// (tile t + 2 in flight).
+// LDS tile rings. dkv at r <= 16 runs two workgroups per CU with a 2-deep ring (tile t + 1 in
+// flight while tile t is processed, 15 KB per tile): a deeper ring costs it the registers it
+// has left (3 buffers spill 14 VGPRs to scratch). dkv at r <= 32 (one workgroup per CU) and dq
+// (two) fetch tile t + 3 while processing tile t.
 template <int KP>
 constexpr int kBufsDkv = KP == 1 ? 2 : 4;
-constexpr int kBufsDq = 3;
+constexpr int kBufsDq = 4;
 
 // Workgroup barrier without the release fence of __syncthreads, which would
 // wait for every tile DMA in flight. Callers wait for the DMA they depend on
@@ -89,6 +85,30 @@ __device__ __forceinline__ void barrier_dma() { asm volatile("s_barrier" ::: "me
 __device__ __forceinline__ bf16x8 lds_frag(const u32x4* p) { return __builtin_bit_cast(bf16x8, *p); }
 
 __device__ __forceinline__ bf16x8 zero_frag() { return __builtin_bit_cast(bf16x8, u32x4(0u)); }
+
+// Channel-major MFMA operand from token-major rows in LDS (part: the rows' first chunk,
+// row_chunks: the row pitch in 16-byte chunks) by transposing reads (ds_read_b64_tr_b16): in
+// each 16-lane group, lane i gets element i & 3 of the 8 bytes read by lanes (i >> 2) + 4j,
+// j = 0..3. Lane si of the group reads rows row0 + (si >> 2) and row0 + 8 + (si >> 2) at
+// channels ch0 + 4 (si & 3) .. + 3, so lane i gets channel ch0 + i of rows row0 + 0..3 and
+// row0 + 8..11 (the order of the P / dS operands: bits 2 and 3 of the row swapped). row0 and
+// ch0 must be uniform over each 16-lane group.
+__device__ __forceinline__ bf16x8 tr_frag(const u32x4* part, int row_chunks, int row0, int ch0, int lane) {
+  const int si = lane & 15;
+  auto* b = (__attribute__((address_space(3))) char*)part + (ch0 + 4 * (si & 3)) * 2;
+  const int r = row0 + (si >> 2);
+  const bf16x4v lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4v*)(b + r * row_chunks * 16));
+  const bf16x4v hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+      (__attribute__((address_space(3))) bf16x4v*)(b + (r + 8) * row_chunks * 16));
+  bf16x8 out;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    out[j] = lo[j];
+    out[4 + j] = hi[j];
+  }
+  return out;
+}
 
 
 // Loads the lane's 8 channels (16s + 8h ..) of row `row` of a [content 32 | pos rp] token.
@@ -107,9 +127,9 @@ __device__ __forceinline__ bf16x8 token_frag(const bf16* content, const bf16* po
 // j < 8) of the sub-tile. Swapping the odd 16-lane rows of sb[1] with the even rows of
 // sb[0] (v_permlane16_swap) leaves two B operands of 16 columns each: b[0] columns 0-15,
 // b[1] columns 16-31, and in both, k-block l / 16 = 0, 1, 2, 3 holds (s, h) = (1, 0),
-// (0, 0), (1, 1), (0, 1). In the channel-major kappa copy those indices are the 16-byte
-// chunk 2 s + h of the sub-tile, so the A fragment of lane l is chunk pos16_chunk(l) of
-// channel l % 16.
+// (0, 0), (1, 1), (0, 1), i.e. (s, h) = (c / 2, c % 2) with c = pos16_chunk(l): the A
+// fragment of lane l is channel l % 16 of the sub-tile's rows 16 s + 4 h + 0..3 and
+// 16 s + 8 + 4 h + 0..3.
 __device__ __forceinline__ int pos16_chunk(int lane) {
   const int kb = lane >> 4;
   return 2 * (1 - (kb & 1)) + (kb >> 1);
@@ -134,8 +154,7 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
   typedef BwdCfg<KP> C;
   typedef DkvTile<KP> LP;
   constexpr auto L = LP::get();
-  constexpr int oQc = L.offset(0), oQp = L.offset(1), oDo = L.offset(2), oQt = L.offset(3), oQpt = L.offset(4),
-                oDot = L.offset(5), oL = L.offset(6), oD = L.offset(7);
+  constexpr int oQc = L.offset(0), oQp = L.offset(1), oDo = L.offset(2), oL = L.offset(3), oD = L.offset(4);
   constexpr int kBufs = kBufsDkv<KP>, kAhead = kBufs - 1;   // tiles in flight ahead of the current one
   __shared__ u32x4 sT[kBufs][L.chunks()];
 
@@ -154,11 +173,8 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
   const bf16* kw = (const bf16*)a.kw + ub * 32;
   const bf16* vw = (const bf16*)a.vw + ub * 32;
   const bf16* dow = (const bf16*)a.dow + ub * 32;
-  const bf16* qt = (const bf16*)a.qt + ub * 32;
-  const bf16* dot = (const bf16*)a.dot + ub * 32;
   const bf16* qp = (const bf16*)a.qp;
   const bf16* kp = (const bf16*)a.kp;
-  const bf16* qpt = (const bf16*)a.qpt;
   const float* lse2 = a.lse2 + ub;
   const float* dd = a.dd + ub;
 
@@ -190,10 +206,9 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
   }
 
   // query tiles reach LDS by DMA (buffer_load ... lds), three tiles ahead
-  const int row64 = n_rows * 64, nb2 = n_rows * 2, pos_bytes = n_rows * rp * 2;
-  const DmaSrc src[8] = {
+  const int row64 = n_rows * 64, pos_bytes = n_rows * rp * 2;
+  const DmaSrc src[5] = {
       {qw, row64, 64, kTile * 64},        {qp, pos_bytes, rp * 2, kTile * rp * 2}, {dow, row64, 64, kTile * 64},
-      {qt, row64, nb2, kTile * 2},        {qpt, pos_bytes, nb2, kTile * 2},        {dot, row64, nb2, kTile * 2},
       {lse2, n_rows * 4, 256, kTile * 4}, {dd, n_rows * 4, 256, kTile * 4},
   };
   TileDma<L.kParts, L.slots()> dma;
@@ -229,16 +244,20 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
         for (int i = 0; i < 4; ++i) { nl[4 * gq + i] = l4[i]; nd[4 * gq + i] = d4[i]; }
       }
       bf16x8 dta[2], qta[2], qpta[2];
+      const int ch0 = 16 * ((lane >> 4) & 1);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const int ch = 4 * sub + 2 * s + half;
-        dta[s] = lds_frag(&T[oDot + l32 * C::kTRow + ch]);
-        qta[s] = lds_frag(&T[oQt + l32 * C::kTRow + ch]);
-        if constexpr (KP == 2) qpta[s] = lds_frag(&T[oQpt + l32 * C::kTRow + ch]);
+        const int r0 = sub * 32 + s * 16 + 4 * half;
+        dta[s] = tr_frag(&T[oDo], C::kCRow, r0, ch0, lane);
+        qta[s] = tr_frag(&T[oQc], C::kCRow, r0, ch0, lane);
+        if constexpr (KP == 2) qpta[s] = tr_frag(&T[oQp], C::kPRow, r0, ch0, lane);
       }
       // KP = 1: A of the 16x16x32 dK_p MFMA, channel lane % 16, the sub-tile's queries of
       // k-block lane / 16 in the order pos16_b() leaves dS in
-      if constexpr (KP == 1) qpta[0] = lds_frag(&T[oQpt + (lane & 15) * C::kTRow + 4 * sub + pos16_chunk(lane)]);
+      if constexpr (KP == 1) {
+        const int c = pos16_chunk(lane);
+        qpta[0] = tr_frag(&T[oQp], C::kPRow, sub * 32 + 16 * (c >> 1) + 4 * (c & 1), 0, lane);
+      }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         // sc = S' - LSE2 (log2 domain), dp = dP - D
@@ -286,6 +305,7 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
   bf16* dvm = (bf16*)a.dv_map;
   float* dkp = a.dkp_part + ub * rp;
   const float scale = a.scale;
+  const float kscale = a.scale / a.c;   // dK_hat from the pre-scaled Q_hat rows
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int key = k0 + nb * 32 + l32;
@@ -296,7 +316,7 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         v4[i] = f32_to_bf16(acc_dv[nb][4 * gq + i]);
-        k4[i] = f32_to_bf16(acc_dk[nb][4 * gq + i] * scale);
+        k4[i] = f32_to_bf16(acc_dk[nb][4 * gq + i] * kscale);
       }
       const int ch = 8 * gq + 4 * half;
       const int64_t row = map_base + (int64_t)(key / g.w) * row_elems + (int64_t)(key % g.w) * pix_elems;
@@ -305,7 +325,7 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
       if (KP == 2) {
         f32x4 p4;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) p4[i] = acc_dkp[nb][4 * gq + i] * scale;
+        for (int i = 0; i < 4; ++i) p4[i] = acc_dkp[nb][4 * gq + i] * kscale;
         *(f32x4*)(dkp + (int64_t)key * rp + ch) = p4;
       }
     }
@@ -317,7 +337,7 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         const int key = k0 + nb * 32 + 16 * m + (lane & 15);
-        if (key < N) *(f32x4*)(dkp + (int64_t)key * rp + 4 * (lane >> 4)) = acc_dkp16[nb][m] * scale;
+        if (key < N) *(f32x4*)(dkp + (int64_t)key * rp + 4 * (lane >> 4)) = acc_dkp16[nb][m] * kscale;
       }
   }
 }
@@ -328,7 +348,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   typedef BwdCfg<KP> C;
   typedef DqTile<KP> LP;
   constexpr auto L = LP::get();
-  constexpr int oKc = L.offset(0), oKp = L.offset(1), oV = L.offset(2), oKt = L.offset(3), oKpt = L.offset(4);
+  constexpr int oKc = L.offset(0), oKp = L.offset(1), oV = L.offset(2);
   __shared__ u32x4 sT[kBufsDq][L.chunks()];
 
   const Geom& g = a.g;
@@ -346,10 +366,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   const bf16* kw = (const bf16*)a.kw + ub * 32;
   const bf16* vw = (const bf16*)a.vw + ub * 32;
   const bf16* dow = (const bf16*)a.dow + ub * 32;
-  const bf16* kt = (const bf16*)a.kt + ub * 32;
   const bf16* qp = (const bf16*)a.qp;
   const bf16* kp = (const bf16*)a.kp;
-  const bf16* kpt = (const bf16*)a.kpt;
 
   // owned queries: B operands of S^T = K_hat Q_hat^T and dP^T = V dO^T
   const int q0 = qb * kPerBlock + wave * 64;
@@ -394,23 +412,23 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     acc_dqp16[nb][0] = acc_dqp16[nb][1] = f32x4(0.f);
   }
 
-  // key tiles reach LDS by DMA (buffer_load ... lds), two tiles ahead
-  const int row64 = n_rows * 64, nb2 = n_rows * 2, pos_bytes = n_rows * rp * 2;
-  const DmaSrc src[5] = {
+  // key tiles reach LDS by DMA (buffer_load ... lds), three tiles ahead
+  const int row64 = n_rows * 64, pos_bytes = n_rows * rp * 2;
+  const DmaSrc src[3] = {
       {kw, row64, 64, kTile * 64}, {kp, pos_bytes, rp * 2, kTile * rp * 2}, {vw, row64, 64, kTile * 64},
-      {kt, row64, nb2, kTile * 2}, {kpt, pos_bytes, nb2, kTile * 2},
   };
   TileDma<L.kParts, L.slots()> dma;
   tile_dma_init<LP>(dma, src, wave, lane);
 
   const int nkt = (N + kTile - 1) / kTile;
-  tile_dma_issue<LP>(dma, wave, 0, sT[0]);
-  tile_dma_issue<LP>(dma, wave, min(1, nkt - 1), sT[1]);
-  tile_dma_wait<LP, 1>(wave);
+  constexpr int kAhead = kBufsDq - 1;
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) tile_dma_issue<LP>(dma, wave, min(i, nkt - 1), sT[i]);
+  tile_dma_wait<LP, kAhead - 1>(wave);
   __syncthreads();
   for (int t = 0; t < nkt; ++t) {
-    // tile t + 2 (the last tile again past the end) into the buffer tile t - 1 used
-    tile_dma_issue<LP>(dma, wave, min(t + 2, nkt - 1), sT[(t + 2) % kBufsDq]);
+    // tile t + kAhead (the last tile again past the end) into the buffer tile t - 1 used
+    tile_dma_issue<LP>(dma, wave, min(t + kAhead, nkt - 1), sT[(t + kAhead) % kBufsDq]);
     const u32x4* T = sT[t % kBufsDq];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
@@ -420,14 +438,18 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
       for (int s = 0; s < C::kSteps; ++s)
         ka[s] = s < 2 ? lds_frag(&T[oKc + row * C::kCRow + 2 * s + half])
                       : lds_frag(&T[oKp + row * C::kPRow + 2 * (s - 2) + half]);
+      const int ch0 = 16 * ((lane >> 4) & 1);
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         va[s] = lds_frag(&T[oV + row * C::kCRow + 2 * s + half]);
-        const int ch = 4 * sub + 2 * s + half;
-        kta[s] = lds_frag(&T[oKt + l32 * C::kTRow + ch]);
-        if constexpr (KP == 2) kpta[s] = lds_frag(&T[oKpt + l32 * C::kTRow + ch]);
+        const int r0 = sub * 32 + s * 16 + 4 * half;
+        kta[s] = tr_frag(&T[oKc], C::kCRow, r0, ch0, lane);
+        if constexpr (KP == 2) kpta[s] = tr_frag(&T[oKp], C::kPRow, r0, ch0, lane);
       }
-      if constexpr (KP == 1) kpta[0] = lds_frag(&T[oKpt + (lane & 15) * C::kTRow + 4 * sub + pos16_chunk(lane)]);
+      if constexpr (KP == 1) {
+        const int c = pos16_chunk(lane);
+        kpta[0] = tr_frag(&T[oKp], C::kPRow, sub * 32 + 16 * (c >> 1) + 4 * (c & 1), 0, lane);
+      }
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         // one query per lane: -LSE2 enters as the score MFMA's accumulator input (a lane
@@ -462,7 +484,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
         }
       }
     }
-    tile_dma_wait<LP, 1>(wave);   // tile t + 1 landed (this wave's part); t + 2 may be in flight
+    tile_dma_wait<LP, kAhead - 1>(wave);   // tile t + 1 landed (this wave's part); later ones may be in flight
     barrier_dma();
   }
 

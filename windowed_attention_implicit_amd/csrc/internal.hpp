@@ -32,9 +32,8 @@ hipError_t launch_partition(const Geom& g, int esize, const void* x, void* xw, h
 hipError_t launch_gather_kv_bound(const Geom& g, int rp, const void* k, const void* v, const void* kp, void* kw,
                                   void* vt, float* kmax2, hipStream_t stream);
 // bf16, d_c = 32 backward preparation in one pass (gather_bwd_kernel): maps
-// [B, H, W, heads, 32] -> rows [units][n_rows][32] and kappa [units][32][n_rows];
-// lse [B, H, W, heads] -> -LSE2, and -D from dO and O, per row [units][n_rows];
-// Q_p, K_p [N][r] -> rows [n_rows][rp] and kappa [rp][n_rows].
+// [B, H, W, heads, 32] -> rows [units][n_rows][32]; lse [B, H, W, heads] -> -LSE2, and
+// -D from dO and O, per row [units][n_rows]; Q_p, K_p [N][r] -> rows [n_rows][rp].
 struct BwdGather {
   PixelMap pm;
   int N, n_rows, r, rp;
@@ -42,9 +41,9 @@ struct BwdGather {
   const bf16 *q, *k, *v, *d_o, *o;
   const float* lse;
   const bf16 *q_p, *k_p;
-  bf16 *qw, *qt, *kw, *kt, *vw, *dow, *dot;
+  bf16 *qw, *kw, *vw, *dow;
   float *dd, *lse2;
-  bf16 *qp, *qpt, *kp, *kpt;
+  bf16 *qp, *kp;
 };
 hipError_t launch_gather_bwd(const BwdGather& a, int units, hipStream_t stream);
 // windowed rows -> x [B,H,W,heads,d].
@@ -141,13 +140,8 @@ struct BwdArgs {
   const void* kw;       // [units][n_rows][d_c] rows
   const void* vw;       // [units][n_rows][d_c] rows
   const void* dow;      // [units][n_rows][d_c] rows
-  const void* qt;       // [units][32][n_rows] kappa (bf16 only)
-  const void* kt;       // [units][32][n_rows] kappa (bf16 only)
-  const void* dot;      // [units][32][n_rows] kappa (bf16 only)
   const void* qp;       // [n_rows][rp]
   const void* kp;       // [n_rows][rp]
-  const void* qpt;      // [rp][n_rows] kappa (bf16 only)
-  const void* kpt;      // [rp][n_rows] kappa (bf16 only)
   const float* lse2;    // [units][n_rows]  log2-domain LSE (negated on the bf16 path)
   const float* dd;      // [units][n_rows]  D_i = sum_c dO_ic O_ic (negated on the bf16 path)
   // outputs: windowed (simple path) or in the [B, H, W, heads, 32] map (bf16 MFMA path)

@@ -167,16 +167,14 @@ __global__ __launch_bounds__(256) void gather_kv_bound_kernel(PixelMap pm, int N
 }
 
 // The bf16 backward's whole preparation in one pass. Block (unit, 64-token group):
-// Q_c, K_c and dO -> the rows layout and the channel-major kappa layout, V -> rows (the Q_c
-// and Q_p rows, which only enter the score MFMAs, pre-scaled to bf16(c q) with c =
-// scale log2(e) exactly as the forward rounds them, so both backward kernels form the
-// forward's scores; the kappa copies, which enter dK_hat = dS^T Q_hat, stay unscaled),
-// and per row the negated softmax statistics the MFMA kernels add: -D with
-// D = sum_c dO O, and -LSE2 = -LSE log2(e) (rows >= N: 0 and -inf, so P = 0). D comes
-// from the dO registers the gather already holds. Blocks of unit 0 also pack Q_p and
-// K_p for their 64 tokens (rows zero-padded to rp channels and their kappa transposes).
+// Q_c, K_c, dO and V -> the token-major rows layout (the Q_c and Q_p rows pre-scaled to
+// bf16(c q) with c = scale log2(e) exactly as the forward rounds them, so both backward
+// kernels form the forward's scores), and per row the negated softmax statistics the MFMA
+// kernels add: -D with D = sum_c dO O, and -LSE2 = -LSE log2(e) (rows >= N: 0 and -inf,
+// so P = 0). D comes from the dO registers the gather already holds. Blocks of unit 0 also
+// pack Q_p and K_p for their 64 tokens (rows zero-padded to rp channels). The kernels take
+// their channel-major operands from these rows by transposing LDS reads.
 __global__ __launch_bounds__(256) void gather_bwd_kernel(BwdGather a) {
-  __shared__ bf16 tile[3][64][32 + 2];
   const int groups = a.n_rows / 64;
   int u, gi;
   block_unit_group(groups, u, gi);
@@ -208,12 +206,6 @@ __global__ __launch_bounds__(256) void gather_bwd_kernel(BwdGather a) {
     *(u32x4*)(a.kw + row) = x[1];
     *(u32x4*)(a.dow + row) = x[2];
     *(u32x4*)(a.vw + row) = x[3];
-#pragma unroll
-    for (int m = 0; m < 3; ++m) {
-      const bf16* pv = (const bf16*)&x[m];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) tile[m][tok][c * 8 + j] = pv[j];
-    }
     const bf16x8 de = __builtin_bit_cast(bf16x8, x[2]), oe = __builtin_bit_cast(bf16x8, ov);
     float dsum = 0.f;
 #pragma unroll
@@ -226,31 +218,15 @@ __global__ __launch_bounds__(256) void gather_bwd_kernel(BwdGather a) {
       a.lse2[i] = t < N ? -(a.lse[ph] * 1.44269504088896340736f) : -INFINITY;
     }
   }
-  if (u == 0) {   // positional tokens of this group: rows and kappa transposes
+  if (u == 0) {   // positional tokens of this group: rows
     for (int i = tid; i < 64 * a.rp; i += 256) {
       const int tl = i / a.rp, j = i - tl * a.rp, t = g0 + tl;
-      const int64_t kpos = (int64_t)j * n_rows + ((t & ~15) | kappa16(t & 15));
       const bool ok = t < N && j < a.r;
       const bf16 qv = ok ? a.q_p[(int64_t)t * a.r + j] : (bf16)0.f;
       const bf16 kv = ok ? a.k_p[(int64_t)t * a.r + j] : (bf16)0.f;
       a.qp[(int64_t)t * a.rp + j] = f32_to_bf16((float)qv * a.c);   // pre-scaled, as Q_c
       a.kp[(int64_t)t * a.rp + j] = kv;
-      a.qpt[kpos] = qv;
-      a.kpt[kpos] = kv;
     }
-  }
-  __syncthreads();
-  const int d = tid >> 3, pc = tid & 7;
-  bf16* outs[3] = {a.qt, a.kt, a.dot};
-#pragma unroll
-  for (int m = 0; m < 3; ++m) {
-    bf16 vals[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int p = pc * 8 + j;
-      vals[j] = tile[m][(p & ~15) | kappa16(p & 15)][d];
-    }
-    *(u32x4*)(outs[m] + ((int64_t)u * 32 + d) * n_rows + g0 + pc * 8) = *(const u32x4*)vals;
   }
 }
 
