@@ -244,8 +244,12 @@ def test_workspace_is_linear_not_quadratic(L):
     # 256 queries x (32 + 2) floats, independent of the map and the window
     # windows whose side divides 64 read K_c and V in their maps: almost no forward workspace
     assert ws(2, 192, 16) <= 1 << 20 and ws(2, 192, 32) <= 1 << 20
+    # ... and the backward's gather writes no K_c, V rows for them: two windowed copies fewer
+    bw = L.rib_bwd_workspace_size
+    copy = 2 * 192 * 192 * 6 * 32 * 2
+    assert ws(2, 192, 16, bw) <= ws(2, 192, 24, bw) - 2 * copy + (1 << 20)
     for fn, split_cap, w_small in ((L.rib_fwd_workspace_size, 1024 * 256 * 34 * 4, 24),
-                                   (L.rib_bwd_workspace_size, 0, 16)):
+                                   (L.rib_bwd_workspace_size, 0, 24)):
         small, big = ws(2, 192, w_small, fn), ws(2, 192, 96, fn)
         # same map, 36x larger windows: only the per-window-size parts (positional tokens, their
         # transposes and per-unit partials, a few MB at w = 96) differ

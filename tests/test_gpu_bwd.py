@@ -55,6 +55,11 @@ def _compare(wl, x, grads, rqp, rkp, units=None, tag="", pos=True):
     (2, 14, 14, 1, 32, 7, 1, "bf16"),
     (1, 24, 48, 2, 32, 24, 17, "bf16"),
     (1, 40, 40, 1, 32, 40, 32, "bf16"),
+    # windows whose side divides 64 at r <= 16: K_c and V read in their maps (several windows
+    # per map row, several heads, H != W)
+    (2, 16, 48, 3, 32, 8, 5, "bf16"),
+    (1, 32, 96, 2, 32, 16, 12, "bf16"),
+    (1, 64, 128, 2, 32, 32, 9, "bf16"),
     # windows of more than 2048 tokens
     (1, 50, 100, 2, 32, 50, 8, "bf16"),     # N = 2500: a 4-row last tile, r padded to 16
     (1, 48, 48, 3, 32, 48, 16, "bf16"),     # N = 2304: whole tiles

@@ -107,9 +107,11 @@ struct FwdLayout {
 bool mfma_path(const Geom& g, rib_dtype_t dt) { return dt == RIB_BF16 && g.d_c == 32; }
 
 // ... and among them, windows whose side divides 64 (a 64-key tile is whole window rows) with
-// one positional K-step: the attention kernel reads K_c and V in their maps, no gather runs.
+// one positional K-step: the attention kernels read K_c and V (backward: and dO) in their maps,
+// through buffer resources spanning one window (w map rows must fit a 31-bit byte range).
 bool mapkv_path(const Geom& g, rib_dtype_t dt) {
-  return mfma_path(g, dt) && g.r <= 16 && g.w >= 8 && 64 % g.w == 0;
+  return mfma_path(g, dt) && g.r <= 16 && g.w >= 8 && 64 % g.w == 0 &&
+         (int64_t)g.w * g.W * g.heads * 64 < ((int64_t)1 << 31);
 }
 
 FwdLayout fwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
@@ -188,11 +190,12 @@ BwdLayout bwd_layout(const Geom& g, rib_dtype_t dt, void* ws) {
   const size_t rowf = (size_t)g.units * g.n_rows * sizeof(float);
   const size_t part = (size_t)g.units * g.n_rows * rp * sizeof(float);
   const bool bf = mfma_path(g, dt);
+  const bool mapkv = mapkv_path(g, dt);   // K_c, V read in their maps
   Carve c(ws);
   BwdLayout L;
   L.qw = c.take(t);
-  L.kw = c.take(t);
-  L.vw = c.take(t);
+  L.kw = mapkv ? nullptr : c.take(t);
+  L.vw = mapkv ? nullptr : c.take(t);
   L.dow = c.take(t);
   L.qp = c.take(pos);
   L.kp = c.take(pos);
@@ -765,8 +768,8 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
   } while (0)
     TimedGroup t_part(RIB_KERNEL_PARTITION, st);
     if (bf) {
-      // one pass: Q_c, K_c, dO and V into windowed rows, -D and -LSE2 per row, and the
-      // positional rows
+      // one pass: Q_c (pre-scaled), K_c, dO and V into windowed rows (map-addressed windows:
+      // Q_c and dO only), -D and -LSE2 per row, and the positional rows
       BwdGather ga;
       ga.pm = make_pixel_map(g);
       ga.N = g.N; ga.n_rows = g.n_rows; ga.r = g.r; ga.rp = rp;
@@ -801,6 +804,7 @@ rib_status_t rib_window_attn_bwd(const rib_shape_t* shape, rib_dtype_t dtype, fl
     a.lse2 = L.lse2; a.dd = L.dd;
     a.dqw = L.dqw; a.dkw = L.dkw; a.dvw = L.dvw;
     a.dq_map = dq_c; a.dk_map = dk_c; a.dv_map = dv;
+    if (mapkv_path(g, dtype)) { a.k_map = k_c; a.v_map = v; }
     a.dqp_part = L.dqp_part; a.dkp_part = L.dkp_part;
     {
       TimedGroup t_dkv(RIB_KERNEL_ATTN_BWD_DKV, st);

@@ -35,6 +35,12 @@
 //    otherwise pick costs a register copy per score.
 //  * Positional-gradient partials are written per unit in float32 and summed
 //    over units in a fixed order by a separate reduction.
+//  * MAPKV (one positional K-step, windows whose side w divides 64): a 64-key
+//    tile is 64 / w whole window rows, so K_c and V tiles (and the owned keys'
+//    K_c, V) are read in their [B, H, W, heads, 32] maps, each token's 64 bytes
+//    at its pixel; the gather then writes only the pre-scaled Q rows, the dO rows
+//    and the row statistics. (dkv keeps reading dO tiles from windowed rows:
+//    map-addressed offsets for them would cost it the last registers it has.)
 #include "internal.hpp"
 #include "tile_dma.hpp"
 
@@ -111,15 +117,45 @@ __device__ __forceinline__ bf16x8 tr_frag(const u32x4* part, int row_chunks, int
 }
 
 
-// Loads the lane's 8 channels (16s + 8h ..) of row `row` of a [content 32 | pos rp] token.
-template <int KP>
-__device__ __forceinline__ bf16x8 token_frag(const bf16* content, const bf16* pos, int64_t row, int s, int half) {
-  constexpr int rp = 16 * KP;
+// Loads the lane's 8 channels (16s + 8h ..) of a [content 32 | pos rp] token whose content and
+// positional rows start at `content` and `pos`.
+__device__ __forceinline__ bf16x8 token_frag(const bf16* content, const bf16* pos, int s, int half) {
   u32x4 v;
-  if (s < 2) v = *(const u32x4*)(content + row * 32 + s * 16 + half * 8);
-  else v = *(const u32x4*)(pos + row * rp + (s - 2) * 16 + half * 8);
+  if (s < 2) v = *(const u32x4*)(content + s * 16 + half * 8);
+  else v = *(const u32x4*)(pos + (s - 2) * 16 + half * 8);
   return __builtin_bit_cast(bf16x8, v);
 }
+
+// Where the token rows of a unit live: its windowed rows (32 elements each) or, for MAPKV,
+// its window in a [B, H, W, heads, 32] map: token t at base + (t / w) W heads 32 +
+// (t % w) heads 32 elements (w a power of two, lw = log2 w). dma() describes 64-token tiles
+// of such rows for tile_dma.
+template <bool MAPKV>
+struct TokenRows {
+  const bf16* base;
+  int lw, row_bytes, pix_bytes, span_bytes;
+  __device__ TokenRows(const void* map, const void* rows, const Geom& g, int unit) {
+    if constexpr (MAPKV) {
+      base = (const bf16*)map + make_pixel_map(g).pixel_head(unit, 0) * 32;
+      lw = __builtin_ctz(g.w);
+      row_bytes = g.W * g.heads * 64;
+      pix_bytes = g.heads * 64;
+      span_bytes = (g.w - 1) * row_bytes + (g.w - 1) * pix_bytes + 64;
+    } else {
+      base = (const bf16*)rows + (int64_t)unit * g.n_rows * 32;
+      lw = row_bytes = pix_bytes = 0;
+      span_bytes = g.n_rows * 64;
+    }
+  }
+  __device__ const bf16* row(int t) const {
+    if constexpr (MAPKV) return base + (int64_t)(t >> lw) * (row_bytes / 2) + (int64_t)(t & ((1 << lw) - 1)) * (pix_bytes / 2);
+    else return base + (int64_t)t * 32;
+  }
+  __device__ DmaSrc dma() const {
+    if constexpr (MAPKV) return {base, span_bytes, row_bytes, (kTile >> lw) * row_bytes, lw, pix_bytes};
+    else return {base, span_bytes, 64, kTile * 64};
+  }
+};
 
 // Positional gradients at r = 16 on v_mfma_f32_16x16x32_bf16. A 32-key (dkv) or
 // 32-query (dq) column block's dS leaves the score layout as sb[2]: lane l holds, for
@@ -149,8 +185,9 @@ __device__ __forceinline__ void pos16_b(const bf16x8 (&sb)[2], bf16x8 (&b)[2]) {
 }
 
 // ------------------------------------------------------------------ dK, dV
-template <int KP>
+template <int KP, bool MAPKV = false>
 __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdArgs a) {
+  static_assert(!MAPKV || KP == 1, "map-addressed K / V: one positional K-step only");
   typedef BwdCfg<KP> C;
   typedef DkvTile<KP> LP;
   constexpr auto L = LP::get();
@@ -170,9 +207,8 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
 
   const int64_t ub = (int64_t)unit * n_rows;
   const bf16* qw = (const bf16*)a.qw + ub * 32;
-  const bf16* kw = (const bf16*)a.kw + ub * 32;
-  const bf16* vw = (const bf16*)a.vw + ub * 32;
-  const bf16* dow = (const bf16*)a.dow + ub * 32;
+  const TokenRows<MAPKV> kr(a.k_map, a.kw, g, unit), vr(a.v_map, a.vw, g, unit);
+  const TokenRows<false> dr(nullptr, a.dow, g, unit);
   const bf16* qp = (const bf16*)a.qp;
   const bf16* kp = (const bf16*)a.kp;
   const float* lse2 = a.lse2 + ub;
@@ -185,13 +221,14 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
   for (int nb = 0; nb < 2; ++nb) {
     const int key = k0 + nb * 32 + l32;
     const bool ok = key < N;
+    const bf16* krow = kr.row(ok ? key : 0);
+    const bf16* vrow = vr.row(ok ? key : 0);
 #pragma unroll
     for (int s = 0; s < C::kSteps; ++s)
-      kf[nb][s] = ok ? token_frag<KP>(kw, kp, key, s, half) : zero_frag();
+      kf[nb][s] = ok ? token_frag(krow, kp + (int64_t)key * rp, s, half) : zero_frag();
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-      vf[nb][s] = ok ? __builtin_bit_cast(bf16x8, *(const u32x4*)(vw + (int64_t)key * 32 + s * 16 + half * 8))
-                     : zero_frag();
+      vf[nb][s] = ok ? __builtin_bit_cast(bf16x8, *(const u32x4*)(vrow + s * 16 + half * 8)) : zero_frag();
   }
 
   // acc_dkp: KP = 2, dK_p^T on 32x32 tiles; KP = 1, its 16 channels on two 16x16 tiles per
@@ -208,7 +245,7 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
   // query tiles reach LDS by DMA (buffer_load ... lds), three tiles ahead
   const int row64 = n_rows * 64, pos_bytes = n_rows * rp * 2;
   const DmaSrc src[5] = {
-      {qw, row64, 64, kTile * 64},        {qp, pos_bytes, rp * 2, kTile * rp * 2}, {dow, row64, 64, kTile * 64},
+      {qw, row64, 64, kTile * 64},        {qp, pos_bytes, rp * 2, kTile * rp * 2}, dr.dma(),
       {lse2, n_rows * 4, 256, kTile * 4}, {dd, n_rows * 4, 256, kTile * 4},
   };
   TileDma<L.kParts, L.slots()> dma;
@@ -343,8 +380,9 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
 }
 
 // ------------------------------------------------------------------ dQ
-template <int KP>
+template <int KP, bool MAPKV = false>
 __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
+  static_assert(!MAPKV || KP == 1, "map-addressed K / V: one positional K-step only");
   typedef BwdCfg<KP> C;
   typedef DqTile<KP> LP;
   constexpr auto L = LP::get();
@@ -363,9 +401,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 
   const int64_t ub = (int64_t)unit * n_rows;
   const bf16* qw = (const bf16*)a.qw + ub * 32;
-  const bf16* kw = (const bf16*)a.kw + ub * 32;
-  const bf16* vw = (const bf16*)a.vw + ub * 32;
-  const bf16* dow = (const bf16*)a.dow + ub * 32;
+  const TokenRows<MAPKV> kr(a.k_map, a.kw, g, unit), vr(a.v_map, a.vw, g, unit);
+  const TokenRows<false> dr(nullptr, a.dow, g, unit);
   const bf16* qp = (const bf16*)a.qp;
   const bf16* kp = (const bf16*)a.kp;
 
@@ -387,12 +424,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     const int q = q0 + nb * 32 + l32;
     const bool ok = q < N;
 #pragma unroll
-    for (int s = 0; s < C::kSteps; ++s)
-      qf[nb][s] = ok ? token_frag<KP>(qw, qp, q, s, half) : zero_frag();   // rows stored pre-scaled
+    for (int s = 0; s < C::kSteps; ++s)   // rows stored pre-scaled
+      qf[nb][s] = ok ? token_frag(qw + (int64_t)q * 32, qp + (int64_t)q * rp, s, half) : zero_frag();
+    const bf16* drow = dr.row(ok ? q : 0);
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-      df[nb][s] = ok ? __builtin_bit_cast(bf16x8, *(const u32x4*)(dow + (int64_t)q * 32 + s * 16 + half * 8))
-                     : zero_frag();
+      df[nb][s] = ok ? __builtin_bit_cast(bf16x8, *(const u32x4*)(drow + s * 16 + half * 8)) : zero_frag();
     nlq[nb] = ok ? a.lse2[ub + q] : -INFINITY;   // stored negated: -LSE2, -D
     const float nd = ok ? a.dd[ub + q] : 0.f;
     ndq[nb] = nd;
@@ -413,10 +450,8 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   }
 
   // key tiles reach LDS by DMA (buffer_load ... lds), three tiles ahead
-  const int row64 = n_rows * 64, pos_bytes = n_rows * rp * 2;
-  const DmaSrc src[3] = {
-      {kw, row64, 64, kTile * 64}, {kp, pos_bytes, rp * 2, kTile * rp * 2}, {vw, row64, 64, kTile * 64},
-  };
+  const int pos_bytes = n_rows * rp * 2;
+  const DmaSrc src[3] = {kr.dma(), {kp, pos_bytes, rp * 2, kTile * rp * 2}, vr.dma()};
   TileDma<L.kParts, L.slots()> dma;
   tile_dma_init<LP>(dma, src, wave, lane);
 
@@ -799,7 +834,8 @@ hipError_t launch_bwd_prep(const Geom& g, int esize, const void* o, const void* 
 hipError_t launch_attn_bwd_dkv_bf16(const BwdArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.g.units * ((a.g.N + kPerBlock - 1) / kPerBlock);
   if (blocks == 0) return hipSuccess;
-  if (a.rp == 16) hipLaunchKernelGGL(attn_bwd_dkv_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  if (a.rp == 16 && a.k_map) hipLaunchKernelGGL((attn_bwd_dkv_kernel<1, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else if (a.rp == 16) hipLaunchKernelGGL(attn_bwd_dkv_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   else hipLaunchKernelGGL(attn_bwd_dkv_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
@@ -807,7 +843,8 @@ hipError_t launch_attn_bwd_dkv_bf16(const BwdArgs& a, hipStream_t stream) {
 hipError_t launch_attn_bwd_dq_bf16(const BwdArgs& a, hipStream_t stream) {
   const int64_t blocks = (int64_t)a.g.units * ((a.g.N + kPerBlock - 1) / kPerBlock);
   if (blocks == 0) return hipSuccess;
-  if (a.rp == 16) hipLaunchKernelGGL(attn_bwd_dq_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  if (a.rp == 16 && a.k_map) hipLaunchKernelGGL((attn_bwd_dq_kernel<1, true>), dim3((unsigned)blocks), dim3(256), 0, stream, a);
+  else if (a.rp == 16) hipLaunchKernelGGL(attn_bwd_dq_kernel<1>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   else hipLaunchKernelGGL(attn_bwd_dq_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }

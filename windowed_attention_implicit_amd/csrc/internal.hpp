@@ -41,7 +41,7 @@ struct BwdGather {
   const bf16 *q, *k, *v, *d_o, *o;
   const float* lse;
   const bf16 *q_p, *k_p;
-  bf16 *qw, *kw, *vw, *dow;
+  bf16 *qw, *kw, *vw, *dow;   // kw, vw nullptr: not written (the kernels read the maps)
   float *dd, *lse2;
   bf16 *qp, *kp;
 };
@@ -151,6 +151,10 @@ struct BwdArgs {
   void* dq_map;
   void* dk_map;
   void* dv_map;
+  // bf16, one positional K-step, w dividing 64: K_c and V read in their maps by the kernels
+  // (kw, vw unused); nullptr otherwise
+  const void* k_map = nullptr;
+  const void* v_map = nullptr;
   float* dqp_part;      // [units][n_rows][rp]
   float* dkp_part;      // [units][n_rows][rp]
 };

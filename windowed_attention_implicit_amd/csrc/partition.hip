@@ -189,10 +189,12 @@ __global__ __launch_bounds__(256) void gather_bwd_kernel(BwdGather a) {
     if (t < N) {
       const int64_t off = ph * 32 + c * 8;
       x[0] = *(const u32x4*)(a.q + off);
-      x[1] = *(const u32x4*)(a.k + off);
       x[2] = *(const u32x4*)(a.d_o + off);
-      x[3] = *(const u32x4*)(a.v + off);
       ov = *(const u32x4*)(a.o + off);
+      if (a.kw) {
+        x[1] = *(const u32x4*)(a.k + off);
+        x[3] = *(const u32x4*)(a.v + off);
+      }
     }
     const int64_t row = ((int64_t)u * n_rows + t) * 32 + c * 8;
     {
@@ -203,9 +205,11 @@ __global__ __launch_bounds__(256) void gather_bwd_kernel(BwdGather a) {
       for (int j = 0; j < 8; ++j) qs[j] = f32_to_bf16((float)qe[j] * a.c);
       *(bf16x8*)(a.qw + row) = qs;
     }
-    *(u32x4*)(a.kw + row) = x[1];
     *(u32x4*)(a.dow + row) = x[2];
-    *(u32x4*)(a.vw + row) = x[3];
+    if (a.kw) {   // windows the kernels cannot read in the maps
+      *(u32x4*)(a.kw + row) = x[1];
+      *(u32x4*)(a.vw + row) = x[3];
+    }
     const bf16x8 de = __builtin_bit_cast(bf16x8, x[2]), oe = __builtin_bit_cast(bf16x8, ov);
     float dsum = 0.f;
 #pragma unroll

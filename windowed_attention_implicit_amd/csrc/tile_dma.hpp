@@ -60,10 +60,14 @@ struct TileDma {
   unsigned off[SLOTS];
 };
 
-// base, addressable bytes, row stride and per-tile step in bytes of one part
+// base, addressable bytes, row stride and per-tile step in bytes of one part. With map_w > 0
+// the rows are the tokens of a w x w window in a [B, H, W, heads, d] map, w = 2^map_w: row r
+// sits r / w map rows (row_bytes each) and r % w pixels (pix_bytes each) below the base, which
+// holds per tile when w divides the tile's 64 rows.
 struct DmaSrc {
   const void* base;
   int num_bytes, row_bytes, tile_step;
+  int map_w = 0, pix_bytes = 0;
 };
 
 template <class LP, int W>
@@ -78,7 +82,10 @@ __device__ __forceinline__ void tile_dma_init_w(TileDma<LP::get().kParts, LP::ge
       const int k = L.part_of(i);
       const int c = (i - L.first(k)) * 64 + lane;
       const int r = c / L.p[k].lds_row, ch = c - r * L.p[k].lds_row;
-      o = r < L.p[k].rows ? (unsigned)(r * src[k].row_bytes + (ch < L.p[k].chunks ? ch : 0) * 16) : 0x80000000u;
+      const int ro = src[k].map_w > 0 ? (r >> src[k].map_w) * src[k].row_bytes +
+                                            (r & ((1 << src[k].map_w) - 1)) * src[k].pix_bytes
+                                      : r * src[k].row_bytes;
+      o = r < L.p[k].rows ? (unsigned)(ro + (ch < L.p[k].chunks ? ch : 0) * 16) : 0x80000000u;
     }
     d.off[j] = o;
   }
