@@ -27,6 +27,9 @@ def _weights(C, seed, dev):
     (1, 5, 3, 1, "bf16"),     # C = 32, a map smaller than one tile
     (1, 64, 64, 8, "bf16"),   # C = 256, the largest supported
     (1, 9, 33, 3, "bf16"),    # C = 96
+    (1, 1, 70, 4, "bf16"),    # C = 128, one row: both halo rows outside the map
+    (3, 2, 31, 5, "bf16"),    # C = 160, two rows, W below one segment
+    (1, 3, 1, 7, "bf16"),     # C = 224, a one-pixel-wide map
     (1, 12, 40, 2, "f32"),
     (2, 7, 7, 6, "f32"),
 ])

@@ -4,25 +4,25 @@
 // conv, point-wise conv and sigmoid; the German summary §2.B: O' = O (.) G; the Chinese summary
 // §2.B: 3x3 depth-wise and 1x1 point-wise).
 //
-// bf16 kernel (persistent workgroups, one wave per 16 output channels):
-//  * A tile is one row segment of 32 pixels with all C channels: in the map that is one
-//    contiguous run, so the three halo rows (34 pixels each) load with 16-byte coalesced
-//    reads and the gate tile stores the same way (staged through LDS). The next tile's halo
-//    is loaded into registers while the current one is computed (the LDS-only barriers leave
-//    those loads in flight). Each XCD walks its own contiguous band of tiles, so the rows a
-//    tile shares with the tiles above and below it are L2 hits on that XCD.
-//  * Depth-wise 3x3 on the vector unit in fp32: a thread owns two adjacent channels and
-//    32 C / (2 threads) consecutive pixels (4 at C = 192); a 3 x 3 window of halo values slides
-//    along them. Taps and biases come from a tap-major LDS table read per tile, which leaves
-//    the registers for two workgroups per CU.
+// bf16 kernel: a workgroup walks down a strip of row segments of 32 SEG pixels (one x segment,
+// `rows` consecutive rows of one image) with SEG x CB waves (CB = C / 32; SEG = 2 where the LDS
+// holds it, C <= 192, which gives one workgroup of 12 waves per CU at C = 192):
+//  * Halo rows (32 SEG + 2 pixels x C channels, one contiguous run of the map) reach a ring of four
+//    LDS rows by DMA (buffer_load ... lds), each row once per strip: rows y - 1, y, y + 1
+//    serve output row y while row y + 2 is on its way. Pixels and rows outside the map
+//    read as zeros through the buffer range check (the conv's zero padding).
+//  * Depth-wise 3x3 on the vector unit in fp32: a thread owns two adjacent channels (taps and
+//    bias in registers for the whole launch) and 8 consecutive pixels; a 3 x 3 window of halo
+//    values slides along them. D (bf16) goes to LDS as [pixel][C], two rows' worth: the
+//    depth-wise conv of row y + 1 runs between the same barriers as the point-wise conv of
+//    row y (one barrier per row), so vector and matrix work overlap within each wave.
 //  * Point-wise 1x1 on the matrix unit: G^T[out][px] = W_pw[out][:] . D[px][:] as
-//    v_mfma_f32_16x16x32_bf16 over 16 outputs x 2 blocks of 16 pixels per wave (independent
-//    accumulators, so consecutive MFMAs do not wait on each other). Each wave keeps its 16 rows
-//    of W_pw as bf16 A fragments in registers for the whole launch; D (bf16) is read from LDS
-//    as the B operand one K-step ahead of its use. With C/16 waves per workgroup (12 at
-//    C = 192) three waves share each SIMD, so one wave's LDS latency hides behind another's
-//    MFMAs.
-//  * Sigmoid in fp32 on the accumulator, rounded once to bf16.
+//    v_mfma_f32_16x16x32_bf16; wave v owns outputs 32 (v % CB) .. + 31 (two 16-row A blocks of
+//    W_pw, bf16, in registers for the whole launch) for the 32 pixels 32 (v / CB) .. + 31 (two
+//    16-column B blocks read from D), so D is read C / 32 times per row segment.
+//  * Sigmoid in fp32 on the accumulator, rounded once to bf16; a lane's accumulator holds 4
+//    consecutive output channels of one pixel, stored as 8 bytes straight to the map at the
+//    start of the next row's step (so the store's latency hides behind that step).
 #include <algorithm>
 
 #include "internal.hpp"
@@ -30,192 +30,218 @@
 namespace rib {
 namespace {
 
-constexpr int kGatePx = 32;   // pixels per tile (one MFMA column block)
-constexpr int kXcds = 8;      // accelerator dies; workgroups are dealt to them round-robin
+constexpr int kGatePx = 32;   // pixels per wave's share of a row segment (two MFMA column blocks)
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS operations, not for its
-// global loads (the release fence of __syncthreads would also wait for the next tile's halo
-// loads, which are meant to stay in flight across the barrier). The memory clobber keeps the
-// compiler from moving memory operations across it.
+// global traffic (the stores and the next halo row's DMA stay in flight across it). The memory
+// clobber keeps the compiler from moving memory operations across it.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Workgroup barrier after all of this wave's memory operations (halo DMA included) completed.
+__device__ __forceinline__ void full_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ float sigmoid_fast(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 __device__ __forceinline__ float sigmoid_exact(float z) { return 1.0f / (1.0f + expf(-z)); }
 
-template <int CB>  // C = 32 CB channels; one wave per 16 output channels
-__global__ __launch_bounds__(128 * CB) void cla_gate_bf16_kernel(GateArgs a) {
+__device__ __forceinline__ float bf_lo(unsigned u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf_hi(unsigned u) { return __builtin_bit_cast(float, u & 0xffff0000u); }
+
+template <int CB, int SEG>  // C = 32 CB channels; segments of 32 SEG pixels; SEG x CB waves
+__global__ __launch_bounds__(64 * CB * SEG) void cla_gate_bf16_kernel(GateArgs a, int rows) {
   constexpr int C = 32 * CB;
-  constexpr int KS = C / 32;                 // MFMA K-steps (32 channels) of the point-wise conv
-  constexpr int NT = 128 * CB;
-  constexpr int HP = kGatePx + 2;            // halo row width in pixels
-  constexpr int DROW = C + 8;                // padded LDS row (bf16) of D and of the staged gate
-  static_assert(NT % (C / 2) == 0 && kGatePx % (NT / (C / 2)) == 0, "thread layout of the depth-wise stage");
-  constexpr int kPxGroups = NT / (C / 2);    // pixel groups of the depth-wise stage
-  constexpr int kPxPerThread = kGatePx / kPxGroups;
-  __shared__ bf16 sX[3 * HP * C];            // halo rows y-1, y, y+1; later the staged gate tile
-  __shared__ bf16 sD[kGatePx * DROW];        // depth-wise output, [px][C] (+ pad)
-  __shared__ float sTap[20][C / 2];          // [9 taps of the even channel, 9 of the odd, 2 biases][pair]:
-                                             // lanes (consecutive pairs) read consecutive words
-  __shared__ float sBpw[C];                  // point-wise bias
-  static_assert(3 * HP * C >= kGatePx * DROW, "the gate tile reuses the halo buffer");
+  constexpr int NW = CB * SEG;                    // waves
+  constexpr int NT = 64 * NW;
+  constexpr int SPX = kGatePx * SEG;              // pixels per row segment
+  constexpr int KS = CB;                          // MFMA K-steps (32 channels) of the point-wise conv
+  constexpr int HP = SPX + 2;                     // halo row width in pixels
+  constexpr int CPX = C / 8;                      // 16-byte chunks per pixel
+  constexpr int kRowChunks = HP * CPX;
+  constexpr int kRowInsts = (kRowChunks + 63) / 64;   // DMA instructions per halo row
+  constexpr int kWaveInsts = (kRowInsts + NW - 1) / NW;
+  constexpr int kRing = 4;
+  constexpr int DROW = C + 8;                     // padded LDS row (bf16) of D
+  constexpr int kPxPerThread = 8;                 // SPX pixels over the 4 SEG thread groups of a channel pair
+  static_assert(NT == 4 * SEG * (C / 2), "two channels x 8 pixels per thread");
+  __shared__ u32x4 sRing[kRing][kRowInsts * 64];
+  __shared__ bf16 sD[2][SPX * DROW];   // two rows' D (double buffer)
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-
-  // point-wise weights of this wave's 16 output rows as 16x16x32 A fragments: lane l holds
-  // row l % 16, channels 32 s + 8 (l / 16) + j
   const int l16 = lane & 15, quad = lane >> 4;
-  bf16x8 wa[KS];
-  {
-    const float* wrow = a.w_pw + (int64_t)(16 * wave + l16) * C;
+  const int og = wave % CB, sg = wave / CB;       // output group (32 channels) and 32-pixel half
+
+  // strip: image b, x segment xt, rows [y0, y1)
+  const int H = a.H, W = a.W;
+  const int ntx = (W + SPX - 1) / SPX;
+  const int nys = (H + rows - 1) / rows;
+  const int col = blockIdx.x / nys, ys = blockIdx.x - col * nys;
+  const int b = col / ntx, xt = col - b * ntx;
+  const int x0 = xt * SPX, y0 = ys * rows, y1 = min(H, y0 + rows);
+  const bf16* x = (const bf16*)a.x;
+  bf16* gout = (bf16*)a.g;
+
+  // halo row DMA: this wave's instructions i = wave + NW j; lane chunk c = 64 i + lane is halo
+  // pixel hp = c / CPX (map pixel x0 - 1 + hp) and channel chunk c % CPX. The row's buffer
+  // starts at map pixel bx = max(x0 - 1, 0) and ends at pixel min(W, x0 + SPX + 1): at x0 = 0 the
+  // left halo pixel's offset is negative and, like pixels past W, fails the unsigned range check
+  // (zeros).
+  const int bx = x0 > 0 ? x0 - 1 : 0;
+  unsigned doff[kWaveInsts];
+#pragma unroll
+  for (int j = 0; j < kWaveInsts; ++j) {
+    const int c = 64 * (wave + NW * j) + lane;
+    const int hp = c / CPX, k = c - hp * CPX;
+    doff[j] = c < kRowChunks ? (unsigned)((x0 - 1 + hp - bx) * C * 2 + 16 * k) : 0x80000000u;
+  }
+  const int seg_bytes = (min(W, x0 + SPX + 1) - bx) * C * 2;
+  auto dma_row = [&](int y) {
+    const bool in = y >= 0 && y < H;
+    const bf16* base = x + (((int64_t)b * H + (in ? y : 0)) * W + bx) * C;
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<bf16*>(base), 0, in ? seg_bytes : 0, 0x00020000);
+    u32x4* slot = sRing[(y - y0 + 1) & (kRing - 1)];
+#pragma unroll
+    for (int j = 0; j < kWaveInsts; ++j) {
+      const int i = wave + NW * j;
+      if (i < kRowInsts)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(slot + 64 * i), 16,
+                                                 (int)doff[j], 0, 0, 0);
+    }
+  };
+
+  // point-wise weights of this wave's 32 output rows as 16x16x32 A fragments: lane l holds row
+  // 32 og + 16 ob + l % 16, channels 32 s + 8 (l / 16) + j; the bias of the lane's
+  // accumulator rows 32 og + 16 ob + 4 (l / 16) + i
+  bf16x8 wa[2][KS];
+  f32x4 bias[2];
+#pragma unroll
+  for (int ob = 0; ob < 2; ++ob) {
+    const float* wrow = a.w_pw + (int64_t)(32 * og + 16 * ob + l16) * C;
 #pragma unroll
     for (int s = 0; s < KS; ++s)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) wa[s][j] = f32_to_bf16(wrow[32 * s + 8 * quad + j]);
-  }
-  // biases and depth-wise taps live in LDS (re-read per tile) to keep registers for two
-  // workgroups per CU
-  for (int i = tid; i < C; i += NT) {
-    sBpw[i] = a.b_pw ? a.b_pw[i] : 0.f;
-    const int pr = i >> 1, e = i & 1;
+      for (int j = 0; j < 8; ++j) wa[ob][s][j] = f32_to_bf16(wrow[32 * s + 8 * quad + j]);
 #pragma unroll
-    for (int k = 0; k < 9; ++k) sTap[9 * e + k][pr] = a.w_dw[i * 9 + k];
-    sTap[18 + e][pr] = a.b_dw ? a.b_dw[i] : 0.f;
+    for (int i = 0; i < 4; ++i) bias[ob][i] = a.b_pw ? a.b_pw[32 * og + 16 * ob + 4 * quad + i] : 0.f;
   }
-  __syncthreads();
+  // depth-wise taps and biases of the thread's channel pair
   const int cp = tid % (C / 2), pg = tid / (C / 2);
+  float tap[2][9], bdw[2];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+#pragma unroll
+    for (int k = 0; k < 9; ++k) tap[e][k] = a.w_dw[(2 * cp + e) * 9 + k];
+    bdw[e] = a.b_dw ? a.b_dw[2 * cp + e] : 0.f;
+  }
 
-  const bf16* x = (const bf16*)a.x;
-  bf16* gout = (bf16*)a.g;
-  const int H = a.H, W = a.W;
-  const int ntx = (W + kGatePx - 1) / kGatePx;
-  const int ntiles = a.B * H * ntx;
-  // halo of a tile: chunk i (16 bytes) of row r, pixel p, channel chunk k sits at sX + 8 i
-  constexpr int kChunksPerPx = C / 8;
-  constexpr int kHaloChunks = 3 * HP * kChunksPerPx;
-  constexpr int kLoads = (kHaloChunks + NT - 1) / NT;
-  u32x4 pre[kLoads];
-  auto fetch = [&](int tile) {
-    const int xt = tile % ntx, by = tile / ntx, y = by % H, x0 = xt * kGatePx;
+  // depth-wise 3x3 (fp32) of output row y for the thread's 8 pixels into D buffer db; rows
+  // y - 1 .. y + 1 sit in ring slots (y - y0) .. (y - y0 + 2) mod 4; a 3 x 3 window of halo
+  // values slides along the pixels
+  auto depthwise = [&](int y, int db) {
+    const unsigned* rr[3];
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      const int i = tid + j * NT;
-      const int r = i / (HP * kChunksPerPx);
-      const int rr = i - r * (HP * kChunksPerPx);
-      const int p = rr / kChunksPerPx, k = rr - p * kChunksPerPx;
-      const int yy = y + r - 1, xx = x0 + p - 1;
-      pre[j] = u32x4(0u);
-      if (i < kHaloChunks && yy >= 0 && yy < H && xx >= 0 && xx < W)
-        pre[j] = *(const u32x4*)(x + ((int64_t)(by + r - 1) * W + xx) * C + 8 * k);
-    }
-  };
-  // workgroup b runs on XCD b % 8 (round-robin dispatch); the grid is a multiple of 8
-  const int xcd = blockIdx.x % kXcds, lw = blockIdx.x / kXcds, nw = gridDim.x / kXcds;
-  const int band = (ntiles + kXcds - 1) / kXcds;
-  const int t_end = min(ntiles, (xcd + 1) * band);
-  const int t_first = xcd * band + lw;
-  if (t_first < t_end) fetch(t_first);
-  for (int tile = t_first; tile < t_end; tile += nw) {
-    const int xt = tile % ntx;
-    const int by = tile / ntx;               // b * H + y
-    const int x0 = xt * kGatePx;
-    // ---- halo rows (zero outside the map) from the registers into LDS; then start the next tile's
-    lds_barrier();                            // the previous tile's gate tile has been copied out
+    for (int ky = 0; ky < 3; ++ky) rr[ky] = (const unsigned*)sRing[(y + ky - y0) & (kRing - 1)] + cp;
+    const int h0 = kPxPerThread * pg;   // halo pixel of the window's left column
+    bf16* dst = sD[db] + h0 * DROW + 2 * cp;
+    float xw[3][3][2];
 #pragma unroll
-    for (int j = 0; j < kLoads; ++j) {
-      const int i = tid + j * NT;
-      if (i < kHaloChunks) *(u32x4*)&sX[8 * i] = pre[j];
-    }
-    lds_barrier();
-    if (tile + nw < t_end) fetch(tile + nw);
-    // ---- depth-wise 3x3 (fp32), rounded to bf16 into D; a 3 x 3 window of halo values slides
-    // along the thread's pixels (three new LDS reads per pixel)
-    {
-      const int px0 = pg * kPxPerThread;
-      float xw[3][3][2];
+    for (int ky = 0; ky < 3; ++ky)
 #pragma unroll
-      for (int ky = 0; ky < 3; ++ky)
+      for (int kx = 0; kx < 2; ++kx) {
+        const unsigned u = rr[ky][(h0 + kx) * (C / 2)];
+        xw[ky][kx + 1][0] = bf_lo(u);
+        xw[ky][kx + 1][1] = bf_hi(u);
+      }
 #pragma unroll
-        for (int kx = 0; kx < 2; ++kx) {
-          const bf16x2 xv = *(const bf16x2*)&sX[(ky * HP + px0 + kx) * C + 2 * cp];
-          xw[ky][kx + 1][0] = (float)xv[0];
-          xw[ky][kx + 1][1] = (float)xv[1];
+    for (int i = 0; i < kPxPerThread; ++i) {
+#pragma unroll
+      for (int ky = 0; ky < 3; ++ky) {
+        const unsigned u = rr[ky][(h0 + i + 2) * (C / 2)];
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          xw[ky][0][e] = xw[ky][1][e];
+          xw[ky][1][e] = xw[ky][2][e];
         }
+        xw[ky][2][0] = bf_lo(u);
+        xw[ky][2][1] = bf_hi(u);
+      }
+      float d[2];
 #pragma unroll
-      for (int i = 0; i < kPxPerThread; ++i) {
-        const int px = px0 + i;
-#pragma unroll
-        for (int ky = 0; ky < 3; ++ky) {
-          const bf16x2 xv = *(const bf16x2*)&sX[(ky * HP + px + 2) * C + 2 * cp];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            xw[ky][0][e] = xw[ky][1][e];
-            xw[ky][1][e] = xw[ky][2][e];
-            xw[ky][2][e] = (float)xv[e];
-          }
-        }
-        float d0 = sTap[18][cp], d1 = sTap[19][cp];
+      for (int e = 0; e < 2; ++e) {
+        d[e] = bdw[e];
 #pragma unroll
         for (int ky = 0; ky < 3; ++ky)
 #pragma unroll
-          for (int kx = 0; kx < 3; ++kx) {
-            d0 = fmaf(sTap[3 * ky + kx][cp], xw[ky][kx][0], d0);
-            d1 = fmaf(sTap[9 + 3 * ky + kx][cp], xw[ky][kx][1], d1);
-          }
-        bf16x2 dv;
-        dv[0] = f32_to_bf16(d0);
-        dv[1] = f32_to_bf16(d1);
-        *(bf16x2*)&sD[px * DROW + 2 * cp] = dv;
+          for (int kx = 0; kx < 3; ++kx) d[e] = fmaf(tap[e][3 * ky + kx], xw[ky][kx][e], d[e]);
       }
+      bf16x2 dv;
+      dv[0] = f32_to_bf16(d[0]);
+      dv[1] = f32_to_bf16(d[1]);
+      *(bf16x2*)(dst + i * DROW) = dv;
     }
-    lds_barrier();
-    // ---- point-wise 1x1 on MFMA: block pb = outputs 16 wave + [0, 16) x pixels 16 pb + [0, 16);
-    // lane l holds outputs 4 (l / 16) + v of the block for pixel l % 16. The accumulators start
-    // at the point-wise bias.
-    f32x4 acc[2];
-    {
-      const f32x4 b4 = *(const f32x4*)&sBpw[16 * wave + 4 * quad];
-      acc[0] = b4;
-      acc[1] = b4;
-    }
-    auto bfrag = [&](int pb, int s) {
-      return *(const bf16x8*)&sD[(16 * pb + l16) * DROW + 32 * s + 8 * quad];
-    };
-    bf16x8 bcur[2] = {bfrag(0, 0), bfrag(1, 0)};
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      bf16x8 bnext[2];
-      if (s + 1 < KS) {
-        bnext[0] = bfrag(0, s + 1);
-        bnext[1] = bfrag(1, s + 1);
-      }
-#pragma unroll
-      for (int pb = 0; pb < 2; ++pb)
-        acc[pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[s], bcur[pb], acc[pb], 0, 0, 0);
-      if (s + 1 < KS) {
-        bcur[0] = bnext[0];
-        bcur[1] = bnext[1];
-      }
-    }
-    // ---- sigmoid; stage the gate tile [px][C] in the halo buffer (free since the last barrier)
+  };
+
+  // G of the previous row, 4 bf16 per (ob, pb), stored at the start of the next step
+  uint2 gres[2][2];
+  auto store_row = [&](int y) {
+    bf16* grow = gout + (((int64_t)b * H + y) * W + x0) * C + 32 * og + 4 * quad;
 #pragma unroll
     for (int pb = 0; pb < 2; ++pb) {
-      bf16 o4[4];
+      const int px = 32 * sg + 16 * pb + l16;
+      if (x0 + px < W)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o4[i] = f32_to_bf16(sigmoid_fast(acc[pb][i]));
-      *(uint2*)&sX[(16 * pb + l16) * DROW + 16 * wave + 4 * quad] = *(const uint2*)o4;
+        for (int ob = 0; ob < 2; ++ob) *(uint2*)(grow + (int64_t)px * C + 16 * ob) = gres[ob][pb];
     }
-    lds_barrier();
-    // ---- coalesced copy-out of the pixels inside the map
-    const int npx = min(kGatePx, W - x0);
-    bf16* gdst = gout + ((int64_t)by * W + x0) * C;
-    for (int i = tid; i < npx * kChunksPerPx; i += NT) {
-      const int p = i / kChunksPerPx, k = i - p * kChunksPerPx;
-      *(u32x4*)(gdst + (int64_t)p * C + 8 * k) = *(const u32x4*)&sX[p * DROW + 8 * k];
+  };
+
+  // Step y: the point-wise conv of row y (D buffer (y - y0) mod 2, formed in the previous step)
+  // and the depth-wise conv of row y + 1 into the other buffer run between the same two barriers,
+  // so each wave has matrix and vector work in flight together; row y + 3's DMA goes into the ring
+  // slot of row y - 1 and row y - 1's gate is stored.
+  dma_row(y0 - 1);
+  dma_row(y0);
+  dma_row(y0 + 1);
+  if (y0 + 2 <= y1) dma_row(y0 + 2);
+  full_barrier();
+  depthwise(y0, 0);
+  for (int y = y0; y < y1; ++y) {
+    // row y + 2 landed, D of row y complete, every wave past the previous step (ring slot of row
+    // y - 1 and the other D buffer free)
+    full_barrier();
+    if (y + 3 <= y1) dma_row(y + 3);
+    if (y > y0) store_row(y - 1);
+    const int db = (y - y0) & 1;
+    // ---- point-wise 1x1: block (ob, pb) = outputs 32 og + 16 ob + [0, 16) x pixels 32 sg + 16 pb +
+    // [0, 16); lane l holds outputs 4 (l / 16) + i of the block for pixel l % 16
+    f32x4 acc[2][2];
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob) acc[ob][0] = acc[ob][1] = bias[ob];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      bf16x8 bf[2];
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb)
+        bf[pb] = *(const bf16x8*)&sD[db][(32 * sg + 16 * pb + l16) * DROW + 32 * s + 8 * quad];
+#pragma unroll
+      for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+        for (int pb = 0; pb < 2; ++pb)
+          acc[ob][pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ob][s], bf[pb], acc[ob][pb], 0, 0, 0);
     }
+    if (y + 1 < y1) depthwise(y + 1, db ^ 1);
+#pragma unroll
+    for (int ob = 0; ob < 2; ++ob)
+#pragma unroll
+      for (int pb = 0; pb < 2; ++pb) {
+        bf16 o4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o4[i] = f32_to_bf16(sigmoid_fast(acc[ob][pb][i]));
+        gres[ob][pb] = *(const uint2*)o4;
+      }
   }
+  if (y1 > y0) store_row(y1 - 1);
 }
 
 // float32 gate: a workgroup per 32-pixel row segment; depth-wise into LDS, then one thread per
@@ -251,24 +277,31 @@ __global__ __launch_bounds__(256) void cla_gate_f32_kernel(GateArgs a) {
   }
 }
 
+// One round of one workgroup per CU: at C = 192 the ring and D buffers take 154 KB of the CU's
+// 160 KB of LDS (SEG = 2), and at C = 224 and 256 (SEG = 1) more than half of it, so a second
+// workgroup would not be resident at the same time.
 template <int CB>
-hipError_t launch_gate_cb(const GateArgs& a, int tiles, hipStream_t stream) {
-  int dev = 0, cus = 0, per_cu = 0;
+hipError_t launch_gate_cb(const GateArgs& a, hipStream_t stream) {
+  constexpr int SEG = CB <= 6 ? 2 : 1;
+  int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-  if (e == hipSuccess)
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, cla_gate_bf16_kernel<CB>, 128 * CB, 0);
   if (e != hipSuccess) return e;
-  const int64_t slots = (int64_t)std::max(cus, 1) * std::max(per_cu, 1);
-  const int grid = (int)std::max<int64_t>(kXcds, std::min<int64_t>(tiles, slots) / kXcds * kXcds);
-  hipLaunchKernelGGL(cla_gate_bf16_kernel<CB>, dim3(grid), dim3(128 * CB), 0, stream, a);
+  // strips of `rows` rows: the fewest rows per strip whose strips all fit one round of resident
+  // workgroups (each strip re-reads two halo rows, so longer strips waste less)
+  const int64_t slots = std::max(cus, 1);
+  const int64_t cols = (int64_t)a.B * ((a.W + kGatePx * SEG - 1) / (kGatePx * SEG));
+  int rows = (int)std::max<int64_t>(1, (cols * a.H + slots - 1) / slots);
+  while (rows < a.H && cols * ((a.H + rows - 1) / rows) > slots) ++rows;
+  const int64_t grid = cols * ((a.H + rows - 1) / rows);
+  hipLaunchKernelGGL((cla_gate_bf16_kernel<CB, SEG>), dim3((unsigned)grid), dim3(64 * CB * SEG), 0, stream, a, rows);
   return hipGetLastError();
 }
 
 }  // namespace
 
-// Up to 8 waves of 32 output channels: two waves per SIMD keep 256 VGPRs each for the
-// register-resident point-wise weights.
+// One wave per 32 output channels, up to 8 (C = 256): the point-wise weights stay resident in
+// registers (8 VGPRs per 32 input channels).
 bool cla_channels_supported(int C) { return C >= 32 && C <= 256 && C % 32 == 0; }
 
 hipError_t launch_cla_gate(const GateArgs& a, int esize, hipStream_t stream) {
@@ -281,14 +314,14 @@ hipError_t launch_cla_gate(const GateArgs& a, int esize, hipStream_t stream) {
     return hipGetLastError();
   }
   switch (a.C / 32) {
-    case 1: return launch_gate_cb<1>(a, (int)tiles, stream);
-    case 2: return launch_gate_cb<2>(a, (int)tiles, stream);
-    case 3: return launch_gate_cb<3>(a, (int)tiles, stream);
-    case 4: return launch_gate_cb<4>(a, (int)tiles, stream);
-    case 5: return launch_gate_cb<5>(a, (int)tiles, stream);
-    case 6: return launch_gate_cb<6>(a, (int)tiles, stream);
-    case 7: return launch_gate_cb<7>(a, (int)tiles, stream);
-    case 8: return launch_gate_cb<8>(a, (int)tiles, stream);
+    case 1: return launch_gate_cb<1>(a, stream);
+    case 2: return launch_gate_cb<2>(a, stream);
+    case 3: return launch_gate_cb<3>(a, stream);
+    case 4: return launch_gate_cb<4>(a, stream);
+    case 5: return launch_gate_cb<5>(a, stream);
+    case 6: return launch_gate_cb<6>(a, stream);
+    case 7: return launch_gate_cb<7>(a, stream);
+    case 8: return launch_gate_cb<8>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }
