@@ -444,6 +444,13 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
   // With RPB the accumulator init carries each score's bias too (rebuilt per
   // subtile) and padded keys start at -inf, so their P is zero.
   float pad_sub[2] = {0.f, 0.f};
+  // Early exit (one positional K-step): after the range's first two tiles every row's partial
+  // sum must already reach the underflow guard; rows whose bound overshoots their scores by
+  // more than the guard allows (the case the exact pass exists for) show it there, and the
+  // workgroup goes to the exact pass without finishing the fast one. The partial sum is a sum
+  // over fewer keys than the final one, so it exits only where the final check could fail too
+  // or, for rows whose large scores all lie past the first 128 keys, a little more often.
+  bool fast_exit = false;
   if constexpr (KP == 1 && !RPB) {
     // ===== fast pass, one positional K-step. Per 32-key subtile h (a half step) a wave
     // forms 16 P words (2 exp2 + 1 pack each, 32 scores) and issues 14 MFMAs: the six score
@@ -577,7 +584,25 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
         hstep(b0, 0, b0, 1);
         hstep(b0, 1, b1, 0);
         dma_wait_older();   // tile t + 2 landed (this wave's part)
-        barrier_dma();
+        if (t == t0 + 1 && t + 1 < t1) {
+          // the partial row sums (the block deferred to the next half step not yet added)
+          bool low = false;
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            const float r0 = __shfl(lsum[nb][0], l32 & 15), r1 = __shfl(lsum[nb][1], l32 & 15);
+            low |= !((l32 < 16 ? r0 : r1) >= kUnderflowGuard);
+          }
+          if (__syncthreads_or(low)) {
+            fast_exit = true;
+            break;
+          }
+        } else {
+          barrier_dma();
+        }
+      }
+      if (fast_exit) {
+        l_run[0] = l_run[1] = 0.f;
+        return;
       }
       R(1, 1);
       P(1, 1);
@@ -744,7 +769,7 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
     }
   }
 
-  bool bad = false;
+  bool bad = fast_exit;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     // both halves of the wave hold part of each row sum; the padded keys are
