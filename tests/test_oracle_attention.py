@@ -128,6 +128,27 @@ def test_matches_torch_sdpa_with_additive_bias():
     np.testing.assert_allclose(O, ref2[0, 0].numpy(), rtol=1e-12, atol=1e-13)
 
 
+def test_default_scale_is_sdpa_default_over_concatenated_channels():
+    """default_scale (reading R8: the scale multiplies the whole concatenated product) against
+    torch SDPA's own default scale, 1/sqrt of the query width, applied to [Q_c | Q_p]: the map-level
+    oracle with scale=None equals SDPA with no scale argument on the concatenated channels."""
+    rng = np.random.default_rng(11)
+    B, H, W, heads, d_c, w, r = 1, 6, 6, 2, 5, 3, 3
+    q = rng.standard_normal((B, H, W, heads, d_c))
+    k = rng.standard_normal((B, H, W, heads, d_c))
+    v = rng.standard_normal((B, H, W, heads, d_c))
+    qp = rng.standard_normal((w * w, r))
+    kp = rng.standard_normal((w * w, r))
+    O, _ = oracle.rib_window_attn_fwd(q, k, v, qp, kp, w)
+    qw, kw, vw, ow = (oracle.window_partition(x, w) for x in (q, k, v, O))   # [windows, heads, N, d]
+    for u in range(qw.shape[0]):
+        for h in range(heads):
+            qh = torch.from_numpy(np.concatenate([qw[u, h], qp], 1))[None, None]
+            kh = torch.from_numpy(np.concatenate([kw[u, h], kp], 1))[None, None]
+            ref = torch.nn.functional.scaled_dot_product_attention(qh, kh, torch.from_numpy(vw[u, h])[None, None])
+            np.testing.assert_allclose(ow[u, h], ref[0, 0].numpy(), rtol=1e-12, atol=1e-13)
+
+
 def test_zero_positional_tokens_reduce_to_plain_attention():
     rng = np.random.default_rng(4)
     qc, kc, v, qp, kp = _unit(rng, N=36)

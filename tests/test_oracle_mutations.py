@@ -67,6 +67,10 @@ def _bwd_unscaled(qc, kc, v, qp, kp, do, scale):
     return g[0], g[1] / scale, g[2], g[3], g[4] / scale
 
 
+def _default_scale_content_only(d_c, rank):
+    return 1.0 / math.sqrt(d_c)
+
+
 def _coords_pixel_centres(w):
     n = [2 * i + 1 - w for i in range(w)]
     return n, np.array([v / w for v in n])
@@ -187,6 +191,7 @@ MUTATIONS = [
     ("attention_window_fwd", _fwd_wrong_axis, [(ta.test_softmax_rows_sum_to_one_and_lse,), (ta.test_closed_forms,)]),
     ("attention_window_bwd", _bwd_missing_d, [(ta.test_backward_finite_differences,), (ta.test_backward_invariants,)]),
     ("attention_window_bwd", _bwd_unscaled, [(ta.test_backward_finite_differences,), (ta.test_worked_example_w2, "golden")]),
+    ("default_scale", _default_scale_content_only, [(ta.test_default_scale_is_sdpa_default_over_concatenated_channels,)]),
     ("window_coords", _coords_pixel_centres, [(tp.test_coords_match_linspace, 16), (tp.test_fourier_hand_derived, "golden")]),
     ("fourier_features", _fourier_linear_freqs, [(tp.test_fourier_hand_derived, "golden"), (tp.test_fourier_periodicity_power_of_two_windows, 4)]),
     ("fourier_features", _fourier_interleaved, [(tp.test_fourier_hand_derived, "golden")]),
