@@ -117,6 +117,32 @@ __device__ __forceinline__ bf16x8 tr_frag(const u32x4* part, int row_chunks, int
 }
 
 
+// Epilogue stores of a 32-channel bf16 result whose lane holds the channels 8 gq + 4 h + i
+// (i < 4) of token (block nb, lane % 32): stored as they are, each store instruction would
+// touch 32 map rows with 8 bytes each. The wave stages its 64 rows in its own LDS region
+// ([64 rows][5 chunks]) and writes whole 64-byte rows back, 16 rows per store instruction.
+// `row_of(t)` is the map element offset of token t, `val(nb, v)` the lane's value v of block nb.
+constexpr int kStageRow = 5;
+template <class RowOf, class Val>
+__device__ __forceinline__ void stage_store_rows(bf16* stage, bf16* dst, int t0, int N, int lane, RowOf row_of, Val val) {
+  const int half = lane >> 5, l32 = lane & 31;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+    for (int gq = 0; gq < 4; ++gq) {
+      bf16 o4[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o4[i] = f32_to_bf16(val(nb, 4 * gq + i));
+      *(uint2*)(stage + (nb * 32 + l32) * kStageRow * 8 + 8 * gq + 4 * half) = *(const uint2*)o4;
+    }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int rl = (lane >> 2) + 16 * j, ch = 8 * (lane & 3);
+    const u32x4 v = *(const u32x4*)(stage + rl * kStageRow * 8 + ch);
+    if (t0 + rl < N) *(u32x4*)(dst + row_of(t0 + rl) + ch) = v;
+  }
+}
+
 // Loads the lane's 8 channels (16s + 8h ..) of a [content 32 | pos rp] token whose content and
 // positional rows start at `content` and `pos`.
 __device__ __forceinline__ bf16x8 token_frag(const bf16* content, const bf16* pos, int s, int half) {
@@ -343,22 +369,24 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
   float* dkp = a.dkp_part + ub * rp;
   const float scale = a.scale;
   const float kscale = a.scale / a.c;   // dK_hat from the pre-scaled Q_hat rows
+  {
+    // dV, then dK, staged through the wave's LDS region (the tile ring is free once the DMA of
+    // tiles past the end has drained and every wave is past the loop)
+    static_assert(4 * 64 * kStageRow <= kBufs * L.chunks(), "staging fits the tile ring");
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    __syncthreads();
+    bf16* stage = (bf16*)&sT[0][0] + wave * 64 * kStageRow * 8;
+    auto row_of = [&](int t) { return map_base + (int64_t)(t / g.w) * row_elems + (int64_t)(t % g.w) * pix_elems; };
+    stage_store_rows(stage, dvm, k0, N, lane, row_of, [&](int nb, int v) { return acc_dv[nb][v]; });
+    stage_store_rows(stage, dkm, k0, N, lane, row_of, [&](int nb, int v) { return acc_dk[nb][v] * kscale; });
+  }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int key = k0 + nb * 32 + l32;
     if (key >= N) continue;
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      bf16 v4[4], k4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v4[i] = f32_to_bf16(acc_dv[nb][4 * gq + i]);
-        k4[i] = f32_to_bf16(acc_dk[nb][4 * gq + i] * kscale);
-      }
       const int ch = 8 * gq + 4 * half;
-      const int64_t row = map_base + (int64_t)(key / g.w) * row_elems + (int64_t)(key % g.w) * pix_elems;
-      *(uint2*)(dvm + row + ch) = *(const uint2*)v4;
-      *(uint2*)(dkm + row + ch) = *(const uint2*)k4;
       if (KP == 2) {
         f32x4 p4;
 #pragma unroll
@@ -529,18 +557,21 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   bf16* dqm = (bf16*)a.dq_map;
   float* dqp = a.dqp_part + ub * rp;
   const float scale = a.scale;
+  {
+    static_assert(4 * 64 * kStageRow <= kBufsDq * L.chunks(), "staging fits the tile ring");
+    __builtin_amdgcn_s_waitcnt(vmcnt_only(0));
+    __syncthreads();
+    bf16* stage = (bf16*)&sT[0][0] + wave * 64 * kStageRow * 8;
+    auto row_of = [&](int t) { return map_base + (int64_t)(t / g.w) * row_elems + (int64_t)(t % g.w) * pix_elems; };
+    stage_store_rows(stage, dqm, q0, N, lane, row_of, [&](int nb, int v) { return acc_dq[nb][v] * scale; });
+  }
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int q = q0 + nb * 32 + l32;
     if (q >= N) continue;
 #pragma unroll
     for (int gq = 0; gq < 4; ++gq) {
-      bf16 q4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) q4[i] = f32_to_bf16(acc_dq[nb][4 * gq + i] * scale);
       const int ch = 8 * gq + 4 * half;
-      *(uint2*)(dqm + map_base + (int64_t)(q / g.w) * row_elems + (int64_t)(q % g.w) * pix_elems + ch) =
-          *(const uint2*)q4;
       if (KP == 2) {
         f32x4 p4;
 #pragma unroll

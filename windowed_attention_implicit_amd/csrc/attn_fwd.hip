@@ -881,28 +881,63 @@ __global__ __launch_bounds__(RPB ? 512 : 256, RPB ? 1 : 2) void attn_fwd_bf16_ke
   // rows (map layout) and the LSE of the ungated attention
   bf16* omap = (bf16*)a.o_map;
   const float kLn2 = 0.69314718055994530942f;
+  if constexpr (!RPB) {
+    // A lane holds 16 of its query's 32 channels in 4-channel pieces; stored as they are, every
+    // store instruction would touch 32 rows with 8 bytes each. Instead each wave stages its 64
+    // normalized rows in its own LDS region ([64 rows][5 chunks], the tile ring is free: every
+    // wave is past the loops and the DMA of tiles past the range has drained) and writes them
+    // back as whole 64-byte rows, 16 rows per store instruction.
+    constexpr int kORow = 5;
+    static_assert(C::kWv * kQPerWave * kORow <= kBufs * C::kChunks, "O staging fits the tile ring");
+    __builtin_amdgcn_s_waitcnt(kVmcnt0);
+    __syncthreads();
+    bf16* stage = (bf16*)&sT[0][0] + wave * kQPerWave * kORow * 8;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int q = q0 + nb * 32 + l32;
-    const float l_tot = l_run[nb] + swap_halves(l_run[nb]);
-    const float inv = 1.f / l_tot;
-    if (q < N) {
+    for (int nb = 0; nb < 2; ++nb) {
+      const int q = q0 + nb * 32 + l32;
+      const float l_tot = l_run[nb] + swap_halves(l_run[nb]);
+      const float inv = 1.f / l_tot;
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
-        const int64_t at = map_row(q) + 8 * gq + 4 * half;
         float gv[4] = {inv, inv, inv, inv};
         if constexpr (GATE) {
-          bf16 g4[4];
-          *(uint2*)g4 = *(const uint2*)((const bf16*)a.gate + at);
+          if (q < N) {
+            bf16 g4[4];
+            *(uint2*)g4 = *(const uint2*)((const bf16*)a.gate + map_row(q) + 8 * gq + 4 * half);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) gv[i] = inv * (float)g4[i];
+            for (int i = 0; i < 4; ++i) gv[i] = inv * (float)g4[i];
+          }
         }
         bf16 o4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) o4[i] = f32_to_bf16(acc[nb][4 * gq + i] * gv[i]);
-        *(uint2*)(omap + at) = *(const uint2*)o4;
+        *(uint2*)(stage + (nb * 32 + l32) * kORow * 8 + 8 * gq + 4 * half) = *(const uint2*)o4;
       }
-      if (a.lse && half == 0) a.lse[pm.pixel_head(unit, q)] = (m_run[nb] + log2f(l_tot)) * kLn2;
+      if (q < N && a.lse && half == 0) a.lse[pm.pixel_head(unit, q)] = (m_run[nb] + log2f(l_tot)) * kLn2;
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rl = (lane >> 2) + 16 * j, ch = 8 * (lane & 3);
+      const int q = q0 + rl;
+      const u32x4 v = *(const u32x4*)(stage + rl * kORow * 8 + ch);
+      if (q < N) *(u32x4*)(omap + map_row(q) + ch) = v;
+    }
+  } else {
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int q = q0 + nb * 32 + l32;
+      const float l_tot = l_run[nb] + swap_halves(l_run[nb]);
+      const float inv = 1.f / l_tot;
+      if (q < N) {
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          bf16 o4[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) o4[i] = f32_to_bf16(acc[nb][4 * gq + i] * inv);
+          *(uint2*)(omap + map_row(q) + 8 * gq + 4 * half) = *(const uint2*)o4;
+        }
+        if (a.lse && half == 0) a.lse[pm.pixel_head(unit, q)] = (m_run[nb] + log2f(l_tot)) * kLn2;
+      }
     }
   }
 }
