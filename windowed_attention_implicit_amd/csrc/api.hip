@@ -8,6 +8,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <optional>
 #include <string>
 #include <utility>
 #include <vector>
@@ -549,7 +550,10 @@ static rib_status_t attn_fwd_impl(const rib_shape_t* shape, rib_dtype_t dtype, f
     a.part = L.part;
     // the split plan queries the device (it can fail), so it is made before anything is launched
     if (bf && (e = plan_fwd_split(a)) != hipSuccess) return hip_fail(e, "split plan");
-    TimedGroup t_part(RIB_KERNEL_PARTITION, st);
+    // the partition group is timed only where it launches something (map-addressed windows with
+    // r = 16 or 32 gather nothing)
+    std::optional<TimedGroup> t_part;
+    if (L.qp || !mapkv) t_part.emplace(RIB_KERNEL_PARTITION, st);
     if (L.qp) {   // positional rows padded to rp (the fused gather below reads K_p)
       if ((e = launch_pack_pos(g.N, g.n_rows, g.r, rp, es, q_p, es, L.qp, st)) != hipSuccess)
         return hip_fail(e, "pack q_p");
@@ -567,7 +571,7 @@ static rib_status_t attn_fwd_impl(const rib_shape_t* shape, rib_dtype_t dtype, f
       if ((e = launch_partition(g, es, k_c, L.kw, st)) != hipSuccess) return hip_fail(e, "partition k");
       if ((e = launch_partition(g, es, v, L.vw, st)) != hipSuccess) return hip_fail(e, "partition v");
     }
-    t_part.end();
+    if (t_part) t_part->end();
     TimedGroup t_attn(RIB_KERNEL_ATTN_FWD, st);
     e = bf ? launch_attn_fwd_bf16(a, st) : launch_attn_fwd_simple(a, es, st);
     if (e != hipSuccess) return hip_fail(e, "attention forward");
