@@ -22,7 +22,13 @@
 //    16-column B blocks read from D), so D is read C / 32 times per row segment.
 //  * Sigmoid in fp32 on the accumulator, rounded once to bf16; a lane's accumulator holds 4
 //    consecutive output channels of one pixel, stored as 8 bytes straight to the map at the
-//    start of the next row's step (so the store's latency hides behind that step).
+//    start of the next row's step (so the store's latency hides behind that step), through a
+//    range-checked buffer store that drops pixels past the map's edge.
+//  * The point-wise weights reach LDS once per workgroup by coalesced DMA (one float32 row per
+//    instruction) before the first depth-wise conv, in the D buffers and the last ring slot, and
+//    each wave reads its A fragments there: loading them per lane straight from global memory
+//    (16 rows of 16-byte pieces per instruction, every row twice per workgroup) took a quarter
+//    of the kernel's time on a 192-channel map.
 #include <algorithm>
 
 #include "internal.hpp"
@@ -33,6 +39,7 @@ namespace {
 constexpr int kGatePx = 32;   // pixels per wave's share of a row segment (two MFMA column blocks)
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
 
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS operations, not for its
 // global traffic (the stores and the next halo row's DMA stay in flight across it). The memory
@@ -41,6 +48,12 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 
 // Workgroup barrier after all of this wave's memory operations (halo DMA included) completed.
 __device__ __forceinline__ void full_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Workgroup barrier after all but this wave's last four memory operations completed: the row
+// stores that follow the halo DMA the barrier waits for (memory operations complete in order).
+__device__ __forceinline__ void barrier_after_dma_of_prev_step() {
+  asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 __device__ __forceinline__ float sigmoid_fast(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 __device__ __forceinline__ float sigmoid_exact(float z) { return 1.0f / (1.0f + expf(-z)); }
@@ -65,7 +78,7 @@ __global__ __launch_bounds__(64 * CB * SEG) void cla_gate_bf16_kernel(GateArgs a
   constexpr int kPxPerThread = 8;                 // SPX pixels over the 4 SEG thread groups of a channel pair
   static_assert(NT == 4 * SEG * (C / 2), "two channels x 8 pixels per thread");
   __shared__ u32x4 sRing[kRing][kRowInsts * 64];
-  __shared__ bf16 sD[2][SPX * DROW];   // two rows' D (double buffer)
+  __shared__ __align__(16) bf16 sD[2][SPX * DROW];   // two rows' D (double buffer)
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -114,18 +127,12 @@ __global__ __launch_bounds__(64 * CB * SEG) void cla_gate_bf16_kernel(GateArgs a
   // point-wise weights of this wave's 32 output rows as 16x16x32 A fragments: lane l holds row
   // 32 og + 16 ob + l % 16, channels 32 s + 8 (l / 16) + j; the bias of the lane's
   // accumulator rows 32 og + 16 ob + 4 (l / 16) + i
-  bf16x8 wa[2][KS];
+  bf16x8 wa[2][KS];   // filled in the prologue, from LDS
   f32x4 bias[2];
 #pragma unroll
-  for (int ob = 0; ob < 2; ++ob) {
-    const float* wrow = a.w_pw + (int64_t)(32 * og + 16 * ob + l16) * C;
-#pragma unroll
-    for (int s = 0; s < KS; ++s)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) wa[ob][s][j] = f32_to_bf16(wrow[32 * s + 8 * quad + j]);
+  for (int ob = 0; ob < 2; ++ob)
 #pragma unroll
     for (int i = 0; i < 4; ++i) bias[ob][i] = a.b_pw ? a.b_pw[32 * og + 16 * ob + 4 * quad + i] : 0.f;
-  }
   // depth-wise taps and biases of the thread's channel pair
   const int cp = tid % (C / 2), pg = tid / (C / 2);
   float tap[2][9], bdw[2];
@@ -183,16 +190,22 @@ __global__ __launch_bounds__(64 * CB * SEG) void cla_gate_bf16_kernel(GateArgs a
     }
   };
 
-  // G of the previous row, 4 bf16 per (ob, pb), stored at the start of the next step
   uint2 gres[2][2];
+  // G of the previous row, 4 bf16 per (ob, pb), stored at the start of the next step through a
+  // range-checked buffer: pixels past W fall outside the row's range and are dropped, so every
+  // wave issues exactly four stores per row (the barrier below counts on it)
+  const int seg_px = min(W, x0 + SPX) - x0;
   auto store_row = [&](int y) {
-    bf16* grow = gout + (((int64_t)b * H + y) * W + x0) * C + 32 * og + 4 * quad;
+    bf16* grow = gout + (((int64_t)b * H + y) * W + x0) * C;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(grow, 0, seg_px * C * 2, 0x00020000);
 #pragma unroll
     for (int pb = 0; pb < 2; ++pb) {
       const int px = 32 * sg + 16 * pb + l16;
-      if (x0 + px < W)
 #pragma unroll
-        for (int ob = 0; ob < 2; ++ob) *(uint2*)(grow + (int64_t)px * C + 16 * ob) = gres[ob][pb];
+      for (int ob = 0; ob < 2; ++ob) {
+        const int off = (px * C + 32 * og + 16 * ob + 4 * quad) * 2;
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, gres[ob][pb]), rs, off, 0, 0);
+      }
     }
   };
 
@@ -200,16 +213,76 @@ __global__ __launch_bounds__(64 * CB * SEG) void cla_gate_bf16_kernel(GateArgs a
   // and the depth-wise conv of row y + 1 into the other buffer run between the same two barriers,
   // so each wave has matrix and vector work in flight together; row y + 3's DMA goes into the ring
   // slot of row y - 1 and row y - 1's gate is stored.
-  dma_row(y0 - 1);
-  dma_row(y0);
-  dma_row(y0 + 1);
-  if (y0 + 2 <= y1) dma_row(y0 + 2);
-  full_barrier();
+  // Prologue. The first depth-wise conv needs halo rows y0 - 1 .. y0 + 1 (ring slots 0 - 2); row
+  // y0 + 2 (slot 3) is first read in step y0, and the D buffers are first written by the first
+  // depth-wise conv. Until then the D buffers and ring slot 3 stage the point-wise weights: rounds
+  // of kRoundRows float32 rows (whole 32-row output groups), one coalesced DMA instruction per
+  // row, rows kWPitch bytes apart (16 bytes of padding spread the 16 rows of a fragment read over
+  // the LDS banks), first in the D buffers, then in slot 3. The first round's weights go out
+  // before the three halo rows and are waited for alone; the waves owning a round's rows read
+  // their A fragments and round them to bf16. Row y0 + 2 goes out once the weights are read.
+  {
+    constexpr int kWPitch = 4 * C + 16;
+    constexpr int kRowsA = (int)sizeof(sD) / kWPitch;
+    constexpr int kRowsB = (int)sizeof(sRing[3]) / kWPitch;
+    constexpr int kRoundRows = std::min(C, 32 * ((kRowsA + kRowsB) / 32));
+    static_assert(kRoundRows >= 32, "a round holds at least one 32-row output group");
+    // halo DMA instructions each wave issues after the first round's weights (three rows)
+    constexpr int kMinHalo = std::min(63, 3 * (kRowInsts / NW));
+    char* stage_a = (char*)sD;
+    char* stage_b = (char*)sRing[3];
+    auto stage_row = [&](int i) { return i < kRowsA ? stage_a + i * kWPitch : stage_b + (i - kRowsA) * kWPitch; };
+    const __amdgpu_buffer_rsrc_t wrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.w_pw), 0, C * C * 4, 0x00020000);
+#pragma unroll
+    for (int r0 = 0; r0 < C; r0 += kRoundRows) {
+      const int nr = std::min(kRoundRows, C - r0);
+      for (int i = wave; i < nr; i += NW)
+        if (lane < C / 4)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (__attribute__((address_space(3))) void*)stage_row(i), 16,
+                                                   ((r0 + i) * C + 4 * lane) * 4, 0, 0, 0);
+      if (r0 == 0) {
+        dma_row(y0 - 1);
+        dma_row(y0);
+        dma_row(y0 + 1);
+        asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(kMinHalo) : "memory");
+      } else {
+        full_barrier();
+      }
+      if (32 * og >= r0 && 32 * og < r0 + nr) {
+#pragma unroll
+        for (int ob = 0; ob < 2; ++ob) {
+          const float* wrow = (const float*)stage_row(32 * og - r0 + 16 * ob + l16);
+#pragma unroll
+          for (int s = 0; s < KS; ++s) {
+            const f32x4 w0 = *(const f32x4*)(wrow + 32 * s + 8 * quad);
+            const f32x4 w1 = *(const f32x4*)(wrow + 32 * s + 8 * quad + 4);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              wa[ob][s][j] = f32_to_bf16(w0[j]);
+              wa[ob][s][4 + j] = f32_to_bf16(w1[j]);
+            }
+          }
+        }
+      }
+      lds_barrier();
+    }
+  }
+  // rows y0 - 1 .. y0 + 1 landed in every wave's part; row y0 + 2's DMA (at least kRowInsts / NW
+  // instructions of each wave) may stay in flight until step y0
+  if (y0 + 2 <= y1) {
+    dma_row(y0 + 2);
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(std::min(63, kRowInsts / NW)) : "memory");
+  } else {
+    full_barrier();
+  }
   depthwise(y0, 0);
   for (int y = y0; y < y1; ++y) {
     // row y + 2 landed, D of row y complete, every wave past the previous step (ring slot of row
-    // y - 1 and the other D buffer free)
-    full_barrier();
+    // y - 1 and the other D buffer free). Row y + 2's DMA went out in step y - 1 before that
+    // step's four stores, which from step y0 + 2 on may stay in flight.
+    if (y >= y0 + 2) barrier_after_dma_of_prev_step();
+    else full_barrier();
     if (y + 3 <= y1) dma_row(y + 3);
     if (y > y0) store_row(y - 1);
     const int db = (y - y0) & 1;
