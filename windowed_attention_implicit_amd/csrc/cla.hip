@@ -20,10 +20,13 @@
 //    v_mfma_f32_16x16x32_bf16; wave v owns outputs 32 (v % CB) .. + 31 (two 16-row A blocks of
 //    W_pw, bf16, in registers for the whole launch) for the 32 pixels 32 (v / CB) .. + 31 (two
 //    16-column B blocks read from D), so D is read C / 32 times per row segment.
-//  * Sigmoid in fp32 on the accumulator, rounded once to bf16; a lane's accumulator holds 4
-//    consecutive output channels of one pixel, stored as 8 bytes straight to the map at the
-//    start of the next row's step (so the store's latency hides behind that step), through a
-//    range-checked buffer store that drops pixels past the map's edge.
+//  * Sigmoid in fp32 on the accumulator, rounded once to bf16. A lane's accumulators hold two
+//    4-channel pieces of one pixel 16 channels apart; two lane swaps (v_permlane32_swap, then
+//    v_permlane16_swap) regroup them into 8 consecutive channels per lane, stored as 16 bytes
+//    straight to the map at the start of the next row's step (so the store's latency hides
+//    behind that step) through a range-checked buffer store that drops pixels past the map's
+//    edge: two store instructions per wave and row, each writing 16 whole 64-byte runs (four
+//    8-byte stores of 32-byte runs cost a fifth of the step).
 //  * The point-wise weights reach LDS once per workgroup by coalesced DMA (one float32 row per
 //    instruction) before the first depth-wise conv, in the D buffers and the last ring slot, and
 //    each wave reads its A fragments there: loading them per lane straight from global memory
@@ -49,10 +52,10 @@ __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(
 // Workgroup barrier after all of this wave's memory operations (halo DMA included) completed.
 __device__ __forceinline__ void full_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Workgroup barrier after all but this wave's last four memory operations completed: the row
+// Workgroup barrier after all but this wave's last two memory operations completed: the row
 // stores that follow the halo DMA the barrier waits for (memory operations complete in order).
 __device__ __forceinline__ void barrier_after_dma_of_prev_step() {
-  asm volatile("s_waitcnt vmcnt(4) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  asm volatile("s_waitcnt vmcnt(2) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 __device__ __forceinline__ float sigmoid_fast(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
@@ -190,10 +193,12 @@ __global__ __launch_bounds__(64 * CB * SEG) void cla_gate_bf16_kernel(GateArgs a
     }
   };
 
-  uint2 gres[2][2];
-  // G of the previous row, 4 bf16 per (ob, pb), stored at the start of the next step through a
-  // range-checked buffer: pixels past W fall outside the row's range and are dropped, so every
-  // wave issues exactly four stores per row (the barrier below counts on it)
+  // G of the previous row: per pixel block pb, 8 consecutive output channels 32 og + 8 (l / 16)
+  // .. + 7 of pixel l % 16 per lane, stored at the start of the next step through a
+  // range-checked buffer (pixels past W fall outside the row's range and are dropped), so every
+  // wave issues exactly two stores per row (the barrier below counts on it), each writing whole
+  // 64-byte runs of 16 pixels
+  u32x4 gres[2];
   const int seg_px = min(W, x0 + SPX) - x0;
   auto store_row = [&](int y) {
     bf16* grow = gout + (((int64_t)b * H + y) * W + x0) * C;
@@ -201,11 +206,7 @@ __global__ __launch_bounds__(64 * CB * SEG) void cla_gate_bf16_kernel(GateArgs a
 #pragma unroll
     for (int pb = 0; pb < 2; ++pb) {
       const int px = 32 * sg + 16 * pb + l16;
-#pragma unroll
-      for (int ob = 0; ob < 2; ++ob) {
-        const int off = (px * C + 32 * og + 16 * ob + 4 * quad) * 2;
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, gres[ob][pb]), rs, off, 0, 0);
-      }
+      __builtin_amdgcn_raw_buffer_store_b128(gres[pb], rs, (px * C + 32 * og + 8 * quad) * 2, 0, 0);
     }
   };
 
@@ -280,7 +281,7 @@ __global__ __launch_bounds__(64 * CB * SEG) void cla_gate_bf16_kernel(GateArgs a
   for (int y = y0; y < y1; ++y) {
     // row y + 2 landed, D of row y complete, every wave past the previous step (ring slot of row
     // y - 1 and the other D buffer free). Row y + 2's DMA went out in step y - 1 before that
-    // step's four stores, which from step y0 + 2 on may stay in flight.
+    // step's two stores, which from step y0 + 2 on may stay in flight.
     if (y >= y0 + 2) barrier_after_dma_of_prev_step();
     else full_barrier();
     if (y + 3 <= y1) dma_row(y + 3);
@@ -304,15 +305,31 @@ __global__ __launch_bounds__(64 * CB * SEG) void cla_gate_bf16_kernel(GateArgs a
           acc[ob][pb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ob][s], bf[pb], acc[ob][pb], 0, 0, 0);
     }
     if (y + 1 < y1) depthwise(y + 1, db ^ 1);
+    // Lane l holds outputs 16 ob + 4 (l / 16) + 0..3 of pixel l % 16 (dwords lo, hi per ob).
+    // Counting 16-lane rows, swapping rows 2, 3 of the ob = 0 dword with rows 0, 1 of the
+    // ob = 1 dword (v_permlane32_swap), then the odd rows of the first result with the even rows
+    // of the second (v_permlane16_swap), leaves row q with outputs 4 (2q) .. 4 (2q) + 3 in the
+    // first result and 4 (2q + 1) .. + 3 in the second: 8 consecutive outputs per lane.
 #pragma unroll
-    for (int ob = 0; ob < 2; ++ob)
+    for (int pb = 0; pb < 2; ++pb) {
+      unsigned w[2][2];   // [ob][lo, hi]
 #pragma unroll
-      for (int pb = 0; pb < 2; ++pb) {
+      for (int ob = 0; ob < 2; ++ob) {
         bf16 o4[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) o4[i] = f32_to_bf16(sigmoid_fast(acc[ob][pb][i]));
-        gres[ob][pb] = *(const uint2*)o4;
+        const uint2 u = *(const uint2*)o4;
+        w[ob][0] = u.x;
+        w[ob][1] = u.y;
       }
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const auto r32 = __builtin_amdgcn_permlane32_swap(w[0][h], w[1][h], false, false);
+        const auto r16 = __builtin_amdgcn_permlane16_swap(r32[0], r32[1], false, false);
+        gres[pb][h] = r16[0];        // outputs 8 q + 2 h, + 1
+        gres[pb][2 + h] = r16[1];    // outputs 8 q + 4 + 2 h, + 1
+      }
+    }
   }
   if (y1 > y0) store_row(y1 - 1);
 }
