@@ -321,6 +321,9 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
         const int c = pos16_chunk(lane);
         qpta[0] = tr_frag(&T[oQp], C::kPRow, sub * 32 + 16 * (c >> 1) + 4 * (c & 1), 0, lane);
       }
+      // scores and dP of both key blocks first, so the vector work of block 0 runs while
+      // block 1's MFMAs are in the matrix pipe
+      f32x16 scs[2], dps[2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
         // sc = S' - LSE2 (log2 domain), dp = dP - D
@@ -329,6 +332,12 @@ __global__ __launch_bounds__(256, KP == 1 ? 2 : 1) void attn_bwd_dkv_kernel(BwdA
         for (int s = 1; s < C::kSteps; ++s) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], kf[nb][s], sc, 0, 0, 0);
         f32x16 dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[0], vf[nb][0], nd, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(da[1], vf[nb][1], dp, 0, 0, 0);
+        scs[nb] = sc;
+        dps[nb] = dp;
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const f32x16 sc = scs[nb], dp = dps[nb];
         bf16x8 pb[2], sb[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
@@ -443,10 +452,12 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
   // harmless: their K_hat rows are zero. (KP = 2 has no registers to spare for it and adds
   // -D on the vector pipe.)
   constexpr bool kDext = KP == 1;
-  bf16x8 qf[2][C::kSteps], df[2][2], dext[2], vone;
+  bf16x8 qf[2][C::kSteps], df[2][2], dext[2], vone, lext[2], kone;
   float nlq[2], ndq[2];
 #pragma unroll
   for (int j = 0; j < 8; ++j) vone[j] = (half == 0 && j < 2) ? (bf16)1.0f : (bf16)0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) kone[j] = (half == 0 && j < 3) ? (bf16)1.0f : (bf16)0.0f;
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
     const int q = q0 + nb * 32 + l32;
@@ -465,6 +476,20 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
     const bf16 lo = f32_to_bf16(nd - (float)hi);
 #pragma unroll
     for (int j = 0; j < 8; ++j) dext[nb][j] = half == 0 && j == 0 ? hi : (half == 0 && j == 1 ? lo : (bf16)0.0f);
+    // -LSE2 in three bf16 parts for the score MFMA's extra K-step: 3 x 8 significant bits hold
+    // the float32 value, so the K-step yields it exactly and the scores equal those of the
+    // accumulator-input form bit for bit, while the 32 registers of that input are free for the
+    // second column block's scores. A non-finite value (padded queries: -inf) goes whole into
+    // the first part.
+    const float nl = nlq[nb];
+    const bool fin = __builtin_isfinite(nl);
+    const bf16 l0 = f32_to_bf16(nl);
+    const float r1 = fin ? nl - (float)l0 : 0.f;
+    const bf16 l1 = f32_to_bf16(r1);
+    const bf16 l2 = f32_to_bf16(r1 - (float)l1);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      lext[nb][j] = half != 0 ? (bf16)0.0f : (j == 0 ? l0 : (j == 1 ? l1 : (j == 2 ? l2 : (bf16)0.0f)));
   }
 
   // acc_dqp: as acc_dkp in dkv (16x16 tiles at KP = 1)
@@ -473,7 +498,7 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
 #pragma unroll
   for (int nb = 0; nb < 2; ++nb) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) { acc_dq[nb][i] = 0.f; acc_dqp[nb][i] = 0.f; cl[nb][i] = nlq[nb]; }
+    for (int i = 0; i < 16; ++i) { acc_dq[nb][i] = 0.f; acc_dqp[nb][i] = 0.f; if (!kDext) cl[nb][i] = nlq[nb]; }
     acc_dqp16[nb][0] = acc_dqp16[nb][1] = f32x4(0.f);
   }
 
@@ -513,17 +538,28 @@ __global__ __launch_bounds__(256, 1) void attn_bwd_dq_kernel(BwdArgs a) {
         const int c = pos16_chunk(lane);
         kpta[0] = tr_frag(&T[oKp], C::kPRow, sub * 32 + 16 * (c >> 1) + 4 * (c & 1), 0, lane);
       }
+      // scores and dP of both column blocks first, so the vector work of block 0 runs while
+      // block 1's MFMAs are in the matrix pipe
+      f32x16 scs[2], dps[2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        // one query per lane: -LSE2 enters as the score MFMA's accumulator input (a lane
-        // constant, 32 registers for both column blocks), -D through the third dP K-step
-        f32x16 sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[nb][0], cl[nb], 0, 0, 0);
+        // one query per lane: KP = 1, -LSE2 through an extra score K-step (ones x its three
+        // bf16 parts) and -D through the third dP K-step; KP = 2, -LSE2 as the accumulator input
+        f32x16 sc = kDext ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(kone, lext[nb], f32x16(0.f), 0, 0, 0)
+                          : __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[0], qf[nb][0], cl[nb], 0, 0, 0);
 #pragma unroll
-        for (int s = 1; s < C::kSteps; ++s) sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[nb][s], sc, 0, 0, 0);
+        for (int s = kDext ? 0 : 1; s < C::kSteps; ++s)
+          sc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[s], qf[nb][s], sc, 0, 0, 0);
         f32x16 dp = kDext ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(vone, dext[nb], f32x16(0.f), 0, 0, 0)
                           : f32x16(0.f);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[0], df[nb][0], dp, 0, 0, 0);
         dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[1], df[nb][1], dp, 0, 0, 0);
+        scs[nb] = sc;
+        dps[nb] = dp;
+      }
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const f32x16 sc = scs[nb], dp = dps[nb];
         bf16x8 sb[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s)
