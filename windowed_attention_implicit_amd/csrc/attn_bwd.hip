@@ -212,10 +212,10 @@ __device__ __forceinline__ void pos16_b(const bf16x8 (&sb)[2], bf16x8 (&b)[2]) {
 
 // ------------------------------------------------------------------ dK, dV
 template <int KP, bool MAPKV = false>
-// The register budget of one workgroup per CU (the kernel then runs one wave per SIMD): the
-// schedule the compiler makes with it beats two co-resident workgroups at every window size
-// measured (16 to 96: -4 to -7 %); the dQ kernel is the other way round (two per CU, +35 %
-// when held to one).
+// Compiled with the register budget of one workgroup per CU: the schedule the compiler makes
+// under it is 4-7 % faster at every window size measured (16 to 96) than under the budget of two,
+// and the counters still show about two workgroups resident per CU. (Holding the dQ kernel to
+// one resident workgroup per CU makes it 35 % slower.)
 __global__ __launch_bounds__(256, 1) void attn_bwd_dkv_kernel(BwdArgs a) {
   static_assert(!MAPKV || KP == 1, "map-addressed K / V: one positional K-step only");
   typedef BwdCfg<KP> C;
