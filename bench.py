@@ -369,6 +369,35 @@ def rpb_compare(wl, x, dev, steps: int, rib_attn_ms: float):
             "materialized_bias_bytes_bf16": wl.heads * wl.N * wl.N * 2}
 
 
+def cla_gate_only(wl, dev, steps: int, warmup: int):
+    """The CLA gate alone on the headline map (C = heads * d_c = 192): kernel time and rates."""
+    import torch
+    import rib_synth
+    import windowed_attention_implicit_amd as rib
+    C = wl.heads * wl.d_c
+    xm = to_gpu(rib_synth.make_map(wl.B, wl.H, wl.W, C, "bf16", seed=192), dev)
+    w = {k: torch.from_numpy(v).to(dev) for k, v in rib_synth.make_cla(C, seed=193).items()}
+    g = torch.empty_like(xm)
+
+    def gate():
+        rib.cla_gate(xm, w["w_dw"], w["b_dw"], w["w_pw"], w["b_pw"], wl.heads, out=g)
+
+    def reset():
+        for grp in rib.KERNEL_GROUPS:
+            rib.kernel_timing_read(grp)
+
+    rib.kernel_timing_enable(True)
+    time_steps(gate, steps, warmup, reset)
+    gate_ms, n = kernel_avg_ms(rib, "cla_gate")
+    rib.kernel_timing_enable(False)
+    tensor_bytes = wl.B * wl.H * wl.W * C * 2
+    flops = wl.B * wl.H * wl.W * (2 * 9 * C + 2 * C * C)
+    return {"workload": f"gate of a [{wl.B}, {wl.H}, {wl.W}, {C}] bf16 map", "launches": n,
+            "gate_kernel_ms": round(gate_ms, 5), "gate_GB/s": round(2 * tensor_bytes / gate_ms / 1e6, 1),
+            "gate_frac_hbm": round(2 * tensor_bytes / gate_ms / 1e6 / PEAK_HBM_GBS, 3),
+            "gate_tflops": round(flops / gate_ms / 1e9, 1)}
+
+
 def cla_measure(wl, x, step, dev, steps: int):
     """The CLA gate on the headline map (C = heads * d_c = 192) and the forward with O' = O * G fused into
     the attention kernel's output stage."""
@@ -442,6 +471,9 @@ def main():
     ap.add_argument("--only-headline", action="store_true",
                     help="time the headline step only (no CLA, tiers, other workloads, RPB, stack or CPU "
                          "baseline): the command the profiler runs")
+    ap.add_argument("--only-cla", action="store_true",
+                    help="time the CLA gate on the headline map only and print its record (the command the "
+                         "gate's counter runs use)")
     ap.add_argument("--calibration-copy-mib", type=int, default=0,
                     help="also run one plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -460,6 +492,9 @@ def main():
         sys.exit(1)
     dev = torch.device("cuda:0")
     wl = rib_synth.HEADLINE
+    if args.only_cla:
+        print(json.dumps({"cla": cla_gate_only(wl, dev, args.steps, args.warmup)}), flush=True)
+        return
     x = rib_synth.make_inputs(wl)
     step = FwdStep(wl, x, dev)
     print(f"bench: {wl.name} units={wl.units} N={wl.N}", file=sys.stderr, flush=True)
