@@ -57,6 +57,40 @@ def test_cla_gate_null_biases_and_repeat():
     check("G no biases", to_f64(g1), oracle.cla_gate(x.f64(), p["w_dw"], None, p["w_pw"], None), "bf16")
 
 
+def _strip_rows(B, H, W, C, cus):
+    """Rows per strip the bf16 gate's launcher picks: 64-pixel segments up to C = 192 (32 above), and
+    the fewest rows whose strips fit one round of one workgroup per CU."""
+    seg = 64 if C <= 192 else 32
+    cols = B * ((W + seg - 1) // seg)
+    rows = max(1, (cols * H + cus - 1) // cus)
+    while rows < H and cols * ((H + rows - 1) // rows) > cus:
+        rows += 1
+    return rows
+
+
+@pytest.mark.parametrize("B,H,W,heads", [
+    (2, 162, 130, 1),   # C = 32: 2 waves, 64-pixel segments; strips of 4 rows, the last of 2
+    (2, 97, 150, 3),    # C = 96: 6 waves; strips of 3 rows, the last of 1; a 22-pixel last segment
+    (2, 100, 100, 7),   # C = 224: 7 waves, 32-pixel segments
+    (2, 128, 96, 8),    # C = 256: 8 waves, the point-wise weights in eight rounds
+])
+def test_cla_gate_parity_multirow_strips(B, H, W, heads):
+    """Maps on which every workgroup walks a strip of three or more rows, so the waits that count
+    memory operations still in flight (the fourth halo row after the prologue, two row stores per
+    step after that) run for every wave count and segment width, not only at C = 192."""
+    dev = device()
+    C = 32 * heads
+    rows = _strip_rows(B, H, W, C, torch.cuda.get_device_properties(dev).multi_processor_count)
+    print(f"CLA {B}x{H}x{W}x{C}: strips of {rows} rows", flush=True)
+    assert rows >= 3
+    x = rib_synth.make_map(B, H, W, C, "bf16", seed=H + W + C)
+    p, t = _weights(C, seed=C + 7, dev=dev)
+    g = rib.cla_gate(to_gpu(x, dev), t["w_dw"], t["b_dw"], t["w_pw"], t["b_pw"], heads)
+    torch.cuda.synchronize()
+    ref = oracle.cla_gate(x.f64(), p["w_dw"], p["b_dw"], p["w_pw"], p["b_pw"])
+    check(f"G {B}x{H}x{W}x{C} strips of {rows}", to_f64(g), ref, "bf16")
+
+
 def test_cla_gate_headline_map_full():
     """The gate of the 96x96-window workload's map (batch 4, 192 x 192, C = 192), every value."""
     dev = device()
