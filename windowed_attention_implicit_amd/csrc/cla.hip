@@ -285,6 +285,9 @@ __global__ __launch_bounds__(64 * CB * SEG) void cla_gate_bf16_kernel(GateArgs a
     if (y >= y0 + 2) barrier_after_dma_of_prev_step();
     else full_barrier();
     if (y + 3 <= y1) dma_row(y + 3);
+    // the stores must follow the DMA in issue order: the next step's barrier waits for all but
+    // this wave's last two memory operations
+    asm volatile("" ::: "memory");
     if (y > y0) store_row(y - 1);
     const int db = (y - y0) & 1;
     // ---- point-wise 1x1: block (ob, pb) = outputs 32 og + 16 ob + [0, 16) x pixels 32 sg + 16 pb +
