@@ -243,6 +243,8 @@ __global__ __launch_bounds__(64 * CB * SEG) void cla_gate_bf16_kernel(GateArgs a
           __builtin_amdgcn_raw_ptr_buffer_load_lds(wrs, (__attribute__((address_space(3))) void*)stage_row(i), 16,
                                                    ((r0 + i) * C + 4 * lane) * 4, 0, 0, 0);
       if (r0 == 0) {
+        // the halo rows follow the round's weights in issue order (the wait below counts on it)
+        asm volatile("" ::: "memory");
         dma_row(y0 - 1);
         dma_row(y0);
         dma_row(y0 + 1);
